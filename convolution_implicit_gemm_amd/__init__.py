@@ -1,0 +1,78 @@
+"""FusedConv for MI355X (gfx950): Y = act(conv(X, W) + B + Z) in hand-written HIP.
+
+The computation lives in libfusedconv.so behind the C ABI of
+include/fusedconv.h.  This package marshals arguments: torch tensors supply
+device memory and the current HIP stream, nothing else.  Semantics follow the
+FusedConv README ("Description", "Inputs", "Outputs", "Attributes").
+"""
+from __future__ import annotations
+
+from ._binding import EXPORTS, FusedConvError, Handle, LIB_PATH, load
+
+__all__ = ["fused_conv", "FusedConv", "Handle", "FusedConvError", "load", "LIB_PATH", "EXPORTS"]
+
+_cache: dict = {}
+
+
+def _dtype_name(t):
+    import torch
+    if t.dtype == torch.float32:
+        return "f32"
+    if t.dtype == torch.float16:
+        return "f16"
+    raise FusedConvError(-2, f"dtype {t.dtype} is not float32 or float16")
+
+
+class FusedConv:
+    """A planned FusedConv for fixed shapes and attributes, run on torch tensors."""
+
+    def __init__(self, x_shape, w_shape, dtype, has_bias=False, has_z=False, **attrs):
+        self.attrs = attrs
+        z_shape = None
+        if has_z:
+            # Z must have Y's shape; resolve Y first with a probe handle.
+            z_shape = Handle(dtype, x_shape, w_shape, [w_shape[0]] if has_bias else None,
+                             None, **attrs).y_shape
+        self.handle = Handle(dtype, x_shape, w_shape, [w_shape[0]] if has_bias else None,
+                             z_shape, **attrs)
+        self.y_shape = self.handle.y_shape
+        self.workspace_bytes = self.handle.workspace_bytes
+
+    def __call__(self, x, w, bias=None, z=None, out=None, workspace=None, stream=None):
+        import torch
+        for name, t in (("x", x), ("w", w), ("bias", bias), ("z", z), ("out", out)):
+            if t is None:
+                continue
+            if not t.is_cuda:
+                raise FusedConvError(-1, f"{name} must be a device tensor (no CPU path)")
+            if not t.is_contiguous():
+                raise FusedConvError(-1, f"{name} must be contiguous")
+        y = out if out is not None else torch.empty(self.y_shape, dtype=x.dtype, device=x.device)
+        ws = workspace
+        if self.workspace_bytes and ws is None:
+            ws = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=x.device)
+        st = stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream
+        self.handle.run(x.data_ptr(), w.data_ptr(),
+                        bias.data_ptr() if bias is not None else None,
+                        z.data_ptr() if z is not None else None, y.data_ptr(),
+                        ws.data_ptr() if ws is not None else None,
+                        self.workspace_bytes if ws is not None else 0, st)
+        return y
+
+
+def fused_conv(x, w, bias=None, z=None, *, auto_pad=None, group=1, kernel_shape=None,
+               strides=None, dilations=None, pads=None, activation=None,
+               activation_params=None, route="auto", split_k=0):
+    """Y = act(conv(x, w) + bias + z) on the current stream; Y is allocated with torch."""
+    attrs = dict(auto_pad=auto_pad, group=group, kernel_shape=kernel_shape, strides=strides,
+                 dilations=dilations, pads=pads, activation=activation,
+                 activation_params=activation_params, route=route, split_k=split_k)
+    key = (tuple(x.shape), tuple(w.shape), x.dtype, bias is not None, z is not None,
+           tuple((k, tuple(v) if isinstance(v, (list, tuple)) else v)
+                 for k, v in sorted(attrs.items())))
+    op = _cache.get(key)
+    if op is None:
+        op = FusedConv(list(x.shape), list(w.shape), _dtype_name(x), bias is not None,
+                       z is not None, **attrs)
+        _cache[key] = op
+    return op(x, w, bias, z)

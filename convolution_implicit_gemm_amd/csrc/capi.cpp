@@ -1,0 +1,167 @@
+// C ABI entry points (include/fusedconv.h).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+#include <new>
+#include <string>
+
+#include "internal.h"
+
+struct fusedconv_handle {
+  fc::Geometry geo;
+  fc::Plan plan;
+};
+
+namespace {
+
+thread_local std::string t_last_error;
+
+int set_err(int code, const std::string& msg) {
+  t_last_error = msg;
+  return code;
+}
+
+// Per-device "is gfx950" cache: 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_ok[kMaxDevices];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_err(FUSEDCONV_ERR_DEVICE, "no current HIP device");
+  int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+      return set_err(FUSEDCONV_ERR_DEVICE, "hipGetDeviceProperties failed");
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  if (st != 1) return set_err(FUSEDCONV_ERR_DEVICE, "the current device is not a gfx950 GPU");
+  return FUSEDCONV_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+void fusedconv_desc_init(fusedconv_desc* d) {
+  if (!d) return;
+  memset(d, 0, sizeof(*d));
+  d->dtype = FUSEDCONV_F32;
+  d->group = 1;
+}
+
+int fusedconv_create(const fusedconv_desc* d, fusedconv_handle** out) {
+  if (out) *out = nullptr;
+  if (!d || !out) return set_err(FUSEDCONV_ERR_NULL_ARG, "desc and out must not be NULL");
+  fusedconv_handle* h = new (std::nothrow) fusedconv_handle;
+  if (!h) return set_err(FUSEDCONV_ERR_ALLOC, "out of host memory");
+  std::string err;
+  int rc = fc::resolve(*d, h->geo, err);
+  if (rc == FUSEDCONV_OK) rc = fc::make_plan(h->geo, d->route, d->split_k, h->plan, err);
+  if (rc != FUSEDCONV_OK) {
+    delete h;
+    return set_err(rc, err);
+  }
+  *out = h;
+  t_last_error.clear();
+  return FUSEDCONV_OK;
+}
+
+int fusedconv_output_shape(const fusedconv_handle* h, int64_t dims[FUSEDCONV_MAX_RANK],
+                           int32_t* rank) {
+  if (!h || !dims || !rank) return set_err(FUSEDCONV_ERR_NULL_ARG, "NULL argument");
+  *rank = h->geo.y_rank;
+  for (int i = 0; i < FUSEDCONV_MAX_RANK; ++i) dims[i] = i < h->geo.y_rank ? h->geo.y_dims[i] : 0;
+  return FUSEDCONV_OK;
+}
+
+int fusedconv_workspace_size(const fusedconv_handle* h, size_t* bytes) {
+  if (!h || !bytes) return set_err(FUSEDCONV_ERR_NULL_ARG, "NULL argument");
+  *bytes = h->plan.workspace;
+  return FUSEDCONV_OK;
+}
+
+int fusedconv_plan_info(const fusedconv_handle* h, int32_t* route, int32_t* split_k, char* name,
+                        size_t name_len) {
+  if (!h) return set_err(FUSEDCONV_ERR_NULL_ARG, "NULL handle");
+  if (route) *route = h->plan.route;
+  if (split_k) *split_k = h->plan.split_k;
+  if (name && name_len > 0) {
+    strncpy(name, h->plan.name, name_len - 1);
+    name[name_len - 1] = '\0';
+  }
+  return FUSEDCONV_OK;
+}
+
+int fusedconv_run(const fusedconv_handle* h, const void* x, const void* w, const void* bias,
+                  const void* z, void* y, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (!h || !x || !w || !y) return set_err(FUSEDCONV_ERR_NULL_ARG, "h, x, w and y are required");
+  const fc::ConvParams& cp = h->geo.cp;
+  if (cp.has_bias && !bias) return set_err(FUSEDCONV_ERR_NULL_ARG, "bias declared but NULL");
+  if (!cp.has_bias && bias)
+    return set_err(FUSEDCONV_ERR_NULL_ARG, "bias given but not declared in the descriptor");
+  if (cp.has_z && !z) return set_err(FUSEDCONV_ERR_NULL_ARG, "z declared but NULL");
+  if (!cp.has_z && z) return set_err(FUSEDCONV_ERR_NULL_ARG, "z given but not declared");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (bias && !aligned16(bias)) ||
+      (z && !aligned16(z)) || (workspace && !aligned16(workspace)))
+    return set_err(FUSEDCONV_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  if (h->plan.workspace > 0 && (!workspace || workspace_bytes < h->plan.workspace))
+    return set_err(FUSEDCONV_ERR_WORKSPACE,
+                   "workspace smaller than fusedconv_workspace_size() reports");
+  int rc = check_device();
+  if (rc != FUSEDCONV_OK) return rc;
+  (void)hipGetLastError();  // drop a stale error so a launch failure is reported as ours
+  fc::RunArgs a{x, w, bias, z, y, workspace, stream};
+  switch (h->plan.route) {
+    case FUSEDCONV_ROUTE_DIRECT: rc = fc::launch_direct(h->geo, h->plan, a); break;
+    case FUSEDCONV_ROUTE_IGEMM: rc = fc::launch_igemm(h->geo, h->plan, a); break;
+    case FUSEDCONV_ROUTE_DEPTHWISE: rc = fc::launch_depthwise(h->geo, h->plan, a); break;
+    case FUSEDCONV_ROUTE_IGEMM_HALO: rc = fc::launch_igemm_halo(h->geo, h->plan, a); break;
+    default: return set_err(FUSEDCONV_ERR_ROUTE, "handle has no route");
+  }
+  if (rc != FUSEDCONV_OK) {
+    hipError_t e = hipGetLastError();
+    return set_err(rc, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  }
+  return FUSEDCONV_OK;
+}
+
+void fusedconv_destroy(fusedconv_handle* h) { delete h; }
+
+const char* fusedconv_status_string(int status) {
+  switch (status) {
+    case FUSEDCONV_OK: return "ok";
+    case FUSEDCONV_ERR_NULL_ARG: return "null argument";
+    case FUSEDCONV_ERR_DTYPE: return "unsupported dtype";
+    case FUSEDCONV_ERR_RANK: return "bad rank";
+    case FUSEDCONV_ERR_ATTR_LENGTH: return "bad attribute length";
+    case FUSEDCONV_ERR_ATTR_VALUE: return "bad attribute value";
+    case FUSEDCONV_ERR_PADS_WITH_AUTO_PAD: return "pads given with auto_pad";
+    case FUSEDCONV_ERR_KERNEL_SHAPE: return "kernel_shape does not match w";
+    case FUSEDCONV_ERR_GROUP: return "bad group";
+    case FUSEDCONV_ERR_BIAS_SHAPE: return "bad bias shape";
+    case FUSEDCONV_ERR_Z_SHAPE: return "bad residual shape";
+    case FUSEDCONV_ERR_ACTIVATION: return "unknown activation";
+    case FUSEDCONV_ERR_ACTIVATION_PARAMS: return "bad activation parameters";
+    case FUSEDCONV_ERR_OUTPUT_SHAPE: return "bad output shape";
+    case FUSEDCONV_ERR_WORKSPACE: return "workspace too small";
+    case FUSEDCONV_ERR_ALIGNMENT: return "misaligned pointer";
+    case FUSEDCONV_ERR_ROUTE: return "route cannot run this problem";
+    case FUSEDCONV_ERR_LAUNCH: return "launch failed";
+    case FUSEDCONV_ERR_DEVICE: return "unsupported device";
+    case FUSEDCONV_ERR_ALLOC: return "host allocation failed";
+    case FUSEDCONV_ERR_TOO_LARGE: return "tensor too large";
+    default: return "unknown status";
+  }
+}
+
+const char* fusedconv_last_error(void) { return t_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// Resolved problem and plan, shared by the host resolver/planner and the
+// device kernels.  Plain structs only: passed to kernels by value.
+#pragma once
+
+#include <stdint.h>
+
+namespace fc {
+
+// Activation ids, in the order of the FusedConv manifest.json activation list
+// ("attributeConstraints.activation"), 0 = none.
+enum Act : int32_t {
+  ACT_NONE = 0, ACT_RELU, ACT_LEAKYRELU, ACT_SIGMOID, ACT_TANH, ACT_HARDSIGMOID,
+  ACT_HARDSWISH, ACT_CLIP, ACT_QUICKGELU, ACT_ELU, ACT_GELU, ACT_FASTGELU, ACT_SOFTPLUS,
+  ACT_THRESHOLDEDRELU, ACT_ERF, ACT_COUNT
+};
+
+// The convolution after attribute resolution.  Spatial axes are stored as
+// (D, H, W) right-aligned: a 2-D problem has D = OD = KD = 1, a 1-D problem
+// also H = OH = KH = 1 (the manifest's inputDepth / inputHeight defaults).
+// Pads are the effective begin pads; end pads only shape the output size.
+struct ConvParams {
+  int64_t n;            // batch
+  int32_t C, M, G;      // input channels, output channels, groups
+  int32_t Cg, Mg;       // per group
+  int32_t D, H, W;      // input spatial
+  int32_t OD, OH, OW;   // output spatial
+  int32_t KD, KH, KW;   // kernel spatial
+  int32_t sd, sh, sw;   // strides
+  int32_t dd, dh, dw;   // dilations
+  int32_t pd, ph, pw;   // effective begin pads
+  int32_t taps;         // KD*KH*KW
+  int32_t K;            // Cg*taps: GEMM reduction length
+  int64_t in_sz;        // D*H*W
+  int64_t out_sz;       // OD*OH*OW
+  int64_t P;            // n*out_sz: GEMM columns
+  int32_t act;          // Act
+  float alpha, beta;    // activation parameters after defaulting
+  int32_t has_bias, has_z;
+};
+
+}  // namespace fc

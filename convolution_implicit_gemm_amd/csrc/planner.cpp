@@ -1,0 +1,136 @@
+// Planner: picks the kernel route, tile variant and K split for a resolved
+// problem.  Host only.
+//
+// The pages' planners are tuned for WebGPU adapters (FusedConv manifest.json
+// derive implicitTiledWorthIt, tiledSplitK*, preferImplicitSplitK); what
+// carries over is the shape of the decision: grouped convs with one input
+// channel per group go to a direct halo kernel, dense channel counts go to an
+// implicit GEMM, and a GEMM whose output grid cannot fill the device splits
+// its reduction (split-K: raw fp32 partials, then one reduce that applies
+// bias, residual and activation once).  Thresholds here are for 256 CUs.
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "internal.h"
+
+namespace fc {
+namespace {
+
+constexpr int kBK = 32;                     // IGEMM reduction tile
+constexpr int kBN = 128;                    // IGEMM column (output pixel) tile
+constexpr int64_t kSplitTargetBlocks = 512; // about two workgroups per CU
+constexpr int64_t kSplitMaxBase = 128;      // only split grids this small
+constexpr size_t kSplitMaxBytes = (size_t)256 << 20;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Grid limits of the IGEMM launch: x = column tiles, y = row tiles, z = group * split.
+bool igemm_grid_ok(const ConvParams& cp, int64_t split) {
+  const int bm = cp.Mg > 64 ? 128 : 64;
+  return cdiv(cp.P, kBN) < ((int64_t)1 << 31) && cdiv(cp.Mg, bm) <= 65535 &&
+         cp.G * split <= 65535;
+}
+
+int plan_igemm(const Geometry& g, int32_t split_req, Plan& p, std::string& err) {
+  const ConvParams& cp = g.cp;
+  const int bm = cp.Mg > 64 ? 128 : 64;
+  p.route = FUSEDCONV_ROUTE_IGEMM;
+  p.tile = bm == 128 ? IGEMM_BM128_BN128 : IGEMM_BM64_BN128;
+  p.k_tiles = (int32_t)cdiv(cp.K, kBK);
+  const int64_t base = cdiv(cp.Mg, bm) * cdiv(cp.P, kBN) * cp.G;
+  int split = 1;
+  if (split_req > 0) {
+    if (split_req > p.k_tiles) {
+      err = "split_k larger than the number of K tiles";
+      return FUSEDCONV_ERR_ROUTE;
+    }
+    split = split_req;
+  } else if (base <= kSplitMaxBase && cp.K >= 8 * kBK) {
+    for (int s = 16; s >= 2; s /= 2) {
+      if (base * s <= kSplitTargetBlocks && p.k_tiles >= 2 * s &&
+          (size_t)s * cp.M * cp.P * 4 <= kSplitMaxBytes) {
+        split = s;
+        break;
+      }
+    }
+  }
+  p.k_tiles_per_split = (int32_t)cdiv(p.k_tiles, split);
+  split = (int32_t)cdiv(p.k_tiles, p.k_tiles_per_split);  // no empty slices
+  if (!igemm_grid_ok(cp, split)) {
+    err = "IGEMM grid exceeds the launch limits (row tiles or group * split above 65535)";
+    return FUSEDCONV_ERR_ROUTE;
+  }
+  p.split_k = split;
+  p.workspace = split > 1 ? (size_t)split * cp.M * cp.P * sizeof(float) : 0;
+  snprintf(p.name, sizeof(p.name), "igemm_%s_bm%d_bn%d%s", g.dtype == FUSEDCONV_F16 ? "f16" : "f32",
+           bm, kBN, split > 1 ? "_splitk" : "");
+  return FUSEDCONV_OK;
+}
+
+}  // namespace
+
+int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std::string& err) {
+  memset(&p, 0, sizeof(p));
+  p.split_k = 1;
+  const ConvParams& cp = g.cp;
+  if (split_req < 0) {
+    err = "split_k must be >= 0";
+    return FUSEDCONV_ERR_ROUTE;
+  }
+  if (route < FUSEDCONV_ROUTE_AUTO || route > FUSEDCONV_ROUTE_IGEMM_HALO) {
+    err = "unknown route";
+    return FUSEDCONV_ERR_ROUTE;
+  }
+  if (split_req > 1 && route != FUSEDCONV_ROUTE_IGEMM && route != FUSEDCONV_ROUTE_AUTO) {
+    err = "split_k applies to the IGEMM route only";
+    return FUSEDCONV_ERR_ROUTE;
+  }
+  int32_t th = 0, tw = 0;
+  size_t halo_ws = 0;
+  if (route == FUSEDCONV_ROUTE_AUTO) {
+    if (split_req > 1) route = FUSEDCONV_ROUTE_IGEMM;
+    else if (cp.Cg == 1 && depthwise_fits(cp, th, tw)) route = FUSEDCONV_ROUTE_DEPTHWISE;
+    else if (igemm_halo_fits(cp, g.dtype, th, tw, halo_ws)) route = FUSEDCONV_ROUTE_IGEMM_HALO;
+    else if (cp.K >= 8 && cp.Mg >= 8 && igemm_grid_ok(cp, 1)) route = FUSEDCONV_ROUTE_IGEMM;
+    else route = FUSEDCONV_ROUTE_DIRECT;
+  }
+  switch (route) {
+    case FUSEDCONV_ROUTE_DIRECT:
+      p.route = route;
+      snprintf(p.name, sizeof(p.name), "direct_%s", g.dtype == FUSEDCONV_F16 ? "f16" : "f32");
+      return FUSEDCONV_OK;
+    case FUSEDCONV_ROUTE_IGEMM:
+      return plan_igemm(g, split_req, p, err);
+    case FUSEDCONV_ROUTE_DEPTHWISE:
+      if (cp.Cg != 1 || !depthwise_fits(cp, th, tw)) {
+        err = "DEPTHWISE needs one input channel per group, at most 2 spatial dims and a "
+              "halo tile that fits in LDS";
+        return FUSEDCONV_ERR_ROUTE;
+      }
+      p.route = route;
+      p.tile_h = th;
+      p.tile_w = tw;
+      snprintf(p.name, sizeof(p.name), "depthwise_%s_t%dx%d",
+               g.dtype == FUSEDCONV_F16 ? "f16" : "f32", th, tw);
+      return FUSEDCONV_OK;
+    case FUSEDCONV_ROUTE_IGEMM_HALO:
+      if (!igemm_halo_fits(cp, g.dtype, th, tw, halo_ws)) {
+        err = "IGEMM_HALO needs fp16, C/group >= 32, at most 64 taps and a halo box that fits "
+              "in LDS";
+        return FUSEDCONV_ERR_ROUTE;
+      }
+      p.route = route;
+      p.tile_h = th;
+      p.tile_w = tw;
+      p.workspace = halo_ws;
+      snprintf(p.name, sizeof(p.name), "igemm_halo_f16_t%dx%d", th, tw);
+      return FUSEDCONV_OK;
+    default:
+      err = "unknown route";
+      return FUSEDCONV_ERR_ROUTE;
+  }
+}
+
+}  // namespace fc

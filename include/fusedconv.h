@@ -1,0 +1,193 @@
+/*
+ * fusedconv.h -- C ABI of the MI355X (gfx950) FusedConv library.
+ *
+ * FusedConv computes, for 1 to 3 spatial dimensions in NCHW / NCDHW layout,
+ *
+ *     Y = act(conv(X, W; strides, pads or auto_pad, dilations, group) + B + Z)
+ *
+ * (FusedConv README, "Description", "Inputs", "Outputs", "Attributes";
+ * FusedConv manifest.json, "inputs", "outputs", "attributes",
+ * "attributeConstraints", "typeConstraints").  B (bias, one value per output
+ * channel) and Z (residual, same shape as Y) are optional; both are added
+ * before the activation.  The convolution is a cross-correlation: output o
+ * reads input o*stride - pad_begin + tap*dilation on every axis, and input
+ * coordinates outside the tensor read as zero.  Output channel m reads input
+ * channels [g*C/group, (g+1)*C/group) with g = m / (M/group).  Accumulation
+ * is fp32 for both element types; an fp16 result is rounded once
+ * (round-to-nearest-even) when stored.
+ *
+ * Lifecycle: fill a fusedconv_desc (start from fusedconv_desc_init), call
+ * fusedconv_create -- it validates everything on the host, touches no device
+ * and allocates no device memory -- then call fusedconv_run any number of
+ * times with device pointers, and finally fusedconv_destroy.
+ *
+ * Errors: every function returns FUSEDCONV_OK (0) or a negative
+ * FUSEDCONV_ERR_* code; nothing is thrown across the boundary.  A failing
+ * call leaves a description in fusedconv_last_error() (per thread).  All
+ * checks except FUSEDCONV_ERR_LAUNCH happen before any kernel is launched.
+ */
+#ifndef FUSEDCONV_H
+#define FUSEDCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FUSEDCONV_MAX_RANK 8
+
+/* Element type T, shared by X, W, B, Z and Y (manifest "typeConstraints"). */
+typedef enum fusedconv_dtype {
+  FUSEDCONV_F32 = 0,
+  FUSEDCONV_F16 = 1
+} fusedconv_dtype;
+
+/*
+ * Kernel route.  AUTO lets the planner choose; the others force one route
+ * (used by tests and tuning).  A forced route that cannot run the problem
+ * makes fusedconv_create fail with FUSEDCONV_ERR_ROUTE.
+ *   DIRECT     one output element per lane, any problem.
+ *   IGEMM      implicit GEMM on MFMA with im2col tiles gathered into LDS,
+ *              any problem; supports split-K.
+ *   DEPTHWISE  grouped direct kernel with one input channel per group
+ *              (C/group == 1), 1 or 2 spatial dims, LDS halo tiles.
+ *   IGEMM_HALO implicit GEMM on MFMA, fp16 only, whose input tile is one
+ *              channel-last halo box per 32 input channels; needs
+ *              C/group >= 32 and at most 64 kernel taps.
+ */
+typedef enum fusedconv_route {
+  FUSEDCONV_ROUTE_AUTO = 0,
+  FUSEDCONV_ROUTE_DIRECT = 1,
+  FUSEDCONV_ROUTE_IGEMM = 2,
+  FUSEDCONV_ROUTE_DEPTHWISE = 3,
+  FUSEDCONV_ROUTE_IGEMM_HALO = 4
+} fusedconv_route;
+
+/* Shape of one tensor.  present = 0 means the (optional) input is absent. */
+typedef struct fusedconv_tensor {
+  int32_t present;
+  int32_t rank;
+  int64_t dims[FUSEDCONV_MAX_RANK];
+} fusedconv_tensor;
+
+/*
+ * Problem description.  Attribute lists are (pointer, count) pairs; a NULL
+ * pointer means the attribute is absent (its default applies), a non-NULL
+ * pointer means present with `count` entries, which must match the spatial
+ * rank (manifest derive kernelShapeLengthOk, stridesLengthOk,
+ * dilationsLengthOk, padsLengthOk).  The library copies everything it needs
+ * during fusedconv_create; the caller's arrays and strings need not outlive
+ * that call.
+ */
+typedef struct fusedconv_desc {
+  int32_t dtype;              /* fusedconv_dtype */
+  fusedconv_tensor x;         /* (N, C, D1..Dn), n = 1..3, required */
+  fusedconv_tensor w;         /* (M, C/group, k1..kn), required */
+  fusedconv_tensor bias;      /* optional, rank 1, length M */
+  fusedconv_tensor z;         /* optional, exactly the shape of Y */
+  const char* auto_pad;       /* NULL = "NOTSET"; or SAME_UPPER, SAME_LOWER, VALID */
+  int64_t group;              /* default 1 */
+  const int64_t* kernel_shape; int32_t n_kernel_shape;  /* must match W if present */
+  const int64_t* strides;      int32_t n_strides;       /* default all 1, values >= 1 */
+  const int64_t* dilations;    int32_t n_dilations;     /* default all 1, values >= 1 */
+  const int64_t* pads;         int32_t n_pads;          /* ONNX order [begins..., ends...],
+                                                           values >= 0, only with NOTSET */
+  const char* activation;     /* NULL = none; Relu, LeakyRelu, Sigmoid, Tanh, HardSigmoid,
+                                 HardSwish, Clip, QuickGelu, Elu, Gelu, FastGelu, Softplus,
+                                 ThresholdedRelu, Erf */
+  const float* activation_params; int32_t n_activation_params;
+                              /* LeakyRelu: exactly [alpha]; HardSigmoid: exactly [alpha, beta];
+                                 Clip: exactly [min, max]; QuickGelu, Elu, ThresholdedRelu:
+                                 optional [alpha] (defaults 1.702, 1.0, 1.0); Gelu: optional
+                                 [approximate] (0 = erf form, nonzero = tanh form); ignored by
+                                 the parameter-free activations (README "Attributes",
+                                 manifest derive activationParamsOk, actAlpha, actBeta) */
+  int32_t route;              /* fusedconv_route; 0 = planner's choice */
+  int32_t split_k;            /* 0 = planner's choice; >= 1 forces the K split (IGEMM only) */
+} fusedconv_desc;
+
+/* Status codes.  The cited passage is the rule the check enforces. */
+enum {
+  FUSEDCONV_OK = 0,
+  FUSEDCONV_ERR_NULL_ARG = -1,            /* a required pointer is NULL */
+  FUSEDCONV_ERR_DTYPE = -2,               /* T not float32/float16 (typeConstraints) */
+  FUSEDCONV_ERR_RANK = -3,                /* ranks of X/W/Y differ or spatial rank not 1..3
+                                             (derive spatialAttributesOk, *RanksOk) */
+  FUSEDCONV_ERR_ATTR_LENGTH = -4,         /* attribute list length (derive *LengthOk) */
+  FUSEDCONV_ERR_ATTR_VALUE = -5,          /* stride/dilation < 1, pad < 0, kernel extent < 1
+                                             (derive stridesValuesOk, dilationsValuesOk,
+                                             padsValuesOk, kernelExtentsOk), bad auto_pad */
+  FUSEDCONV_ERR_PADS_WITH_AUTO_PAD = -6,  /* pads given with an automatic mode
+                                             (derive explicitPadsOk) */
+  FUSEDCONV_ERR_KERNEL_SHAPE = -7,        /* kernel_shape differs from W (kernelShapeMatchesWeights) */
+  FUSEDCONV_ERR_GROUP = -8,               /* group < 1, M % group, W.dim1 * group != C (groupOk) */
+  FUSEDCONV_ERR_BIAS_SHAPE = -9,          /* bias not rank 1 of length M (biasOk) */
+  FUSEDCONV_ERR_Z_SHAPE = -10,            /* Z shape differs from Y (zOk) */
+  FUSEDCONV_ERR_ACTIVATION = -11,         /* unknown activation name (activationOk) */
+  FUSEDCONV_ERR_ACTIVATION_PARAMS = -12,  /* wrong number of parameters (activationParamsOk) */
+  FUSEDCONV_ERR_OUTPUT_SHAPE = -13,       /* an output dim < 1, or a zero-sized input */
+  FUSEDCONV_ERR_WORKSPACE = -14,          /* workspace missing or smaller than required */
+  FUSEDCONV_ERR_ALIGNMENT = -15,          /* a device pointer is not 16-byte aligned */
+  FUSEDCONV_ERR_ROUTE = -16,              /* forced route / split cannot run this problem */
+  FUSEDCONV_ERR_LAUNCH = -17,             /* a HIP call or kernel launch failed */
+  FUSEDCONV_ERR_DEVICE = -18,             /* current device is not a gfx950 GPU */
+  FUSEDCONV_ERR_ALLOC = -19,              /* host allocation of the handle failed */
+  FUSEDCONV_ERR_TOO_LARGE = -20           /* a tensor exceeds the library's index limits */
+};
+
+typedef struct fusedconv_handle fusedconv_handle;  /* opaque, host memory only */
+
+/* Fill *d with "absent" for every optional field, group = 1, dtype f32. */
+void fusedconv_desc_init(fusedconv_desc* d);
+
+/*
+ * Validate and resolve the problem (padding, output dims, activation
+ * parameters) and plan the kernels.  Host only: no device call, no device
+ * allocation.  On success *out owns a new handle; on failure *out is NULL.
+ */
+int fusedconv_create(const fusedconv_desc* d, fusedconv_handle** out);
+
+/* Y's shape: *rank = rank of X, dims[0..rank) filled. */
+int fusedconv_output_shape(const fusedconv_handle* h, int64_t dims[FUSEDCONV_MAX_RANK],
+                           int32_t* rank);
+
+/* Device workspace bytes fusedconv_run needs (0 if none). */
+int fusedconv_workspace_size(const fusedconv_handle* h, size_t* bytes);
+
+/*
+ * Chosen plan: route (fusedconv_route), K split factor, and a short
+ * NUL-terminated kernel name written into name[0..name_len) (may be NULL).
+ */
+int fusedconv_plan_info(const fusedconv_handle* h, int32_t* route, int32_t* split_k, char* name,
+                        size_t name_len);
+
+/*
+ * Enqueue the computation on `stream` (a hipStream_t; NULL = the default
+ * stream) and return without waiting.  x, w, y: device pointers, contiguous,
+ * 16-byte aligned.  bias / z: device pointers iff the descriptor declared
+ * them present, else NULL.  workspace: at least fusedconv_workspace_size()
+ * bytes of device memory (may be NULL if that is 0), 16-byte aligned, owned
+ * by the caller and not used by another run at the same time.  Y must not
+ * overlap X, W, B or the workspace; Y may be the same buffer as Z
+ * (in-place residual).  The caller owns every buffer and the stream; the
+ * library allocates nothing on the device.
+ */
+int fusedconv_run(const fusedconv_handle* h, const void* x, const void* w, const void* bias,
+                  const void* z, void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Release a handle (NULL is allowed). */
+void fusedconv_destroy(fusedconv_handle* h);
+
+/* Static text for a status code. */
+const char* fusedconv_status_string(int status);
+
+/* Detail text of the calling thread's last failing call ("" if none). */
+const char* fusedconv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FUSEDCONV_H */

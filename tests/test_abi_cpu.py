@@ -1,0 +1,190 @@
+"""C-ABI checks that need no GPU: the library loads, exports what the header
+declares, and its host-side resolver and planner behave (FusedConv manifest
+derive rules; README "Attributes").  No compute call is made here."""
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+import convolution_implicit_gemm_amd as fc
+from convolution_implicit_gemm_amd import _binding as B
+from oracle import oracle
+from workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def setup_module(module):
+    oracle.build(force=False)
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "fusedconv.h")).read()
+    declared = set(re.findall(r"^(?:int|void|const char\*)\s+(fusedconv_[a-z_]+)\s*\(", header,
+                              re.M))
+    assert declared == set(B.EXPORTS)
+    lib = ctypes.CDLL(fc.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = fc.load()
+    for code in B.STATUS:
+        assert lib.fusedconv_status_string(code)
+    assert lib.fusedconv_status_string(12345) == b"unknown status"
+
+
+def _h(x, w, dtype="f32", b=None, z=None, **kw):
+    return B.Handle(dtype, x, w, b, z, **kw)
+
+
+def test_output_shapes_match_oracle_sweep():
+    rng = np.random.default_rng(3)
+    n_checked = 0
+    for nsp in (1, 2, 3):
+        for mode in ("NOTSET", "SAME_UPPER", "SAME_LOWER", "VALID"):
+            for _ in range(60):
+                ins = [int(v) for v in rng.integers(1, 20, nsp)]
+                ks = [int(v) for v in rng.integers(1, 7, nsp)]
+                ss = [int(v) for v in rng.integers(1, 5, nsp)]
+                ds = [int(v) for v in rng.integers(1, 4, nsp)]
+                pads = [int(v) for v in rng.integers(0, 4, 2 * nsp)] if mode == "NOTSET" else None
+                ref = oracle.output_dims(ins, ks, ss, ds, mode, pads)
+                kw = dict(strides=ss, dilations=ds, auto_pad=mode, pads=pads)
+                if ref is None:
+                    with pytest.raises(B.FusedConvError) as e:
+                        _h([2, 3] + ins, [4, 3] + ks, **kw)
+                    assert e.value.status == "FUSEDCONV_ERR_OUTPUT_SHAPE"
+                else:
+                    h = _h([2, 3] + ins, [4, 3] + ks, **kw)
+                    assert h.y_shape == [2, 4] + ref[0]
+                n_checked += 1
+    assert n_checked == 720
+
+
+def test_workload_shapes_and_routes():
+    for name, wl in WORKLOADS.items():
+        h = B.Handle(wl["dtype"], wl["x"], wl["w"], wl["b"], wl["z"], **wl["attrs"])
+        assert h.y_shape == wl["y"], name
+        assert h.route in ("direct", "igemm", "depthwise", "igemm_halo"), name
+        if wl["attrs"].get("group", 1) == wl["x"][1]:
+            assert h.route == "depthwise", name
+
+
+def test_readme_example():
+    h = _h([1, 32, 8, 8], [32, 32, 1, 1])
+    assert h.y_shape == [1, 32, 8, 8]
+
+
+ERR_CASES = [
+    # (kwargs for Handle, expected status)
+    (dict(dtype=7), "FUSEDCONV_ERR_DTYPE"),
+    (dict(x=[1, 3, 8, 8, 8, 8]), "FUSEDCONV_ERR_RANK"),
+    (dict(x=[1, 3]), "FUSEDCONV_ERR_RANK"),
+    (dict(w=[4, 3, 3]), "FUSEDCONV_ERR_RANK"),
+    (dict(strides=[1]), "FUSEDCONV_ERR_ATTR_LENGTH"),
+    (dict(dilations=[1, 1, 1]), "FUSEDCONV_ERR_ATTR_LENGTH"),
+    (dict(pads=[1, 1]), "FUSEDCONV_ERR_ATTR_LENGTH"),
+    (dict(kernel_shape=[3]), "FUSEDCONV_ERR_ATTR_LENGTH"),
+    (dict(kernel_shape=[3, 2]), "FUSEDCONV_ERR_KERNEL_SHAPE"),
+    (dict(strides=[0, 1]), "FUSEDCONV_ERR_ATTR_VALUE"),
+    (dict(dilations=[1, -1]), "FUSEDCONV_ERR_ATTR_VALUE"),
+    (dict(pads=[0, 0, -1, 0]), "FUSEDCONV_ERR_ATTR_VALUE"),
+    (dict(auto_pad="SAME"), "FUSEDCONV_ERR_ATTR_VALUE"),
+    (dict(w=[4, 3, 0, 3]), "FUSEDCONV_ERR_ATTR_VALUE"),
+    (dict(auto_pad="VALID", pads=[0, 0, 0, 0]), "FUSEDCONV_ERR_PADS_WITH_AUTO_PAD"),
+    (dict(auto_pad="SAME_UPPER", pads=[1, 1, 1, 1]), "FUSEDCONV_ERR_PADS_WITH_AUTO_PAD"),
+    (dict(group=0), "FUSEDCONV_ERR_GROUP"),
+    (dict(group=2), "FUSEDCONV_ERR_GROUP"),                  # 3 channels, w.dim1 = 3
+    (dict(x=[1, 6, 8, 8], w=[3, 3, 3, 3], group=2), "FUSEDCONV_ERR_GROUP"),  # M % group
+    (dict(b=[5]), "FUSEDCONV_ERR_BIAS_SHAPE"),
+    (dict(b=[4, 1]), "FUSEDCONV_ERR_BIAS_SHAPE"),
+    (dict(z=[1, 4, 8, 8]), "FUSEDCONV_ERR_Z_SHAPE"),
+    (dict(z=[1, 4, 36]), "FUSEDCONV_ERR_Z_SHAPE"),
+    (dict(activation="Swish"), "FUSEDCONV_ERR_ACTIVATION"),
+    (dict(activation="relu"), "FUSEDCONV_ERR_ACTIVATION"),
+    (dict(activation="LeakyRelu"), "FUSEDCONV_ERR_ACTIVATION_PARAMS"),
+    (dict(activation="LeakyRelu", activation_params=[0.1, 0.2]), "FUSEDCONV_ERR_ACTIVATION_PARAMS"),
+    (dict(activation="HardSigmoid", activation_params=[0.2]), "FUSEDCONV_ERR_ACTIVATION_PARAMS"),
+    (dict(activation="Clip"), "FUSEDCONV_ERR_ACTIVATION_PARAMS"),
+    (dict(activation="QuickGelu", activation_params=[1.0, 2.0]), "FUSEDCONV_ERR_ACTIVATION_PARAMS"),
+    (dict(activation="Gelu", activation_params=[0.0, 1.0]), "FUSEDCONV_ERR_ACTIVATION_PARAMS"),
+    (dict(x=[1, 3, 2, 2]), "FUSEDCONV_ERR_OUTPUT_SHAPE"),    # 3x3 kernel, no pads
+    (dict(x=[0, 3, 8, 8]), "FUSEDCONV_ERR_OUTPUT_SHAPE"),
+    (dict(x=[1, 3, 0, 8]), "FUSEDCONV_ERR_OUTPUT_SHAPE"),
+    (dict(x=[1, 3, 8, 8], w=[0, 3, 3, 3]), "FUSEDCONV_ERR_OUTPUT_SHAPE"),
+    (dict(x=[1, 3, 1 << 20, 1 << 12]), "FUSEDCONV_ERR_TOO_LARGE"),
+    (dict(route="depthwise"), "FUSEDCONV_ERR_ROUTE"),         # C/group == 3
+    (dict(route="direct", split_k=2), "FUSEDCONV_ERR_ROUTE"),
+    (dict(route="igemm", split_k=100), "FUSEDCONV_ERR_ROUTE"),  # more splits than K tiles
+    (dict(route=9), "FUSEDCONV_ERR_ROUTE"),
+]
+
+
+@pytest.mark.parametrize("case,status", ERR_CASES)
+def test_every_rejection(case, status):
+    case = dict(case)
+    dtype = case.pop("dtype", "f32")
+    x = case.pop("x", [1, 3, 8, 8])
+    w = case.pop("w", [4, 3, 3, 3])
+    b = case.pop("b", None)
+    z = case.pop("z", None)
+    with pytest.raises(B.FusedConvError) as e:
+        B.Handle(dtype, x, w, b, z, **case)
+    assert e.value.status == status, str(e.value)
+    assert fc.load().fusedconv_last_error()  # detail text set
+
+
+def test_parameter_free_activations_ignore_params():
+    for act in ("Relu", "Sigmoid", "Tanh", "HardSwish", "FastGelu", "Softplus", "Erf"):
+        _h([1, 3, 8, 8], [4, 3, 3, 3], activation=act, activation_params=[1.0, 2.0, 3.0])
+
+
+def test_optional_params_and_empty_list():
+    for act in ("QuickGelu", "Elu", "ThresholdedRelu", "Gelu"):
+        _h([1, 3, 8, 8], [4, 3, 3, 3], activation=act)
+        _h([1, 3, 8, 8], [4, 3, 3, 3], activation=act, activation_params=[])
+        _h([1, 3, 8, 8], [4, 3, 3, 3], activation=act, activation_params=[0.5])
+
+
+def test_attribute_present_with_zero_length_is_a_length_error():
+    with pytest.raises(B.FusedConvError) as e:
+        _h([1, 3, 8, 8], [4, 3, 3, 3], strides=[])
+    assert e.value.status == "FUSEDCONV_ERR_ATTR_LENGTH"
+
+
+def test_null_arguments():
+    lib = fc.load()
+    h = ctypes.c_void_p()
+    assert lib.fusedconv_create(None, ctypes.byref(h)) == -1
+    d = B.Desc()
+    lib.fusedconv_desc_init(ctypes.byref(d))
+    assert d.group == 1 and d.x.present == 0
+    assert lib.fusedconv_create(ctypes.byref(d), ctypes.byref(h)) == -1  # x, w absent
+    assert not h.value
+    hd = _h([1, 3, 8, 8], [4, 3, 3, 3], b=[4])
+    # run-time argument checks happen on the host before any device call
+    assert lib.fusedconv_run(hd._h, None, None, None, None, None, None, 0, None) == -1
+    assert lib.fusedconv_run(hd._h, 16, 16, None, None, 16, None, 0, None) == -1  # bias missing
+    assert lib.fusedconv_run(hd._h, 16, 16, 8, None, 16, None, 0, None) == -15    # misaligned
+    lib.fusedconv_destroy(None)
+
+
+def test_forced_routes_and_split_plan():
+    h = _h([2, 8, 9, 9], [8, 1, 3, 3], group=8, route="depthwise")
+    assert h.route == "depthwise"
+    h = _h([2, 8, 9, 9], [8, 1, 3, 3], group=8, route="direct")
+    assert h.route == "direct"
+    h = _h([1, 512, 8, 8], [64, 512, 3, 3], pads=[1, 1, 1, 1])  # starved grid, K = 4608
+    assert h.route == "igemm" and h.split_k > 1
+    assert h.workspace_bytes == h.split_k * 64 * 64 * 4
+    h = _h([1, 512, 8, 8], [64, 512, 3, 3], pads=[1, 1, 1, 1], split_k=1)
+    assert h.split_k == 1 and h.workspace_bytes == 0
+    h = _h([1, 16, 8, 8], [16, 16, 3, 3], route="igemm", split_k=3)
+    assert h.split_k == 3  # K = 144 -> 5 tiles of 32 -> slices of 2, 2, 1
+    h = _h([1, 16, 8, 8], [16, 16, 3, 3], route="igemm", split_k=5)
+    assert h.split_k == 5

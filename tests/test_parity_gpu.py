@@ -1,0 +1,269 @@
+"""GPU parity: the HIP path against the oracle, element by element.
+
+Tolerance (stated for this path): max|Y_gpu - Y_ref| <= tau * max|Y_ref| with
+tau = 1e-4 for fp32 and 2e-2 for fp16 (fp32 accumulation, one fp16 rounding
+of the output), Y_ref being the oracle's unrounded double result on the same
+inputs.  Small cases compare every element; the full-size workloads compare
+sampled outputs (the oracle computes them one by one) in the launch
+configuration the benchmark times.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import convolution_implicit_gemm_amd as fc
+from convolution_implicit_gemm_amd import _binding as B
+from oracle import oracle
+from workloads import WORKLOADS, make_inputs, random_tensors
+
+pytestmark = pytest.mark.gpu
+TAU = {"f32": 1e-4, "f16": 2e-2}
+ACTS = [(None, None), ("Relu", None), ("LeakyRelu", [0.1]), ("Sigmoid", None), ("Tanh", None),
+        ("HardSigmoid", [0.2, 0.5]), ("HardSwish", None), ("Clip", [-0.5, 1.5]),
+        ("QuickGelu", [1.702]), ("Elu", [0.8]), ("Gelu", None), ("Gelu", [1.0]),
+        ("FastGelu", None), ("Softplus", None), ("ThresholdedRelu", [0.3]), ("Erf", None)]
+
+
+def log(msg):
+    sys.__stderr__.write(msg + "\n")
+    sys.__stderr__.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    assert name.startswith("gfx950"), name
+    fc.load()  # fails loudly when the library is not built
+    oracle.build(force=False)
+
+
+def f32params(p):
+    return None if p is None else [float(np.float32(v)) for v in p]
+
+
+def dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_gpu(x, w, b, z, **kw):
+    y = fc.fused_conv(dev(x), dev(w), dev(b), dev(z), **kw)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def check(got, ref, dtype, what):
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    g = got.astype(np.float64)
+    assert np.all(np.isfinite(g)), what
+    scale = max(np.max(np.abs(ref)), 1e-30)
+    err = np.max(np.abs(g - ref)) / scale
+    assert err <= TAU[dtype], f"{what}: rel err {err:.3e} > {TAU[dtype]}"
+    return err
+
+
+def case_attrs(rng, nsp, allow_group=True):
+    group = int(rng.choice([1, 2, 3])) if allow_group else 1
+    cg = int(rng.integers(3, 24))
+    mg = int(rng.integers(5, 45))
+    ks = [int(v) for v in rng.integers(1, 4, nsp)]
+    ins = [int(v) for v in rng.integers(5, 14 if nsp == 3 else (22 if nsp == 2 else 300), nsp)]
+    ss = [int(v) for v in rng.integers(1, 3, nsp)]
+    ds = [int(v) for v in rng.integers(1, 3, nsp)]
+    mode = str(rng.choice(["NOTSET", "SAME_UPPER", "SAME_LOWER", "VALID"]))
+    pads = [int(v) for v in rng.integers(0, 3, 2 * nsp)] if mode == "NOTSET" else None
+    for i in range(nsp):
+        ins[i] = max(ins[i], (ks[i] - 1) * ds[i] + 1)
+    return dict(n=int(rng.integers(1, 4)), C=cg * group, M=mg * group, group=group, ks=ks,
+                ins=ins, strides=ss, dilations=ds, auto_pad=mode, pads=pads)
+
+
+def run_case(c, dtype, seed, route, split_k=0, act=(None, None), bias=True, resid=True):
+    x_shape = [c["n"], c["C"]] + c["ins"]
+    w_shape = [c["M"], c["C"] // c["group"]] + c["ks"]
+    out = oracle.output_dims(c["ins"], c["ks"], c["strides"], c["dilations"], c["auto_pad"],
+                             c["pads"])
+    y_shape = [c["n"], c["M"]] + out[0]
+    x, w, b, z = random_tensors(seed, dtype, x_shape, w_shape, [c["M"]] if bias else None,
+                                y_shape if resid else None)
+    attrs = dict(group=c["group"], strides=c["strides"], dilations=c["dilations"],
+                 auto_pad=c["auto_pad"], pads=c["pads"], activation=act[0],
+                 activation_params=f32params(act[1]))
+    what = f"seed={seed} route={route} split={split_k} dtype={dtype} x={x_shape} w={w_shape} {attrs}"
+    log("CASE " + what)
+    got = run_gpu(x, w, b, z, route=route, split_k=split_k, **attrs)
+    ref = oracle.fusedconv(x, w, b, z, **attrs)
+    return check(got, ref, dtype, what)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("nsp", [1, 2, 3])
+@pytest.mark.parametrize("route", ["direct", "igemm"])
+def test_routes_random_small(route, nsp, dtype):
+    rng = np.random.default_rng([1000, nsp, len(route), dtype == "f16"])
+    for trial in range(6):
+        c = case_attrs(rng, nsp)
+        act = ACTS[int(rng.integers(0, len(ACTS)))]
+        run_case(c, dtype, [2000, nsp, trial, len(route)], route, act=act,
+                 bias=trial % 3 != 1, resid=trial % 3 != 2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("split", [2, 3, 7])
+def test_igemm_forced_split(split, dtype):
+    rng = np.random.default_rng([3000, split])
+    for trial in range(3):
+        c = case_attrs(rng, 2)
+        c["C"] = c["group"] * 40  # K = 40 * taps >= 7 tiles of 32 when taps >= 6
+        c["ks"] = [3, 3]
+        c["ins"] = [max(v, 5) for v in c["ins"]]
+        run_case(c, dtype, [3001, split, trial], "igemm", split_k=split,
+                 act=ACTS[trial * 5 % len(ACTS)])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("act", ACTS, ids=[str(a[0]) + str(a[1] or "") for a in ACTS])
+def test_every_activation(act, dtype):
+    c = dict(n=2, C=24, M=40, group=1, ks=[3, 3], ins=[13, 17], strides=[1, 1],
+             dilations=[1, 1], auto_pad="SAME_UPPER", pads=None)
+    for route in ("igemm", "direct"):
+        run_case(c, dtype, [4000, ACTS.index(act)], route, act=act)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_depthwise_route(dtype):
+    rng = np.random.default_rng(5000)
+    for trial in range(10):
+        nsp = 1 if trial % 4 == 3 else 2
+        C = int(rng.integers(3, 40))
+        mult = int(rng.choice([1, 1, 2]))
+        ks = [int(v) for v in rng.integers(1, 8, nsp)]
+        ds = [int(v) for v in rng.integers(1, 3, nsp)]
+        ins = [int(v) for v in rng.integers(5, 70 if nsp == 2 else 3000, nsp)]
+        for i in range(nsp):
+            ins[i] = max(ins[i], (ks[i] - 1) * ds[i] + 1)
+        mode = str(rng.choice(["NOTSET", "SAME_UPPER", "SAME_LOWER", "VALID"]))
+        c = dict(n=int(rng.integers(1, 3)), C=C, M=C * mult, group=C, ks=ks, ins=ins,
+                 strides=[int(v) for v in rng.integers(1, 3, nsp)], dilations=ds, auto_pad=mode,
+                 pads=[int(v) for v in rng.integers(0, 4, 2 * nsp)] if mode == "NOTSET" else None)
+        run_case(c, dtype, [5001, trial], "depthwise", act=ACTS[trial % len(ACTS)],
+                 bias=trial % 2 == 0, resid=trial % 3 == 0)
+
+
+@pytest.mark.parametrize("route", ["direct", "igemm", "depthwise"])
+def test_edge_shapes(route):
+    cases = [
+        # 1x1 kernel, stride 2 (pure subsample + channel mix)
+        dict(n=1, C=5, M=7, group=1, ks=[1, 1], ins=[9, 11], strides=[2, 2], dilations=[1, 1],
+             auto_pad="NOTSET", pads=None),
+        # kernel as large as the input: 1x1 output
+        dict(n=2, C=3, M=4, group=1, ks=[5, 6], ins=[5, 6], strides=[1, 1], dilations=[1, 1],
+             auto_pad="VALID", pads=None),
+        # stride larger than the kernel, big asymmetric pads
+        dict(n=1, C=4, M=4, group=1, ks=[2, 2], ins=[10, 10], strides=[5, 3], dilations=[1, 1],
+             auto_pad="NOTSET", pads=[3, 0, 0, 4]),
+        # single channel, single output channel
+        dict(n=3, C=1, M=1, group=1, ks=[3, 3], ins=[7, 7], strides=[1, 1], dilations=[2, 2],
+             auto_pad="SAME_LOWER", pads=None),
+        # pads wider than the kernel span
+        dict(n=1, C=2, M=2, group=1, ks=[2, 1], ins=[3, 4], strides=[1, 1], dilations=[1, 1],
+             auto_pad="NOTSET", pads=[4, 4, 4, 4]),
+    ]
+    for i, c in enumerate(cases):
+        if route == "depthwise":
+            c = dict(c, M=c["C"], group=c["C"])
+        for dtype in ("f32", "f16"):
+            run_case(c, dtype, [6000, i], route, act=ACTS[(3 * i) % len(ACTS)])
+
+
+def test_starved_grid_splits_and_matches_unsplit():
+    c = dict(n=1, C=512, M=64, group=1, ks=[3, 3], ins=[8, 8], strides=[1, 1],
+             dilations=[1, 1], auto_pad="NOTSET", pads=[1, 1, 1, 1])
+    x, w, b, z = random_tensors([7000], "f32", [1, 512, 8, 8], [64, 512, 3, 3], [64],
+                                [1, 64, 8, 8], w_std=1 / 48)
+    attrs = dict(pads=[1, 1, 1, 1], activation="Gelu")
+    h = B.Handle("f32", [1, 512, 8, 8], [64, 512, 3, 3], [64], [1, 64, 8, 8], **attrs)
+    assert h.split_k > 1
+    log(f"CASE starved split={h.split_k}")
+    ys = run_gpu(x, w, b, z, **attrs)
+    y1 = run_gpu(x, w, b, z, route="igemm", split_k=1, **attrs)
+    ref = oracle.fusedconv(x, w, b, z, **attrs)
+    check(ys, ref, "f32", "split")
+    check(y1, ref, "f32", "unsplit")
+    check(ys, y1.astype(np.float64), "f32", "split vs unsplit")
+
+
+@pytest.mark.parametrize("route", ["direct", "igemm", "depthwise"])
+def test_deterministic_and_inplace_residual(route):
+    C = 16
+    M, grp = (C, C) if route == "depthwise" else (24, 1)
+    x, w, b, z = random_tensors([8000], "f16", [2, C, 19, 23], [M, C // grp, 3, 3], [M],
+                                [2, M, 19, 23])
+    attrs = dict(group=grp, auto_pad="SAME_UPPER", activation="QuickGelu", route=route)
+    log(f"CASE determinism route={route}")
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    y1 = fc.fused_conv(xd, wd, bd, dev(z), **attrs)
+    y2 = fc.fused_conv(xd, wd, bd, dev(z), **attrs)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    # Y written into Z's buffer (in-place residual)
+    zd = dev(z)
+    op = fc.FusedConv([2, C, 19, 23], [M, C // grp, 3, 3], "f16", True, True,
+                      group=grp, auto_pad="SAME_UPPER", activation="QuickGelu", route=route)
+    y3 = op(xd, wd, bd, zd, out=zd)
+    torch.cuda.synchronize()
+    assert y3.data_ptr() == zd.data_ptr()
+    assert torch.equal(y3, y1)
+
+
+def test_run_errors_on_device():
+    h = B.Handle("f32", [1, 3, 8, 8], [4, 3, 3, 3], None, None)
+    x = torch.zeros(1 * 3 * 8 * 8 + 4, device="cuda")
+    w = torch.zeros(4 * 27, device="cuda")
+    y = torch.zeros(4 * 36, device="cuda")
+    with pytest.raises(B.FusedConvError) as e:
+        h.run(x.data_ptr() + 4, w.data_ptr(), None, None, y.data_ptr(), None, 0, 0)
+    assert e.value.status == "FUSEDCONV_ERR_ALIGNMENT"
+    hs = B.Handle("f32", [1, 512, 8, 8], [64, 512, 3, 3], None, None, pads=[1, 1, 1, 1],
+                  split_k=4)
+    with pytest.raises(B.FusedConvError) as e:
+        hs.run(x.data_ptr(), w.data_ptr(), None, None, y.data_ptr(), None, 0, 0)
+    assert e.value.status == "FUSEDCONV_ERR_WORKSPACE"
+    with pytest.raises(B.FusedConvError):
+        fc.fused_conv(torch.zeros(1, 3, 8, 8), torch.zeros(4, 3, 3, 3))  # host tensors
+
+
+def sample_indices(shape, count, seed):
+    """Random flat indices plus the corners and edges of the first/last planes."""
+    total = int(np.prod(shape))
+    rng = np.random.default_rng(seed)
+    idx = list(rng.integers(0, total, count))
+    sp = int(np.prod(shape[2:]))
+    for nm in (0, shape[0] * shape[1] - 1):
+        base = nm * sp
+        idx += [base, base + sp - 1, base + shape[-1] - 1, base + sp - shape[-1]]
+        idx += list(base + np.arange(0, min(sp, 64)))
+    return np.unique(np.asarray(idx, dtype=np.int64))
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_full_size_workloads(name):
+    wl = WORKLOADS[name]
+    log(f"CASE workload {name} x={wl['x']} w={wl['w']}")
+    inp = make_inputs(name)
+    attrs = dict(wl["attrs"])
+    attrs["activation_params"] = f32params(attrs.get("activation_params"))
+    got = run_gpu(inp["x"], inp["w"], inp["b"], inp["z"], **attrs)
+    assert list(got.shape) == wl["y"]
+    if got.size <= 1 << 16:
+        ref = oracle.fusedconv(inp["x"], inp["w"], inp["b"], inp["z"], **attrs)
+        check(got, ref, wl["dtype"], name)
+        return
+    idx = sample_indices(wl["y"], 6000, 9000)
+    ref = oracle.fusedconv_at(inp["x"], inp["w"], inp["b"], inp["z"], idx=idx, **attrs)
+    g = got.ravel()[idx].astype(np.float64)
+    assert np.all(np.isfinite(got)), name
+    # tau relative to the largest |Y_ref| among the sampled outputs
+    check(g, ref, wl["dtype"], name)
