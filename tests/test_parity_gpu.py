@@ -152,6 +152,37 @@ def test_depthwise_route(dtype):
                  bias=trial % 2 == 0, resid=trial % 3 == 0)
 
 
+HALO_CASES = [
+    # (x, w, attrs) for the channel-last halo route (fp16)
+    ([2, 64, 16, 16], [96, 64, 3, 3], dict(pads=[1, 1, 1, 1])),            # M tail (96 < 128)
+    ([2, 40, 13, 13], [64, 40, 3, 3], dict(pads=[1, 1, 1, 1])),            # partial channel
+    # block, W % 8 != 0 (scalar loader), OW % 4 != 0 (scalar epilogue)
+    ([1, 64, 24, 24], [64, 64, 2, 2], dict(strides=[2, 2])),               # patchify, stride 2
+    ([2, 64, 500], [64, 32, 5], dict(group=2, auto_pad="SAME_UPPER")),     # 1-D, 2 groups
+    ([1, 32, 6, 16, 16], [48, 32, 3, 3, 3], dict(pads=[1] * 6)),           # 3-D
+    ([2, 48, 21, 13], [40, 48, 3, 3], dict(dilations=[2, 1], auto_pad="SAME_LOWER")),
+    ([1, 64, 40, 40], [300, 64, 3, 3], dict(pads=[1, 1, 1, 1])),           # BM 256, 2 m tiles
+    ([2, 32, 34, 70], [64, 32, 5, 7], dict(strides=[1, 2], pads=[2, 3, 2, 3])),  # 35 taps
+]
+
+
+@pytest.mark.parametrize("ci", range(len(HALO_CASES)))
+def test_halo_route(ci):
+    xs, ws, attrs = HALO_CASES[ci]
+    h = B.Handle("f16", xs, ws, None, None, route="igemm_halo", **attrs)
+    y_shape = h.y_shape
+    for k, (bias, resid) in enumerate([(True, True), (False, False), (True, False)]):
+        act, params = ACTS[(5 * ci + 7 * k) % len(ACTS)]
+        x, w, b, z = random_tensors([9100, ci, k], "f16", xs, ws, [ws[0]] if bias else None,
+                                    y_shape if resid else None, dist="normal",
+                                    w_std=1.0 / np.sqrt(np.prod(ws[1:])))
+        a = dict(attrs, activation=act, activation_params=f32params(params))
+        log(f"CASE halo {ci} x={xs} w={ws} {a} bias={bias} z={resid}")
+        got = run_gpu(x, w, b, z, route="igemm_halo", **a)
+        ref = oracle.fusedconv(x, w, b, z, **a)
+        check(got, ref, "f16", f"halo case {ci}")
+
+
 @pytest.mark.parametrize("route", ["direct", "igemm", "depthwise"])
 def test_edge_shapes(route):
     cases = [
@@ -195,9 +226,9 @@ def test_starved_grid_splits_and_matches_unsplit():
     check(ys, y1.astype(np.float64), "f32", "split vs unsplit")
 
 
-@pytest.mark.parametrize("route", ["direct", "igemm", "depthwise"])
+@pytest.mark.parametrize("route", ["direct", "igemm", "depthwise", "igemm_halo"])
 def test_deterministic_and_inplace_residual(route):
-    C = 16
+    C = 16 if route != "igemm_halo" else 64
     M, grp = (C, C) if route == "depthwise" else (24, 1)
     x, w, b, z = random_tensors([8000], "f16", [2, C, 19, 23], [M, C // grp, 3, 3], [M],
                                 [2, M, 19, 23])
