@@ -51,6 +51,7 @@ struct HaloTile {
   int ncb;             // channel blocks
   int mgp;             // Wp rows per (tap, channel block): M/group rounded up to BM
   int vec_x;           // W % 8 == 0: 16-byte aligned 8-column groups
+  int ltw;             // log2(TW); tiles are one depth slice, TW and TH powers of two
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -231,13 +232,24 @@ __global__ __launch_bounds__(kThreads, 2) void halo_kernel(const half_t* __restr
   HALO_LOAD_X(0);
   store_x(0, 0);
   if (PFX && ncb > 1) HALO_LOAD_X(1);
-  half8 wf0[TM], wf1[TM];
+  // Step bookkeeping is incremental (uniform, scalar): the weight tile of
+  // step (cb, t) is Wp tile t * ncb + cb, the box offset of tap (kd, kh, kw)
+  // is ((kd*dd*BH + kh*dh)*BW + kw*dw) positions.
+  const int dkw = cp.dw * kLDC;
+  const int dkh = (cp.dh * ht.BW - (cp.KW - 1) * cp.dw) * kLDC;
+  const int dkd = (cp.dd * ht.BH * ht.BW - (cp.KH - 1) * cp.dh * ht.BW - (cp.KW - 1) * cp.dw) * kLDC;
+  const int64_t wtap = (int64_t)ncb * wstep;                 // next tap, same channel block
+  const int64_t wcb = wstep - (int64_t)(taps - 1) * ncb * wstep;  // next channel block, tap 0
+
+  // weight fragments: two register sets, prefetch distance one step
+  half8 wa[TM], wb[TM];
 #pragma unroll
-  for (int j = 0; j < TM; ++j) wf0[j] = *(const half8*)(wlane + j * 16 * kCB);
+  for (int j = 0; j < TM; ++j) wa[j] = *(const half8*)(wlane + j * 16 * kCB);
+  int64_t wnext = (taps > 1) ? wtap : wcb;                   // Wp offset of step 1
   __syncthreads();
 
-  // One step: (cb, t, box offset), current weights WC, prefetch target WN.
-#define HALO_STEP(WC, WN)                                                                \
+  int cb = 0, t = 0, kd = 0, kh = 0, kw = 0, toff = 0;
+#define HALO_STEP(WC, WN, HAS_NEXT)                                                      \
   {                                                                                      \
     if (t == taps - 1 && cb + 1 < ncb) {                                                 \
       if (!PFX) HALO_LOAD_X(cb + 1);                                                     \
@@ -245,79 +257,139 @@ __global__ __launch_bounds__(kThreads, 2) void halo_kernel(const half_t* __restr
       __syncthreads();                                                                   \
       if (PFX && cb + 2 < ncb) HALO_LOAD_X(cb + 2);                                      \
     }                                                                                    \
-    if (s + 1 < nsteps) {                                                                \
-      const int nt_ = t + 1 == taps ? 0 : t + 1;                                         \
-      const int ncb_ = t + 1 == taps ? cb + 1 : cb;                                      \
-      const half_t* src_ = wlane + (int64_t)(nt_ * ncb + ncb_) * wstep;                  \
-      _Pragma("unroll") for (int j = 0; j < TM; ++j) WN[j] = *(const half8*)(src_ + j * 16 * kCB); \
+    if (HAS_NEXT) {                                                                      \
+      const half_t* sn_ = wlane + wnext;                                                 \
+      _Pragma("unroll") for (int j = 0; j < TM; ++j) WN[j] = *(const half8*)(sn_ + j * 16 * kCB); \
     }                                                                                    \
-    const half_t* xs_ = lds + (cb & 1) * box +                                           \
-                        (((kd * cp.dd) * ht.BH + kh * cp.dh) * ht.BW + kw * cp.dw) * kLDC; \
-    _Pragma("unroll") for (int i = 0; i < TP; ++i) {                                     \
-      const half8 a_ = *(const half8*)(xs_ + aoff[i]);                                   \
+    const half_t* xs_ = lds + (cb & 1) * box + toff;                                     \
+    half8 a_[TP];                                                                        \
+    _Pragma("unroll") for (int i = 0; i < TP; ++i) a_[i] = *(const half8*)(xs_ + aoff[i]); \
+    _Pragma("unroll") for (int i = 0; i < TP; ++i)                                       \
       _Pragma("unroll") for (int j = 0; j < TM; ++j)                                     \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_, WC[j], acc[i][j], 0, 0, 0); \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_[i], WC[j], acc[i][j], 0, 0, 0); \
+    /* advance to the next step */                                                       \
+    if (++t == taps) {                                                                   \
+      t = kd = kh = kw = toff = 0;                                                       \
+      ++cb;                                                                              \
+    } else if (++kw < cp.KW) {                                                           \
+      toff += dkw;                                                                       \
+    } else if (kw = 0, ++kh < cp.KH) {                                                   \
+      toff += dkh;                                                                       \
+    } else {                                                                             \
+      kh = 0;                                                                            \
+      ++kd;                                                                              \
+      toff += dkd;                                                                       \
     }                                                                                    \
-    ++s;                                                                                 \
-    if (++kw == cp.KW) { kw = 0; if (++kh == cp.KH) { kh = 0; ++kd; } }                  \
-    if (++t == taps) { t = kd = kh = kw = 0; ++cb; }                                     \
+    /* Wp offset of the step after the new current one */                               \
+    wnext += (t == taps - 1) ? wcb : wtap;                                               \
   }
-  int s = 0, cb = 0, t = 0, kd = 0, kh = 0, kw = 0;
-  while (s < nsteps) {
-    HALO_STEP(wf0, wf1);
-    if (s >= nsteps) break;
-    HALO_STEP(wf1, wf0);
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    HALO_STEP(wa, wb, true);
+    HALO_STEP(wb, wa, s + 2 < nsteps);
   }
+  if (s < nsteps) HALO_STEP(wa, wb, false);
 #undef HALO_STEP
 #undef HALO_LOAD_X
 
   // ---- epilogue.  The accumulators go through LDS (the boxes are dead now)
-  // so that bias, residual and activation run in a rolled loop over rows of
-  // consecutive pixels: 8-byte Z loads and Y stores by consecutive lanes.
+  // one 16-channel block at a time: staged as 16 rows of consecutive pixels,
+  // Z is added into the stage with loads issued a pass ahead, then a rolled
+  // loop applies bias and activation and stores Y; consecutive lanes touch
+  // consecutive 8-byte pieces of a row.
   __syncthreads();
   constexpr int PW = BN / 2;              // pixels per wave
   constexpr int RP = PW + 4;              // fp32 row pitch (padded)
+  constexpr int GPR = PW / 4;             // 4-pixel groups per row
+  constexpr int ITER = 16 * GPR / 64;     // groups per lane per pass
   float* stage = (float*)lds + wave * 16 * RP;
   const bool vec_ok = (cp.OW & 3) == 0;
+  // per-lane slots of a pass: row (channel within the block) and 4 pixels
+  int slot_lds[ITER], slot_nv[ITER];
+  int64_t slot_y[ITER];                   // Y offset of the slot for channel block 0
+  const int mw = m0 + wmi * (BM / 2);     // first channel of this wave
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int idx = it * 64 + lane;
+    const int row = idx / GPR, p4 = (idx % GPR) * 4;
+    const int pl = wpi * PW + p4;
+    const int tw = pl % ht.TW, th = (pl / ht.TW) % ht.TH, td = pl / (ht.TW * ht.TH);
+    const int od = od0 + td, oh = oh0 + th, ow = ow0 + tw;
+    const bool ok = od < cp.OD && oh < cp.OH && ow < cp.OW;
+    slot_lds[it] = row * RP + p4;
+    slot_nv[it] = ok ? min(4, cp.OW - ow) : 0;
+    slot_y[it] = (n * cp.M + g * cp.Mg + mw + row) * cp.out_sz +
+                 ((int64_t)od * cp.OH + oh) * cp.OW + ow;
+  }
+  half4 zv[TM][ITER];
+  auto load_z = [&](int j) {
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      half4 v = {};
+      const int m = mw + j * 16 + (it * 64 + lane) / GPR;
+      if (cp.has_z && slot_nv[it] > 0 && m < cp.Mg) {
+        const half_t* zp = z + slot_y[it] + (int64_t)j * 16 * cp.out_sz;
+        if (vec_ok && slot_nv[it] == 4) {
+          v = *(const half4*)zp;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (r < slot_nv[it]) v[r] = zp[r];
+        }
+      }
+      zv[j][it] = v;
+    }
+  };
+  // every Z value of this wave is requested before any is needed
+  if (cp.has_z) {
+#pragma unroll
+    for (int j = 0; j < TM; ++j) load_z(j);
+  }
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
-    // phase 1: channel block j of this wave -> 16 rows (channels) x PW pixels
 #pragma unroll
     for (int i = 0; i < TP; ++i) *(float4v*)(stage + r16 * RP + i * 16 + q * 4) = acc[i][j];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // phase 2: each lane takes 4 consecutive pixels of one channel row
-    constexpr int GPR = PW / 4;           // 4-pixel groups per row
-    constexpr int ITER = 16 * GPR / 64;
+    if (cp.has_z) {
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) {
+        float4v* sp = (float4v*)(stage + slot_lds[it]);
+        float4v v = *sp;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] += (float)zv[j][it][r];
+        *sp = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    // rolled: slot coordinates are recomputed with shifts (tile width and
+    // height are powers of two), the activation is dispatched per 4 values
     for (int it = 0; it < ITER; ++it) {
       const int idx = it * 64 + lane;
       const int row = idx / GPR, p4 = (idx % GPR) * 4;
-      const int m = m0 + wmi * (BM / 2) + j * 16 + row;
+      const int m = mw + j * 16 + row;
       const int pl = wpi * PW + p4;
-      const int tw = pl % ht.TW, th = (pl / ht.TW) % ht.TH, td = pl / (ht.TW * ht.TH);
-      const int od = od0 + td, oh = oh0 + th, ow = ow0 + tw;
-      if (m >= cp.Mg || od >= cp.OD || oh >= cp.OH || ow >= cp.OW) continue;
-      const int gm = g * cp.Mg + m;
-      const int64_t yi = (n * cp.M + gm) * cp.out_sz + ((int64_t)od * cp.OH + oh) * cp.OW + ow;
-      const float4v v4 = *(const float4v*)(stage + row * RP + p4);
-      const float bv = cp.has_bias ? to_f32(bias[gm]) : 0.0f;
-      if (vec_ok && ow + 3 < cp.OW) {
-        half4 zv = {};
-        if (cp.has_z) zv = *(const half4*)(z + yi);
-        half4 out;
+      const int oh = oh0 + (pl >> ht.ltw), ow = ow0 + (pl & (ht.TW - 1));
+      if (m >= cp.Mg || oh >= cp.OH || ow >= cp.OW) continue;
+      const int nv = min(4, cp.OW - ow);
+      const int64_t yi = (n * cp.M + g * cp.Mg + m) * cp.out_sz +
+                         ((int64_t)od0 * cp.OH + oh) * cp.OW + ow;
+      float4v v4 = *(const float4v*)(stage + row * RP + p4);
+      const float bv = cp.has_bias ? to_f32(bias[g * cp.Mg + m]) : 0.0f;
+      v4 += bv;
+      v4 = act_apply4(cp.act, v4, cp.alpha, cp.beta);
+      half4 out;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          out[r] = (half_t)act_apply(cp.act, v4[r] + bv + (float)zv[r], cp.alpha, cp.beta);
+      for (int r = 0; r < 4; ++r) out[r] = (half_t)v4[r];
+      if (vec_ok && nv == 4) {
         *(half4*)(y + yi) = out;
       } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (ow + r >= cp.OW) continue;
-          float v = v4[r] + bv;
-          if (cp.has_z) v += (float)z[yi + r];
-          y[yi + r] = (half_t)act_apply(cp.act, v, cp.alpha, cp.beta);
-        }
+        for (int r = 0; r < 4; ++r)
+          if (r < nv) y[yi + r] = out[r];
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -365,6 +437,7 @@ bool choose(const ConvParams& cp, Choice& ch) {
       const int tw = order[oi], th = bn / tw, td = 1;
       HaloTile ht;
       ht.TD = td; ht.TH = th; ht.TW = tw;
+      ht.ltw = 31 - __builtin_clz((unsigned)tw);
       ht.BD = (td - 1) * cp.sd + (cp.KD - 1) * cp.dd + 1;
       ht.BH = (th - 1) * cp.sh + (cp.KH - 1) * cp.dh + 1;
       ht.BW = (tw - 1) * cp.sw + (cp.KW - 1) * cp.dw + 1;
@@ -434,7 +507,7 @@ bool igemm_halo_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32
 int launch_igemm_halo(const Geometry& g, const Plan&, const RunArgs& a) {
   Choice ch;
   if (!choose(g.cp, ch)) return FUSEDCONV_ERR_ROUTE;
-  return ch.bn == 256 ? launch_t<128, 256, false>(g, ch, a) : launch_t<128, 128, true>(g, ch, a);
+  return ch.bn == 256 ? launch_t<128, 256, true>(g, ch, a) : launch_t<128, 128, true>(g, ch, a);
 }
 
 }  // namespace fc
