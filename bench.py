@@ -65,20 +65,28 @@ def bound_of(wl, flop, nbytes):
     return ("mfma" if t_compute >= t_mem else "hbm"), t_compute, t_mem
 
 
-def csrc_hash():
+# source files each measured kernel is built from
+KERNEL_SOURCES = {"halo_kernel": "kernels_halo.hip", "dw_fast_kernel": "kernels_depthwise.hip",
+                  "depthwise_kernel": "kernels_depthwise.hip", "igemm_kernel": "kernels_igemm.hip",
+                  "direct_kernel": "kernels_direct.hip"}
+
+
+def sources_hash(kernel_pat):
+    csrc = os.path.join(ROOT, "convolution_implicit_gemm_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "convolution_implicit_gemm_amd", "csrc", "*"))):
-        h.update(open(f, "rb").read())
+    for f in (KERNEL_SOURCES[kernel_pat], "epilogue.h", "conv_params.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_for(name, kernel):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+def traffic_for(name):
+    """HBM bytes per launch from committed rocprofv3 counter runs; None when the
+    kernel sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("csrc_hash") != csrc_hash() or rec.get("kernel") != kernel:
+    if rec.get("sources_hash") != sources_hash(rec["kernel_pattern"]):
         return None
     return rec.get("bytes_per_launch")
 
@@ -112,9 +120,15 @@ class Runner:
                    if self.op.workspace_bytes else None)
         torch.cuda.synchronize()
 
-    def step(self, i):
+    def step(self, i, mid=None):
+        """One full pass: weight preparation (a no-op except on the halo route),
+        then the convolution kernel; `mid` is an event recorded between them."""
         s = self.sets[i % len(self.sets)]
-        return self.op(s["x"], s["w"], s["b"], s["z"], out=s["y"], workspace=self.ws)
+        self.op.prepare_weights(s["w"], self.ws)
+        if mid is not None:
+            mid.record(self.torch.cuda.current_stream())
+        return self.op(s["x"], s["w"], s["b"], s["z"], out=s["y"], workspace=self.ws,
+                       weights_prepared=True)
 
     def time(self, steps, warmup):
         torch = self.torch
@@ -122,17 +136,18 @@ class Runner:
             self.step(i)
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             ev[i][0].record(stream)
-            self.step(i)
-            ev[i][1].record(stream)
+            self.step(i, ev[i][1])
+            ev[i][2].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        kern = [a.elapsed_time(b) * 1e-3 for a, b in ev]
+        # the main kernel alone (between the middle and the last event)
+        kern = [a.elapsed_time(b) * 1e-3 for _, a, b in ev]
+        self.prep_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
         return wall / steps, float(np.mean(kern)), float(np.min(kern)), float(np.median(kern))
 
     def max_err(self, n_points=4000):
@@ -158,6 +173,7 @@ class Runner:
         return dict(workload=self.name, kernel=self.kernel, route=self.op.handle.route,
                     split_k=self.op.handle.split_k, dtype=self.wl["dtype"],
                     wall_ms_per_step=per_step * 1e3, kernel_ms_mean=k_mean * 1e3,
+                    weight_prep_ms_mean=self.prep_ms,
                     kernel_ms_min=k_min * 1e3, kernel_ms_median=k_med * 1e3,
                     tflops=tflops, gbs=gbs,
                     mfma_frac=tflops / PEAK_TFLOPS[self.wl["dtype"]], hbm_frac=gbs / PEAK_HBM_GBS,
@@ -168,7 +184,7 @@ class Runner:
         self.ws = None
 
 
-def cpu_baseline(name, target_s=12.0):
+def cpu_baseline(name, target_s=20.0):
     """The oracle, as it stands, on a bounded sample of the workload's images."""
     from oracle import oracle
     wl = WORKLOADS[name]
@@ -177,17 +193,62 @@ def cpu_baseline(name, target_s=12.0):
     n = wl["x"][0]
     flop_all, _ = work(wl, wl["y"])
     per_img = flop_all / n
-    t0 = time.perf_counter()
+    # warm the thread pool, then calibrate on a few images
     oracle.fusedconv(inp["x"], inp["w"], inp["b"], inp["z"], batches=(0, 1), **attrs)
-    t1 = time.perf_counter() - t0
-    k = int(max(1, min(n - 1, target_s / max(t1, 1e-3))))
+    cal = min(4, n)
     t0 = time.perf_counter()
-    oracle.fusedconv(inp["x"], inp["w"], inp["b"], inp["z"], batches=(1, 1 + k), **attrs)
+    oracle.fusedconv(inp["x"], inp["w"], inp["b"], inp["z"], batches=(0, cal), **attrs)
+    t1 = (time.perf_counter() - t0) / cal
+    k = int(max(1, min(n, target_s / max(t1, 1e-4))))
+    t0 = time.perf_counter()
+    oracle.fusedconv(inp["x"], inp["w"], inp["b"], inp["z"], batches=(0, k), **attrs)
     dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or os.cpu_count()
     return dict(value=per_img * k / dt / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
                 sample=f"{k} of {n} images (all {wl['w'][0]} output channels), {dt:.1f} s",
                 seconds=dt)
+
+
+def pmc_summary(name, kernel_pat, fetch_csv, write_csv, copy_bytes):
+    """HBM bytes per launch of the kernel matching kernel_pat, from a FETCH_SIZE
+    run and a WRITE_SIZE run (rocprofv3 --pmc, csv).  Each counter is scaled by
+    the ratio it reads for the plain copy kernel of copy_bytes in the same run."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return vals
+
+    out = {}
+    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        vals = per_kernel(path, counter)
+        copy = [v for k, vs in vals.items() if "copy" in k.lower() for v in vs]
+        kern = [v for k, vs in vals.items() if kernel_pat in k for v in vs]
+        if not copy or not kern:
+            raise SystemExit(f"no copy or no '{kernel_pat}' dispatch with {counter} in {path}")
+        scale = copy_bytes / max(copy)  # the largest copy dispatch is the calibration copy
+        out[key] = dict(measured=float(np.median(kern)), scale=scale,
+                        bytes=float(np.median(kern)) * scale)
+    wl = WORKLOADS[name]
+    algo = work(wl, wl["y"])[1]
+    rec = dict(workload=name, kernel_pattern=kernel_pat, sources_hash=sources_hash(kernel_pat),
+               fetch_bytes=out["fetch"]["bytes"], write_bytes=out["write"]["bytes"],
+               bytes_per_launch=out["fetch"]["bytes"] + out["write"]["bytes"],
+               algorithmic_bytes=algo, fetch_scale=out["fetch"]["scale"],
+               write_scale=out["write"]["scale"], copy_bytes=copy_bytes,
+               commands=[f"cd /tmp && timeout -s KILL 240 rocprofv3 --pmc {c} --output-format csv "
+                         f"-d <out>/pmc_{name}_{c} -o run -- python3 /root/repo/bench.py "
+                         f"--workload {name} --steps 3 --warmup 1 --no-per-config "
+                         f"--no-cpu-baseline --calib-copy-mb {copy_bytes >> 20}"
+                         for c in ("FETCH_SIZE", "WRITE_SIZE")],
+               note="FETCH_SIZE/WRITE_SIZE in KiB per dispatch, median over the kernel's "
+                    "dispatches, times the factor that maps the copy kernel's reading to its "
+                    "known size")
+    return rec
 
 
 def main():
@@ -199,7 +260,17 @@ def main():
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-config-steps", type=int, default=20)
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run a plain device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("KERNEL_PATTERN", "FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two counter runs and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        rec = pmc_summary(args.workload, *args.pmc_summary, copy_bytes=args.calib_copy_mb << 20)
+        path = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+        json.dump(rec, open(path, "w"), indent=1)
+        print(json.dumps(rec))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this FusedConv build runs on one GPU only; "
                           "bench.py measures --gpus 1"}))
@@ -207,6 +278,12 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    if args.calib_copy_mb:
+        src = torch.ones(args.calib_copy_mb << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log(f"bench: workload {args.workload}, {args.steps} steps, {args.warmup} warmup")
     r = Runner(args.workload)
     s = r.summary(args.steps, args.warmup)
@@ -219,9 +296,10 @@ def main():
     else:
         roof = dict(bound="hbm", achieved=s["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=s["hbm_frac"])
-    roof["traffic"] = traffic_for(args.workload, r.kernel)
+    roof["traffic"] = traffic_for(args.workload)
     roof["kernel"] = r.kernel
     roof["kernel_ms_mean"] = s["kernel_ms_mean"]
+    roof["weight_prep_ms_mean"] = s["weight_prep_ms_mean"]
     r.free()
     del r
     torch.cuda.empty_cache()

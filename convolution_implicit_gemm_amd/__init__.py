@@ -38,7 +38,15 @@ class FusedConv:
         self.y_shape = self.handle.y_shape
         self.workspace_bytes = self.handle.workspace_bytes
 
-    def __call__(self, x, w, bias=None, z=None, out=None, workspace=None, stream=None):
+    def prepare_weights(self, w, workspace, stream=None):
+        """Enqueue only the weight preparation of this plan into `workspace`."""
+        import torch
+        st = stream if stream is not None else torch.cuda.current_stream(w.device).cuda_stream
+        self.handle.prepare_weights(w.data_ptr(), workspace.data_ptr() if workspace is not None
+                                    else None, self.workspace_bytes, st)
+
+    def __call__(self, x, w, bias=None, z=None, out=None, workspace=None, stream=None,
+                 weights_prepared=False):
         import torch
         for name, t in (("x", x), ("w", w), ("bias", bias), ("z", z), ("out", out)):
             if t is None:
@@ -56,7 +64,8 @@ class FusedConv:
                         bias.data_ptr() if bias is not None else None,
                         z.data_ptr() if z is not None else None, y.data_ptr(),
                         ws.data_ptr() if ws is not None else None,
-                        self.workspace_bytes if ws is not None else 0, st)
+                        self.workspace_bytes if ws is not None else 0, st,
+                        1 if weights_prepared else 0)
         return y
 
 

@@ -31,7 +31,9 @@ STATUS = {
 # Every symbol include/fusedconv.h declares.
 EXPORTS = ["fusedconv_desc_init", "fusedconv_create", "fusedconv_output_shape",
            "fusedconv_workspace_size", "fusedconv_plan_info", "fusedconv_run",
-           "fusedconv_destroy", "fusedconv_status_string", "fusedconv_last_error"]
+           "fusedconv_prepare_weights", "fusedconv_run_ex", "fusedconv_destroy",
+           "fusedconv_status_string", "fusedconv_last_error"]
+RUN_WEIGHTS_PREPARED = 1
 
 
 class Tensor(ctypes.Structure):
@@ -91,6 +93,11 @@ def load():
         lib.fusedconv_plan_info.restype = ctypes.c_int
         lib.fusedconv_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.fusedconv_run.restype = ctypes.c_int
+        lib.fusedconv_prepare_weights.argtypes = [vp, vp, vp, ctypes.c_size_t, vp]
+        lib.fusedconv_prepare_weights.restype = ctypes.c_int
+        lib.fusedconv_run_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                         ctypes.c_uint, vp]
+        lib.fusedconv_run_ex.restype = ctypes.c_int
         lib.fusedconv_destroy.argtypes = [vp]
         lib.fusedconv_destroy.restype = None
         lib.fusedconv_status_string.argtypes = [ctypes.c_int]
@@ -177,10 +184,15 @@ class Handle:
         self.split_k = s.value
         self.kernel_name = name.value.decode()
 
-    def run(self, x, w, bias, z, y, workspace, workspace_bytes, stream):
+    def run(self, x, w, bias, z, y, workspace, workspace_bytes, stream, flags=0):
         """Raw device pointers (ints or None); stream is a hipStream_t as int (0 = default)."""
-        rc = self._lib.fusedconv_run(self._h, x, w, bias, z, y, workspace, workspace_bytes,
-                                     stream)
+        rc = self._lib.fusedconv_run_ex(self._h, x, w, bias, z, y, workspace, workspace_bytes,
+                                        flags, stream)
+        if rc != 0:
+            raise FusedConvError(rc, self._lib.fusedconv_last_error().decode())
+
+    def prepare_weights(self, w, workspace, workspace_bytes, stream):
+        rc = self._lib.fusedconv_prepare_weights(self._h, w, workspace, workspace_bytes, stream)
         if rc != 0:
             raise FusedConvError(rc, self._lib.fusedconv_last_error().decode())
 

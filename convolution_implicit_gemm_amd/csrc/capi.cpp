@@ -102,6 +102,33 @@ int fusedconv_plan_info(const fusedconv_handle* h, int32_t* route, int32_t* spli
 int fusedconv_run(const fusedconv_handle* h, const void* x, const void* w, const void* bias,
                   const void* z, void* y, void* workspace, size_t workspace_bytes,
                   void* stream) {
+  return fusedconv_run_ex(h, x, w, bias, z, y, workspace, workspace_bytes, 0u, stream);
+}
+
+int fusedconv_prepare_weights(const fusedconv_handle* h, const void* w, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!h || !w) return set_err(FUSEDCONV_ERR_NULL_ARG, "h and w are required");
+  if (!aligned16(w) || (workspace && !aligned16(workspace)))
+    return set_err(FUSEDCONV_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  if (h->plan.workspace > 0 && (!workspace || workspace_bytes < h->plan.workspace))
+    return set_err(FUSEDCONV_ERR_WORKSPACE,
+                   "workspace smaller than fusedconv_workspace_size() reports");
+  if (h->plan.route != FUSEDCONV_ROUTE_IGEMM_HALO) return FUSEDCONV_OK;
+  int rc = check_device();
+  if (rc != FUSEDCONV_OK) return rc;
+  (void)hipGetLastError();
+  fc::RunArgs a{nullptr, w, nullptr, nullptr, nullptr, workspace, stream, 0u};
+  rc = fc::prepare_igemm_halo(h->geo, h->plan, a);
+  if (rc != FUSEDCONV_OK) {
+    hipError_t e = hipGetLastError();
+    return set_err(rc, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  }
+  return FUSEDCONV_OK;
+}
+
+int fusedconv_run_ex(const fusedconv_handle* h, const void* x, const void* w, const void* bias,
+                     const void* z, void* y, void* workspace, size_t workspace_bytes,
+                     unsigned flags, void* stream) {
   if (!h || !x || !w || !y) return set_err(FUSEDCONV_ERR_NULL_ARG, "h, x, w and y are required");
   const fc::ConvParams& cp = h->geo.cp;
   if (cp.has_bias && !bias) return set_err(FUSEDCONV_ERR_NULL_ARG, "bias declared but NULL");
@@ -118,7 +145,9 @@ int fusedconv_run(const fusedconv_handle* h, const void* x, const void* w, const
   int rc = check_device();
   if (rc != FUSEDCONV_OK) return rc;
   (void)hipGetLastError();  // drop a stale error so a launch failure is reported as ours
-  fc::RunArgs a{x, w, bias, z, y, workspace, stream};
+  if (flags & ~FUSEDCONV_RUN_WEIGHTS_PREPARED)
+    return set_err(FUSEDCONV_ERR_ATTR_VALUE, "unknown run flags");
+  fc::RunArgs a{x, w, bias, z, y, workspace, stream, flags};
   switch (h->plan.route) {
     case FUSEDCONV_ROUTE_DIRECT: rc = fc::launch_direct(h->geo, h->plan, a); break;
     case FUSEDCONV_ROUTE_IGEMM: rc = fc::launch_igemm(h->geo, h->plan, a); break;

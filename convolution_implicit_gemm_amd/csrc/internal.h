@@ -50,15 +50,18 @@ struct RunArgs {
   void* y;
   void* ws;
   void* stream;
+  unsigned flags;   // FUSEDCONV_RUN_WEIGHTS_PREPARED
 };
 
 int launch_direct(const Geometry& g, const Plan& p, const RunArgs& a);
 int launch_igemm(const Geometry& g, const Plan& p, const RunArgs& a);
 int launch_depthwise(const Geometry& g, const Plan& p, const RunArgs& a);
 int launch_igemm_halo(const Geometry& g, const Plan& p, const RunArgs& a);
+int prepare_igemm_halo(const Geometry& g, const Plan& p, const RunArgs& a);
 
 // Depthwise planning helper (kernels_depthwise.hip knows its LDS budget).
 bool depthwise_fits(const ConvParams& cp, int32_t& tile_h, int32_t& tile_w);
+bool depthwise_fast(const ConvParams& cp, int32_t dtype);
 bool igemm_halo_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32_t& tile_w,
                      size_t& workspace);
 

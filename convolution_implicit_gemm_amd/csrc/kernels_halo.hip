@@ -463,6 +463,16 @@ bool choose(const ConvParams& cp, Choice& ch) {
   return false;
 }
 
+int launch_repack(const ConvParams& cp, const Choice& ch, const RunArgs& a) {
+  const int64_t total = (int64_t)cp.G * cp.taps * ch.ht.ncb * ch.ht.mgp * kCB;
+  int64_t rblocks = (total + kThreads - 1) / kThreads;
+  if (rblocks > 4096) rblocks = 4096;
+  hipLaunchKernelGGL(repack_w_kernel, dim3((unsigned)rblocks), dim3(kThreads), 0,
+                     (hipStream_t)a.stream, (const half_t*)a.w, (half_t*)a.ws, cp, ch.ht.ncb,
+                     ch.ht.mgp);
+  return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
+}
+
 template <int BM, int BN, bool PFX>
 int launch_t(const Geometry& g, const Choice& ch, const RunArgs& a) {
   const ConvParams& cp = g.cp;
@@ -477,12 +487,10 @@ int launch_t(const Geometry& g, const Choice& ch, const RunArgs& a) {
       return FUSEDCONV_ERR_LAUNCH;
     attr_set = true;
   }
-  const int64_t total = (int64_t)cp.G * cp.taps * ch.ht.ncb * ch.ht.mgp * kCB;
-  int64_t rblocks = (total + kThreads - 1) / kThreads;
-  if (rblocks > 4096) rblocks = 4096;
-  hipLaunchKernelGGL(repack_w_kernel, dim3((unsigned)rblocks), dim3(kThreads), 0, st,
-                     (const half_t*)a.w, (half_t*)a.ws, cp, ch.ht.ncb, ch.ht.mgp);
-  if (hipPeekAtLastError() != hipSuccess) return FUSEDCONV_ERR_LAUNCH;
+  if (!(a.flags & FUSEDCONV_RUN_WEIGHTS_PREPARED)) {
+    const int rc = launch_repack(cp, ch, a);
+    if (rc != FUSEDCONV_OK) return rc;
+  }
   dim3 grid((unsigned)(cp.n * ch.ht.tiles_d * ch.ht.tiles_h * ch.ht.tiles_w),
             (unsigned)cdiv(cp.Mg, BM), (unsigned)cp.G);
   hipLaunchKernelGGL((halo_kernel<BM, BN, PFX>), grid, dim3(kThreads), lds, st, (const half_t*)a.x,
@@ -502,6 +510,12 @@ bool igemm_halo_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32
   tile_w = ch.ht.TW;
   workspace = (size_t)cp.G * cp.taps * ch.ht.ncb * ch.ht.mgp * kCB * sizeof(half_t);
   return true;
+}
+
+int prepare_igemm_halo(const Geometry& g, const Plan&, const RunArgs& a) {
+  Choice ch;
+  if (!choose(g.cp, ch)) return FUSEDCONV_ERR_ROUTE;
+  return launch_repack(g.cp, ch, a);
 }
 
 int launch_igemm_halo(const Geometry& g, const Plan&, const RunArgs& a) {

@@ -112,8 +112,13 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
       p.route = route;
       p.tile_h = th;
       p.tile_w = tw;
-      snprintf(p.name, sizeof(p.name), "depthwise_%s_t%dx%d",
-               g.dtype == FUSEDCONV_F16 ? "f16" : "f32", th, tw);
+      if (depthwise_fast(cp, g.dtype)) {
+        p.tile = 1;  // register-window dot2 kernel
+        snprintf(p.name, sizeof(p.name), "depthwise_dot2_f16_k%dx%d", cp.KH, cp.KW);
+      } else {
+        snprintf(p.name, sizeof(p.name), "depthwise_%s_t%dx%d",
+                 g.dtype == FUSEDCONV_F16 ? "f16" : "f32", th, tw);
+      }
       return FUSEDCONV_OK;
     case FUSEDCONV_ROUTE_IGEMM_HALO:
       if (!igemm_halo_fits(cp, g.dtype, th, tw, halo_ws)) {

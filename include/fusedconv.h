@@ -177,6 +177,24 @@ int fusedconv_plan_info(const fusedconv_handle* h, int32_t* route, int32_t* spli
 int fusedconv_run(const fusedconv_handle* h, const void* x, const void* w, const void* bias,
                   const void* z, void* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Weight preparation, for callers whose W stays the same across many runs
+ * (inference): fusedconv_prepare_weights enqueues only the route's weight
+ * preparation (for IGEMM_HALO a repack of W into the tap-major layout held in
+ * the workspace; a no-op for the other routes), and fusedconv_run_ex with
+ * FUSEDCONV_RUN_WEIGHTS_PREPARED then skips that step and reads the prepared
+ * weights from the workspace.  The caller guarantees that the workspace holds
+ * the prepared form of the same W, made with the same handle; otherwise the
+ * result is undefined.  Arguments and errors as for fusedconv_run; flags = 0
+ * makes fusedconv_run_ex identical to fusedconv_run.
+ */
+#define FUSEDCONV_RUN_WEIGHTS_PREPARED 1u
+int fusedconv_prepare_weights(const fusedconv_handle* h, const void* w, void* workspace,
+                              size_t workspace_bytes, void* stream);
+int fusedconv_run_ex(const fusedconv_handle* h, const void* x, const void* w, const void* bias,
+                     const void* z, void* y, void* workspace, size_t workspace_bytes,
+                     unsigned flags, void* stream);
+
 /* Release a handle (NULL is allowed). */
 void fusedconv_destroy(fusedconv_handle* h);
 

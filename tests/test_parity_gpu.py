@@ -152,6 +152,39 @@ def test_depthwise_route(dtype):
                  bias=trial % 2 == 0, resid=trial % 3 == 0)
 
 
+DW_FAST_CASES = [
+    # (n, C, mult, H, W, k, dilation, auto_pad / pads) for the fp16 dot2 depthwise kernel
+    (2, 5, 1, 56, 56, 7, 1, "SAME_UPPER"),
+    (1, 3, 1, 56, 56, 7, 2, "SAME_UPPER"),
+    (2, 4, 2, 17, 23, 5, 1, "SAME_LOWER"),
+    (1, 6, 1, 31, 9, 3, 3, "VALID"),
+    (3, 2, 1, 13, 61, 7, 1, [3, 1, 2, 0]),
+    (1, 7, 1, 1, 300, 5, 2, "SAME_UPPER"),    # 1-D shaped plane
+]
+
+
+@pytest.mark.parametrize("ci", range(len(DW_FAST_CASES)))
+def test_depthwise_fast_path(ci):
+    n, C, mult, H, W, k, d, pad = DW_FAST_CASES[ci]
+    attrs = dict(group=C, dilations=[d, d])
+    if isinstance(pad, list):
+        attrs["pads"] = pad
+    else:
+        attrs["auto_pad"] = pad
+    xs, ws = [n, C, H, W], [C * mult, 1, k, k]
+    h = B.Handle("f16", xs, ws, None, None, route="depthwise", **attrs)
+    assert h.kernel_name.startswith("depthwise_dot2"), h.kernel_name
+    for kk, (bias, resid) in enumerate([(True, False), (False, True), (True, True)]):
+        act, params = ACTS[(3 * ci + 5 * kk) % len(ACTS)]
+        x, w, b, z = random_tensors([9200, ci, kk], "f16", xs, ws, [C * mult] if bias else None,
+                                    h.y_shape if resid else None, dist="normal")
+        a = dict(attrs, activation=act, activation_params=f32params(params))
+        log(f"CASE dw fast {ci} x={xs} w={ws} {a}")
+        got = run_gpu(x, w, b, z, route="depthwise", **a)
+        ref = oracle.fusedconv(x, w, b, z, **a)
+        check(got, ref, "f16", f"dw fast case {ci}")
+
+
 HALO_CASES = [
     # (x, w, attrs) for the channel-last halo route (fp16)
     ([2, 64, 16, 16], [96, 64, 3, 3], dict(pads=[1, 1, 1, 1])),            # M tail (96 < 128)
@@ -247,6 +280,24 @@ def test_deterministic_and_inplace_residual(route):
     torch.cuda.synchronize()
     assert y3.data_ptr() == zd.data_ptr()
     assert torch.equal(y3, y1)
+
+
+@pytest.mark.parametrize("route", ["igemm_halo", "igemm", "depthwise"])
+def test_prepared_weights_match_plain_run(route):
+    C = 64 if route != "depthwise" else 16
+    M, grp = (C, C) if route == "depthwise" else (96, 1)
+    xs, ws = [2, C, 16, 16], [M, C // grp, 3, 3]
+    x, w, b, z = random_tensors([8100], "f16", xs, ws, [M], None, dist="normal", w_std=0.05)
+    attrs = dict(group=grp, pads=[1, 1, 1, 1], activation="Relu", route=route)
+    op = fc.FusedConv(xs, ws, "f16", True, False, **attrs)
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    ws_t = torch.empty(max(op.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    log(f"CASE prepared route={route}")
+    y1 = op(xd, wd, bd, workspace=ws_t)
+    op.prepare_weights(wd, ws_t)
+    y2 = op(xd, wd, bd, workspace=ws_t, weights_prepared=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
 
 
 def test_run_errors_on_device():
