@@ -1,23 +1,25 @@
 // Implicit GEMM on MFMA with channel-last halo boxes (fp16 in, fp32 accumulate).
 //
-// Same GEMM view as the gathered-im2col route (rows = output pixels p of one
-// image tile, columns = output channels m of one group, reduction over
-// (input channel, tap)), but the reduction is ordered (channel block of 32,
-// tap, channel within block) so that no im2col element is gathered one by
-// one:
-//   * per channel block, the input box that the tile's windows cover (the
-//     tile's "halo", zero outside the image) is copied once into LDS in
-//     channel-last layout [position][32 channels]; for tap t every output
-//     pixel's 32-channel operand row is then one 64-byte LDS row at
-//     position(p) + offset(t), and one lane's 8-channel slice is one
-//     ds_read_b128;
-//   * the weights are first repacked (every run) into a tap-major layout
-//     Wp[g][tap][channel block][m][32] so the operand tile of one (tap,
-//     channel block) is a contiguous BM x 64-byte block; it is staged in LDS,
-//     double-buffered, one barrier per tap;
+// GEMM view per block: rows = BN output pixels of one image tile, columns =
+// BM output channels of one group, reduction over (input channel, tap)
+// ordered as (channel block of 32, tap, channel within the block), so that no
+// im2col element is gathered one by one:
+//   * per channel block, the input box that the tile's windows cover (zero
+//     outside the image) is copied once into LDS in channel-last layout
+//     [position][32 channels].  Positions are split by stride phase along
+//     every axis, so for tap t every output pixel's 32-channel operand row is
+//     the LDS row at pixel(p) + offset(t), consecutive pixels sit in
+//     consecutive rows whatever the stride, and one lane's 8-channel slice is
+//     one ds_read_b128;
+//   * the weights are repacked into a tap-major layout
+//     Wp[g][tap][channel block][m][32] (fusedconv_prepare_weights, or at the
+//     start of every run) and loaded straight into registers one step ahead;
 //   * v_mfma_f32_16x16x32_f16 with pixels as MFMA rows: each lane ends with 4
-//     consecutive pixels of one output channel, so Z is read and Y written in
-//     8-byte pieces in the fused epilogue (bias, residual, activation).
+//     consecutive pixels of one output channel.
+// The fused epilogue of the FusedConv README ("Inputs": B per output channel
+// and Z of Y's shape, added before the activation): the accumulators start
+// at B; after the K loop they are staged through LDS one 16-channel block at
+// a time, Z is added, the activation applied and Y stored once, rounded.
 // The idea of feeding a matrix unit from an input tile that is staged once
 // and re-read per tap is the one the FusedConv manifest's
 // implicit_im2col_subgroup_matrix variants and the tinygrad page's shifted
@@ -27,6 +29,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "epilogue.h"
 #include "internal.h"
@@ -35,33 +38,48 @@ namespace fc {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kCB = 32;          // channels per block = MFMA K
-constexpr int kLDC = kCB + 8;    // LDS row pitch in halves (80 bytes)
-constexpr int kMaxItems = 4;     // loader items per thread kept in registers
-constexpr size_t kMaxLds = 150 * 1024;  // above 80 KB a CU holds one block
+constexpr int kCB = 32;               // channels per block = MFMA K
+constexpr int kLDC = kCB + 8;         // LDS row pitch in halves (80 bytes): conflict-free b128 reads
+constexpr int kMaxTaps = 64;
+constexpr size_t kLds2 = 80 * 1024;    // two blocks per CU
+constexpr size_t kMaxLds = 150 * 1024;  // one block per CU
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
 struct HaloTile {
-  int TD, TH, TW;      // output tile
-  int BD, BH, BW;      // input box
+  int TD, TH, TW;          // output tile
+  int BD, BH, BW;          // input box (box-relative coordinates 0..B*-1)
+  int ND, NH, NW;          // box positions per stride phase along each axis
+  int LH, LW;              // LDS pitches in positions: LH = sh*NH rows, LW = sw*NW columns
+  int box_pos;             // positions per LDS box: sd*ND*LH*LW
   int tiles_d, tiles_h, tiles_w;
-  int ncb;             // channel blocks
-  int mgp;             // Wp rows per (tap, channel block): M/group rounded up to BM
-  int vec_x;           // W % 8 == 0: 16-byte aligned 8-column groups
-  int ltw;             // log2(TW); tiles are one depth slice, TW and TH powers of two
+  int ntile;               // n * tiles_d * tiles_h * tiles_w
+  int nmb;                 // m blocks per group
+  int remap;               // 1: the m blocks of one tile run back to back on one XCD
+  int ncb;                 // input channel blocks
+  int mgp;                 // Wp rows per (tap, channel block): M/group rounded up to BM
+  int vec_x;               // W % 8 == 0: 16-byte input loads
+  int ltw, lth;            // log2(TW), log2(TH)
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Dynamic LDS: two input boxes, and at least the epilogue staging area
-// (4 waves x 16 channels x (BN/2 + 4) fp32).
-size_t lds_bytes(int bpos, int bn) {
-  const size_t boxes = (size_t)2 * bpos * kLDC * 2;
+// Dynamic LDS: two input boxes, or the epilogue staging area (4 waves x 16
+// channels x (BN/2 + 4) fp32) if larger.
+size_t lds_bytes(int box_pos, int bn) {
+  const size_t boxes = (size_t)2 * box_pos * kLDC * 2;
   const size_t stage = (size_t)4 * 16 * (bn / 2 + 4) * 4;
   return boxes > stage ? boxes : stage;
+}
+
+// Box-relative coordinate a along an axis with stride s and n positions per
+// phase -> LDS index (phase-major).
+__device__ __forceinline__ int phase_index(int a, int s, int n) {
+  if (s == 1) return a;
+  const int ph = a % s;
+  return ph * n + a / s;
 }
 
 // Wp[((g*taps + t)*ncb + cb)*mgp + m][c'] = W[g*Mg + m][cb*32 + c'][t]; 0 past
@@ -86,264 +104,291 @@ __global__ __launch_bounds__(kThreads) void repack_w_kernel(const half_t* __rest
   }
 }
 
+// One work unit: output channels [mb*BM, mb*BM + BM) of group g over the
+// output tile at (n, od0, oh0, ow0).
+struct Unit {
+  int64_t n;
+  int g, mb, od0, oh0, ow0;
+};
+
 // Block tile BN pixels x BM channels, 4 waves as 2 x 2, each owning
-// (BN/2) x (BM/2) = TP x TM MFMA blocks of 16x16; two blocks per CU.  Steps
-// run over (channel block, tap).  The input box of a channel block sits in
-// LDS (double-buffered, one barrier per channel block); weight fragments come
-// straight from the repacked buffer into registers one step ahead; input
-// fragments are read from LDS at the start of their step.
-// PFX: keep the next channel block's input in registers across a whole
-// channel block (hides its load latency, costs ~30 registers); without it the
-// box is loaded right before it is stored.
-template <int BM, int BN, bool PFX>
-__global__ __launch_bounds__(kThreads, 2) void halo_kernel(const half_t* __restrict__ x,
-                                                           const half_t* __restrict__ wp,
-                                                           const half_t* __restrict__ bias,
-                                                           const half_t* z, half_t* y,
-                                                           ConvParams cp, HaloTile ht) {
+// (BN/2) x (BM/2) = TP x TM MFMA blocks of 16x16; two blocks per CU.
+// PF: input-box loader items per thread kept in registers across a channel
+// block (each item = 4 channels x 8 columns of one box row, 16 registers);
+// items beyond PF * 256 are loaded and stored at the channel-block boundary.
+// VEC: W % 8 == 0, so an item's 8 columns are one aligned 16-byte load.
+template <int BM, int BN, int PF, bool VEC>
+__device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
+                                          const half_t* __restrict__ wp,
+                                          const half_t* __restrict__ bias, const half_t* z,
+                                          half_t* y, const ConvParams& cp, const HaloTile& ht,
+                                          const Unit& u) {
   constexpr int TP = BN / 32;
   constexpr int TM = BM / 32;
   extern __shared__ __attribute__((aligned(16))) half_t lds[];
-  const int box = ht.BD * ht.BH * ht.BW * kLDC;  // halves per input box
+  const int box = ht.box_pos * kLDC;  // halves per input box
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wpi = wave & 1, wmi = wave >> 1;
   const int r16 = lane & 15, q = lane >> 4;
-
-  // block -> (image, tile), m tile, group
-  int64_t b = blockIdx.x;
-  const int tw_i = (int)(b % ht.tiles_w);
-  b /= ht.tiles_w;
-  const int th_i = (int)(b % ht.tiles_h);
-  b /= ht.tiles_h;
-  const int td_i = (int)(b % ht.tiles_d);
-  const int64_t n = b / ht.tiles_d;
-  const int m0 = blockIdx.y * BM;
-  const int g = blockIdx.z;
-  const int od0 = td_i * ht.TD, oh0 = th_i * ht.TH, ow0 = tw_i * ht.TW;
+  const int g = u.g;
+  const int64_t n = u.n;
+  const int m0 = u.mb * BM;
+  const int od0 = u.od0, oh0 = u.oh0, ow0 = u.ow0;
   const int bd0 = od0 * cp.sd - cp.pd, bh0 = oh0 * cp.sh - cp.ph, bw0 = ow0 * cp.sw - cp.pw;
 
   // ---- zero both input boxes: positions outside the image stay zero
   for (int i = tid; i < 2 * box / 8; i += kThreads) ((half8*)lds)[i] = half8{};
 
-  // ---- input loader items: (channel, d, h, aligned 8-column group) of the
-  // in-image part of the box.  The first kMaxItems per thread keep their
-  // decoded addresses in registers; further ones are decoded when stored.
+  // ---- input loader.  Item i = (row of the in-image part of the box,
+  // aligned 8-column group, channel quad cq = i % 8): four 16-byte loads of
+  // the same 8 columns in 4 channel planes, written as eight 8-byte LDS rows
+  // (4 channels each).  Consecutive lanes cover the 8 quads of one 64-byte
+  // LDS row, so the writes are at most 2-way bank conflicted.
   const int d_lo = max(bd0, 0), d_hi = min(bd0 + ht.BD, cp.D);
   const int h_lo = max(bh0, 0), h_hi = min(bh0 + ht.BH, cp.H);
   const int w_lo = max(bw0, 0), w_hi = min(bw0 + ht.BW, cp.W);
   const int g_lo = w_lo >> 3, g_hi = (w_hi + 7) >> 3;
-  const int nd = d_hi - d_lo, nh = h_hi - h_lo, ngr = g_hi - g_lo;
-  const int nitems = kCB * nd * nh * ngr;
-  const half_t* ximg = x + (n * cp.C + (int64_t)g * cp.Cg) * cp.in_sz;
-  int it_goff[kMaxItems];   // element offset from the channel block's first channel
-  int it_dst[kMaxItems];    // LDS element offset of column 0 of the group, channel c
-  int it_cm[kMaxItems];     // channel (bits 8..) and in-box column mask (bits 0..7); -1 none
+  const int nd = max(d_hi - d_lo, 0), nh = max(h_hi - h_lo, 0), ngr = max(g_hi - g_lo, 0);
+  const int nitems = 8 * nd * nh * ngr;
+  const int cq = tid & 7;
+  const half_t* ximg = x + (n * cp.C + (int64_t)g * cp.Cg + cq * 4) * cp.in_sz;
+  // decoded item: element offset of (channel cq*4, row, column group) from the
+  // channel block's first plane; LDS half offset of the row (+ cq*4); the
+  // box-relative column of the group's first element (+8) and the column mask
+  struct Item { int goff, ldst, cm; };
+  auto decode = [&](int i) __attribute__((always_inline)) {
+    Item it;
+    int r = i >> 3;
+    const int gi = r % ngr;
+    r /= ngr;
+    const int hh = r % nh;
+    const int dd = r / nh;
+    const int id = d_lo + dd, ih = h_lo + hh, iw = (g_lo + gi) * 8;
+    int mask = 0;
 #pragma unroll
-  for (int k = 0; k < kMaxItems; ++k) {
+    for (int e = 0; e < 8; ++e)
+      if (iw + e >= w_lo && iw + e < w_hi) mask |= 1 << e;
+    it.goff = (id * cp.H + ih) * cp.W + iw;
+    it.ldst = ((phase_index(id - bd0, cp.sd, ht.ND) * ht.LH + phase_index(ih - bh0, cp.sh, ht.NH)) *
+               ht.LW) * kLDC + cq * 4;
+    it.cm = ((iw - bw0 + 8) << 8) | mask;
+    return it;
+  };
+  Item items[PF];
+#pragma unroll
+  for (int k = 0; k < PF; ++k) {
     const int i = tid + k * kThreads;
-    it_cm[k] = -1;
-    it_goff[k] = it_dst[k] = 0;
-    if (i < nitems) {
-      int r = i;
-      const int gi = r % ngr; r /= ngr;
-      const int hh = r % nh; r /= nh;
-      const int dd = r % nd;
-      const int c = r / nd;
-      const int id = d_lo + dd, ih = h_lo + hh, iw = (g_lo + gi) * 8;
-      int mask = 0;
+    items[k].cm = -1;
+    items[k].goff = items[k].ldst = 0;
+    if (i < nitems) items[k] = decode(i);
+  }
+  half8 xreg[PF][4];
+  // load item it of channel block cb (4 channel planes) into v
+  // Loads are unconditional (an invalid item or channel reads the first
+  // element of x instead) and validity is applied when the item is written to
+  // LDS: a load under a branch makes the compiler wait for it at the join,
+  // which would turn the prefetch into a synchronous HBM round trip.
+  auto load_item = [&](const Item& it, int cb, half8* v) __attribute__((always_inline)) {
+    const int cvalid = cp.Cg - cb * kCB - cq * 4;  // valid channels of this quad
+    const half_t* src = ximg + (int64_t)cb * kCB * cp.in_sz + it.goff;
+    int cm = it.cm;
+    asm volatile("" : "+v"(cm));  // keep the column tests here, not hoisted
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (iw + e >= w_lo && iw + e < w_hi) mask |= 1 << e;
-      it_cm[k] = (c << 8) | mask;
-      it_goff[k] = c * (int)cp.in_sz + (id * cp.H + ih) * cp.W + iw;
-      it_dst[k] = (((id - bd0) * ht.BH + (ih - bh0)) * ht.BW + (iw - bw0)) * kLDC + c;
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = cm >= 0 && j < cvalid;
+      const half_t* s = ok ? src + j * cp.in_sz : x;
+      if constexpr (VEC) {
+        v[j] = *(const half8*)s;
+      } else {
+        half8 t = {};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (ok && ((cm >> e) & 1)) t[e] = s[e];
+        v[j] = t;
+      }
     }
-  }
-  half8 xreg[kMaxItems];
-#define HALO_LOAD_X(CB)                                                        \
-  {                                                                            \
-    const half_t* xb_ = ximg + (int64_t)(CB) * kCB * cp.in_sz;                 \
-    const int cvalid_ = cp.Cg - (CB) * kCB;                                    \
-    _Pragma("unroll") for (int k = 0; k < kMaxItems; ++k) {                    \
-      half8 v_ = {};                                                           \
-      if (it_cm[k] >= 0 && (it_cm[k] >> 8) < cvalid_) {                        \
-        const half_t* src_ = xb_ + it_goff[k];                                 \
-        if (ht.vec_x) {                                                        \
-          v_ = *(const half8*)src_;                                            \
-        } else {                                                               \
-          _Pragma("unroll") for (int e = 0; e < 8; ++e) if ((it_cm[k] >> e) & 1) v_[e] = src_[e]; \
-        }                                                                      \
-      }                                                                        \
-      xreg[k] = v_;                                                            \
-    }                                                                          \
-  }
-  // store the box of channel block CB (held in xreg) into LDS buffer BUF
-  auto store_x = [&](int buf, int cb) {
+  };
+  // write item it of channel block cb (4 channels in v) into LDS buffer xs:
+  // 8 columns x 8 bytes; channels past C/group are written as zeros
+  auto store_item = [&](const Item& it, int cb, half_t* xs, const half8* v) __attribute__((always_inline)) {
+    int cm = it.cm;
+    asm volatile("" : "+v"(cm));  // keep the column tests here, not hoisted
+    if (cm < 0) return;
+    const int cvalid = cp.Cg - cb * kCB - cq * 4;
+    half8 u[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) u[j] = j < cvalid ? v[j] : half8{};
+    const int aw0 = (cm >> 8) - 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (!((cm >> e) & 1)) continue;
+      const int col = phase_index(aw0 + e, cp.sw, ht.NW);
+      *(half4*)(xs + it.ldst + col * kLDC) = half4{u[0][e], u[1][e], u[2][e], u[3][e]};
+    }
+  };
+  auto prefetch_box = [&](int cb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < PF; ++k) load_item(items[k], cb, xreg[k]);
+  };
+  // store box cb into buffer buf: the prefetched items, then any further items
+  auto store_box = [&](int buf, int cb) __attribute__((always_inline)) {
     half_t* xs = lds + buf * box;
 #pragma unroll
-    for (int k = 0; k < kMaxItems; ++k) {
-      if (it_cm[k] < 0) continue;
+    for (int k = 0; k < PF; ++k) store_item(items[k], cb, xs, xreg[k]);
+    for (int i0 = PF * kThreads; i0 < nitems; i0 += PF * kThreads) {
+      Item more[PF];
+      half8 v[PF][4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if ((it_cm[k] >> e) & 1) xs[it_dst[k] + e * kLDC] = xreg[k][e];
-    }
-    const half_t* xb = ximg + (int64_t)cb * kCB * cp.in_sz;
-    const int cvalid = cp.Cg - cb * kCB;
-    for (int i = tid + kMaxItems * kThreads; i < nitems; i += kThreads) {
-      int r = i;
-      const int gi = r % ngr; r /= ngr;
-      const int hh = r % nh; r /= nh;
-      const int dd = r % nd;
-      const int c = r / nd;
-      const int id = d_lo + dd, ih = h_lo + hh, iw = (g_lo + gi) * 8;
-      const half_t* src = xb + c * (int)cp.in_sz + (id * cp.H + ih) * cp.W + iw;
-      const int dst = (((id - bd0) * ht.BH + (ih - bh0)) * ht.BW + (iw - bw0)) * kLDC + c;
+      for (int k = 0; k < PF; ++k) {
+        const int i = i0 + tid + k * kThreads;
+        more[k].cm = -1;
+        more[k].goff = more[k].ldst = 0;
+        if (i < nitems) more[k] = decode(i);
+        load_item(more[k], cb, v[k]);
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (iw + e >= w_lo && iw + e < w_hi) xs[dst + e * kLDC] = c < cvalid ? src[e] : (half_t)0;
+      for (int k = 0; k < PF; ++k) store_item(more[k], cb, xs, v[k]);
     }
   };
 
   // ---- weight fragments straight from Wp (rows padded to ht.mgp with zeros):
-  // fragment j of step (cb, t) = 16 rows x 64 bytes, each lane reads 16 bytes.
-  const half_t* wlane = wp + (int64_t)g * cp.taps * ht.ncb * ht.mgp * kCB +
-                        (int64_t)(m0 + wmi * (BM / 2) + r16) * kCB + q * 8;
+  // fragment j of step (cb, t) = 16 rows x 64 bytes, each lane reads 16 bytes
+  // at a 32-bit lane offset from the step's (uniform) tile address.
+  const half_t* wg = wp + (int64_t)g * cp.taps * ht.ncb * ht.mgp * kCB;
+  const int wl = (m0 + wmi * (BM / 2) + r16) * kCB + q * 8;
   const int64_t wstep = (int64_t)ht.mgp * kCB;  // halves per (tap, channel block) tile
 
-  // ---- per-lane LDS offsets (halves) of this lane's operand rows (pixels)
+  // ---- LDS offset (halves) of this lane's operand row (pixel) in pixel
+  // tile i.  Tiles are TW (a multiple of 16) pixels wide, so pixel tile i of
+  // a wave is 16 consecutive pixels of one tile row.
   int aoff[TP];
 #pragma unroll
   for (int i = 0; i < TP; ++i) {
-    const int pl = wpi * (BN / 2) + i * 16 + r16;
-    const int tw = pl % ht.TW, th = (pl / ht.TW) % ht.TH, td = pl / (ht.TW * ht.TH);
-    aoff[i] = (((td * cp.sd) * ht.BH + th * cp.sh) * ht.BW + tw * cp.sw) * kLDC + q * 8;
+    const int pu = wpi * (BN / 2) + i * 16;
+    aoff[i] = ((pu >> ht.ltw) * ht.LW + (pu & (ht.TW - 1)) + r16) * kLDC + q * 8;
+  }
+  // ---- LDS offset (halves) of each tap: along every axis the tap's box
+  // offset k*dilation splits into stride phase (k*dil % s) and index
+  // (k*dil / s).  One int per tap, read once per K step, kept in the unused
+  // padding (channels 32..39) of box row t of buffer 0, which neither the
+  // box writes nor the MFMA operand reads touch.
+  int* const tap_tab = (int*)lds;
+  constexpr int kTabStride = kLDC / 2;  // ints per LDS row; entry t at int t*20 + 16
+
+  // ---- accumulators start at the bias: lane column r16 is output channel
+  // m0 + wmi*BM/2 + j*16 + r16
+  float4v acc[TP][TM];
+  {
+    const int mw = m0 + wmi * (BM / 2) + r16;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      float bv = 0.0f;
+      if (cp.has_bias && mw + j * 16 < cp.Mg) bv = to_f32(bias[g * cp.Mg + mw + j * 16]);
+#pragma unroll
+      for (int i = 0; i < TP; ++i) acc[i][j] = float4v{bv, bv, bv, bv};
+    }
   }
 
-  float4v acc[TP][TM];
-#pragma unroll
-  for (int i = 0; i < TP; ++i)
-#pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-
+  const bool vec_y = (cp.OW & 3) == 0;
   const int taps = cp.taps, ncb = ht.ncb, nsteps = ncb * taps;
-  __syncthreads();  // zero fill done before any box write
-  HALO_LOAD_X(0);
-  store_x(0, 0);
-  if (PFX && ncb > 1) HALO_LOAD_X(1);
-  // Step bookkeeping is incremental (uniform, scalar): the weight tile of
-  // step (cb, t) is Wp tile t * ncb + cb, the box offset of tap (kd, kh, kw)
-  // is ((kd*dd*BH + kh*dh)*BW + kw*dw) positions.
-  const int dkw = cp.dw * kLDC;
-  const int dkh = (cp.dh * ht.BW - (cp.KW - 1) * cp.dw) * kLDC;
-  const int dkd = (cp.dd * ht.BH * ht.BW - (cp.KH - 1) * cp.dh * ht.BW - (cp.KW - 1) * cp.dw) * kLDC;
-  const int64_t wtap = (int64_t)ncb * wstep;                 // next tap, same channel block
-  const int64_t wcb = wstep - (int64_t)(taps - 1) * ncb * wstep;  // next channel block, tap 0
+
+  __syncthreads();  // zero fill done before any box or table write
+  if (tid < cp.taps) {
+    const int kw = tid % cp.KW, kh = (tid / cp.KW) % cp.KH, kd = tid / (cp.KW * cp.KH);
+    const int ad = kd * cp.dd, ah = kh * cp.dh, aw = kw * cp.dw;
+    tap_tab[tid * kTabStride + 16] =
+        ((((ad % cp.sd) * ht.ND + ad / cp.sd) * ht.LH + (ah % cp.sh) * ht.NH + ah / cp.sh) * ht.LW +
+         (aw % cp.sw) * ht.NW + aw / cp.sw) * kLDC;
+  }
+  prefetch_box(0);
+  store_box(0, 0);
+  if (ncb > 1) prefetch_box(1);
 
   // weight fragments: two register sets, prefetch distance one step
   half8 wa[TM], wb[TM];
 #pragma unroll
-  for (int j = 0; j < TM; ++j) wa[j] = *(const half8*)(wlane + j * 16 * kCB);
-  int64_t wnext = (taps > 1) ? wtap : wcb;                   // Wp offset of step 1
+  for (int j = 0; j < TM; ++j) wa[j] = *(const half8*)(wg + wl + j * 16 * kCB);
   __syncthreads();
 
-  int cb = 0, t = 0, kd = 0, kh = 0, kw = 0, toff = 0;
-#define HALO_STEP(WC, WN, HAS_NEXT)                                                      \
-  {                                                                                      \
-    if (t == taps - 1 && cb + 1 < ncb) {                                                 \
-      if (!PFX) HALO_LOAD_X(cb + 1);                                                     \
-      store_x((cb + 1) & 1, cb + 1);                                                     \
-      __syncthreads();                                                                   \
-      if (PFX && cb + 2 < ncb) HALO_LOAD_X(cb + 2);                                      \
-    }                                                                                    \
-    if (HAS_NEXT) {                                                                      \
-      const half_t* sn_ = wlane + wnext;                                                 \
-      _Pragma("unroll") for (int j = 0; j < TM; ++j) WN[j] = *(const half8*)(sn_ + j * 16 * kCB); \
-    }                                                                                    \
-    const half_t* xs_ = lds + (cb & 1) * box + toff;                                     \
-    half8 a_[TP];                                                                        \
-    _Pragma("unroll") for (int i = 0; i < TP; ++i) a_[i] = *(const half8*)(xs_ + aoff[i]); \
-    _Pragma("unroll") for (int i = 0; i < TP; ++i)                                       \
-      _Pragma("unroll") for (int j = 0; j < TM; ++j)                                     \
+  // Step s = (cb, t) reads Wp tile t * ncb + cb; wnext is the Wp offset of
+  // step s + 1.  After the last step of a channel block the next block's box
+  // (held in registers) is written to the other buffer and one barrier
+  // separates it from both its readers and the previous readers of that
+  // buffer (the steps of channel block cb - 1, all before the last barrier).
+  const int64_t wtap = (int64_t)ncb * wstep;                       // next tap, same block
+  const int64_t wcb = wstep - (int64_t)(taps - 1) * ncb * wstep;   // next block, tap 0
+  int64_t wnext = (taps > 1) ? wtap : wcb;
+  int cb = 0, t = 0, s = 0;
+  int toff = 0;  // tap 0 is at offset 0
+#define HALO_STEP(WC, WN, HAS_NEXT)                                                       \
+  {                                                                                       \
+    {                                                                                     \
+      /* unconditional (a load under a branch is waited for at once); past */             \
+      /* the last step it re-reads the first tile */                                      \
+      const half_t* sn_ = wg + ((HAS_NEXT) ? wnext : 0);                                  \
+      _Pragma("unroll") for (int j = 0; j < TM; ++j) WN[j] = *(const half8*)(sn_ + wl + j * 16 * kCB); \
+    }                                                                                     \
+    const half_t* xs_ = lds + (cb & 1) * box + toff;                                      \
+    half8 a_[TP];                                                                         \
+    _Pragma("unroll") for (int i = 0; i < TP; ++i) a_[i] = *(const half8*)(xs_ + aoff[i]);   \
+    _Pragma("unroll") for (int i = 0; i < TP; ++i)                                        \
+      _Pragma("unroll") for (int j = 0; j < TM; ++j)                                      \
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_[i], WC[j], acc[i][j], 0, 0, 0); \
-    /* advance to the next step */                                                       \
-    if (++t == taps) {                                                                   \
-      t = kd = kh = kw = toff = 0;                                                       \
-      ++cb;                                                                              \
-    } else if (++kw < cp.KW) {                                                           \
-      toff += dkw;                                                                       \
-    } else if (kw = 0, ++kh < cp.KH) {                                                   \
-      toff += dkh;                                                                       \
-    } else {                                                                             \
-      kh = 0;                                                                            \
-      ++kd;                                                                              \
-      toff += dkd;                                                                       \
-    }                                                                                    \
-    /* Wp offset of the step after the new current one */                               \
-    wnext += (t == taps - 1) ? wcb : wtap;                                               \
+    if (++t == taps) {                                                                    \
+      t = 0;                                                                              \
+      if (cb + 1 < ncb) {                                                                 \
+        store_box((cb + 1) & 1, cb + 1);                                                  \
+        __syncthreads();                                                                  \
+        if (cb + 2 < ncb) prefetch_box(cb + 2);                                           \
+      }                                                                                   \
+      ++cb;                                                                               \
+    }                                                                                     \
+    toff = tap_tab[t * kTabStride + 16];                                                  \
+    ++s;                                                                                  \
+    wnext += (t == taps - 1) ? wcb : wtap;                                                \
   }
-  int s = 0;
-  for (; s + 1 < nsteps; s += 2) {
+  while (s + 1 < nsteps) {
     HALO_STEP(wa, wb, true);
-    HALO_STEP(wb, wa, s + 2 < nsteps);
+    HALO_STEP(wb, wa, s + 1 < nsteps);
   }
   if (s < nsteps) HALO_STEP(wa, wb, false);
 #undef HALO_STEP
-#undef HALO_LOAD_X
 
-  // ---- epilogue.  The accumulators go through LDS (the boxes are dead now)
-  // one 16-channel block at a time: staged as 16 rows of consecutive pixels,
-  // Z is added into the stage with loads issued a pass ahead, then a rolled
-  // loop applies bias and activation and stores Y; consecutive lanes touch
-  // consecutive 8-byte pieces of a row.
+  // ---- epilogue: activation and the rounded store.  The accumulators go
+  // through LDS (the boxes are dead now) one 16-channel block at a time,
+  // staged as 16 rows of consecutive pixels; a rolled loop then applies the
+  // activation and stores Y, consecutive lanes writing consecutive 8-byte
+  // pieces of a row.
   __syncthreads();
   constexpr int PW = BN / 2;              // pixels per wave
   constexpr int RP = PW + 4;              // fp32 row pitch (padded)
   constexpr int GPR = PW / 4;             // 4-pixel groups per row
   constexpr int ITER = 16 * GPR / 64;     // groups per lane per pass
   float* stage = (float*)lds + wave * 16 * RP;
-  const bool vec_ok = (cp.OW & 3) == 0;
-  // per-lane slots of a pass: row (channel within the block) and 4 pixels
-  int slot_lds[ITER], slot_nv[ITER];
-  int64_t slot_y[ITER];                   // Y offset of the slot for channel block 0
-  const int mw = m0 + wmi * (BM / 2);     // first channel of this wave
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int idx = it * 64 + lane;
-    const int row = idx / GPR, p4 = (idx % GPR) * 4;
-    const int pl = wpi * PW + p4;
-    const int tw = pl % ht.TW, th = (pl / ht.TW) % ht.TH, td = pl / (ht.TW * ht.TH);
-    const int od = od0 + td, oh = oh0 + th, ow = ow0 + tw;
-    const bool ok = od < cp.OD && oh < cp.OH && ow < cp.OW;
-    slot_lds[it] = row * RP + p4;
-    slot_nv[it] = ok ? min(4, cp.OW - ow) : 0;
-    slot_y[it] = (n * cp.M + g * cp.Mg + mw + row) * cp.out_sz +
-                 ((int64_t)od * cp.OH + oh) * cp.OW + ow;
-  }
+  const int mw0 = m0 + wmi * (BM / 2);    // first channel of this wave
+  // Z (when OW % 4 == 0, a lane's 4 pixels are all in or all out of the
+  // image): every value this wave needs is requested before any is used, as
+  // unconditional 8-byte loads (an invalid slot reads z[0..3] and is never
+  // stored), so the loads overlap instead of waiting one by one.
+  const bool zvec = cp.has_z && vec_y;
   half4 zv[TM][ITER];
-  auto load_z = [&](int j) {
+  if (zvec) {
 #pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      half4 v = {};
-      const int m = mw + j * 16 + (it * 64 + lane) / GPR;
-      if (cp.has_z && slot_nv[it] > 0 && m < cp.Mg) {
-        const half_t* zp = z + slot_y[it] + (int64_t)j * 16 * cp.out_sz;
-        if (vec_ok && slot_nv[it] == 4) {
-          v = *(const half4*)zp;
-        } else {
+    for (int j = 0; j < TM; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (r < slot_nv[it]) v[r] = zp[r];
-        }
+      for (int it = 0; it < ITER; ++it) {
+        const int idx = it * 64 + lane;
+        const int row = idx / GPR, p4 = (idx % GPR) * 4;
+        const int m = mw0 + j * 16 + row;
+        const int pl = wpi * PW + p4;
+        const int tw = pl & (ht.TW - 1), th = (pl >> ht.ltw) & (ht.TH - 1), td = pl >> (ht.ltw + ht.lth);
+        const int od = od0 + td, oh = oh0 + th, ow = ow0 + tw;
+        const bool ok = m < cp.Mg && od < cp.OD && oh < cp.OH && ow < cp.OW;
+        const int64_t zi = (n * cp.M + g * cp.Mg + m) * cp.out_sz + ((int64_t)od * cp.OH + oh) * cp.OW + ow;
+        zv[j][it] = *(const half4*)(ok ? z + zi : z);
       }
-      zv[j][it] = v;
-    }
-  };
-  // every Z value of this wave is requested before any is needed
-  if (cp.has_z) {
-#pragma unroll
-    for (int j = 0; j < TM; ++j) load_z(j);
   }
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
@@ -352,10 +397,11 @@ __global__ __launch_bounds__(kThreads, 2) void halo_kernel(const half_t* __restr
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (cp.has_z) {
+    if (zvec) {  // Z into the stage (unrolled: zv is indexed statically)
 #pragma unroll
       for (int it = 0; it < ITER; ++it) {
-        float4v* sp = (float4v*)(stage + slot_lds[it]);
+        const int idx = it * 64 + lane;
+        float4v* sp = (float4v*)(stage + (idx / GPR) * RP + (idx % GPR) * 4);
         float4v v = *sp;
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] += (float)zv[j][it][r];
@@ -365,26 +411,29 @@ __global__ __launch_bounds__(kThreads, 2) void halo_kernel(const half_t* __restr
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    // rolled: slot coordinates are recomputed with shifts (tile width and
-    // height are powers of two), the activation is dispatched per 4 values
+    // rolled: one activation dispatch per 4 values
     for (int it = 0; it < ITER; ++it) {
       const int idx = it * 64 + lane;
       const int row = idx / GPR, p4 = (idx % GPR) * 4;
-      const int m = mw + j * 16 + row;
+      const int m = mw0 + j * 16 + row;
       const int pl = wpi * PW + p4;
-      const int oh = oh0 + (pl >> ht.ltw), ow = ow0 + (pl & (ht.TW - 1));
-      if (m >= cp.Mg || oh >= cp.OH || ow >= cp.OW) continue;
+      const int tw = pl & (ht.TW - 1), th = (pl >> ht.ltw) & (ht.TH - 1), td = pl >> (ht.ltw + ht.lth);
+      const int od = od0 + td, oh = oh0 + th, ow = ow0 + tw;
+      if (m >= cp.Mg || od >= cp.OD || oh >= cp.OH || ow >= cp.OW) continue;
       const int nv = min(4, cp.OW - ow);
       const int64_t yi = (n * cp.M + g * cp.Mg + m) * cp.out_sz +
-                         ((int64_t)od0 * cp.OH + oh) * cp.OW + ow;
+                         ((int64_t)od * cp.OH + oh) * cp.OW + ow;
       float4v v4 = *(const float4v*)(stage + row * RP + p4);
-      const float bv = cp.has_bias ? to_f32(bias[g * cp.Mg + m]) : 0.0f;
-      v4 += bv;
+      if (cp.has_z && !zvec) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (r < nv) v4[r] += to_f32(z[yi + r]);
+      }
       v4 = act_apply4(cp.act, v4, cp.alpha, cp.beta);
       half4 out;
 #pragma unroll
       for (int r = 0; r < 4; ++r) out[r] = (half_t)v4[r];
-      if (vec_ok && nv == 4) {
+      if (vec_y && nv == 4) {
         *(half4*)(y + yi) = out;
       } else {
 #pragma unroll
@@ -398,21 +447,89 @@ __global__ __launch_bounds__(kThreads, 2) void halo_kernel(const half_t* __restr
   }
 }
 
+// Block -> work unit (group, tile, m block).  Blocks are dealt to the XCDs
+// round-robin; with remap the m blocks of a tile are 8 blocks apart, i.e.
+// back to back on the same XCD, so the second reads X from that XCD's L2.
+template <int BM, int BN, int PF, bool VEC>
+__global__ __launch_bounds__(kThreads, 2) void halo_kernel(const half_t* __restrict__ x,
+                                                           const half_t* __restrict__ wp,
+                                                           const half_t* __restrict__ bias,
+                                                           const half_t* z, half_t* y,
+                                                           ConvParams cp, HaloTile ht) {
+  const int per_g = ht.ntile * ht.nmb;
+  Unit u;
+  u.g = blockIdx.x / per_g;
+  const int rb = blockIdx.x - u.g * per_g;
+  int tile;
+  if (ht.remap) {
+    const int v = rb >> 3;
+    u.mb = v % ht.nmb;
+    tile = (v / ht.nmb) * 8 + (rb & 7);
+  } else {
+    u.mb = rb % ht.nmb;
+    tile = rb / ht.nmb;
+  }
+  const int tw_i = tile % ht.tiles_w;
+  tile /= ht.tiles_w;
+  const int th_i = tile % ht.tiles_h;
+  tile /= ht.tiles_h;
+  const int td_i = tile % ht.tiles_d;
+  u.n = tile / ht.tiles_d;
+  u.od0 = td_i * ht.TD;
+  u.oh0 = th_i * ht.TH;
+  u.ow0 = tw_i * ht.TW;
+  halo_tile<BM, BN, PF, VEC>(x, wp, bias, z, y, cp, ht, u);
+}
+
 struct Choice {
-  int bm, bn, waves;
+  int bm, bn;
   HaloTile ht;
 };
 
-// Pick BM, BN and the output tile; false if nothing fits.
+int log2i(int v) { return 31 - __builtin_clz((unsigned)v); }
+
+// Fill the tile-dependent fields; false if the box does not fit.
+bool make_tile(const ConvParams& cp, int bm, int bn, int tw, size_t max_lds, HaloTile& ht) {
+  const int th = bn / tw, td = 1;
+  ht.TD = td; ht.TH = th; ht.TW = tw;
+  ht.ltw = log2i(tw);
+  ht.lth = log2i(th);
+  ht.BD = (td - 1) * cp.sd + (cp.KD - 1) * cp.dd + 1;
+  ht.BH = (th - 1) * cp.sh + (cp.KH - 1) * cp.dh + 1;
+  ht.BW = (tw - 1) * cp.sw + (cp.KW - 1) * cp.dw + 1;
+  ht.ND = (int)cdiv(ht.BD, cp.sd);
+  ht.NH = (int)cdiv(ht.BH, cp.sh);
+  ht.NW = (int)cdiv(ht.BW, cp.sw);
+  ht.LH = cp.sh * ht.NH;
+  ht.LW = cp.sw * ht.NW;
+  const int64_t bpos = (int64_t)cp.sd * ht.ND * ht.LH * ht.LW;
+  // (the tap table lives in the padding of the first kMaxTaps box rows)
+  if (bpos < kMaxTaps || bpos > (1 << 16) || lds_bytes((int)bpos, bn) > max_lds) return false;
+  ht.box_pos = (int)bpos;
+  ht.tiles_d = (int)cdiv(cp.OD, td);
+  ht.tiles_h = (int)cdiv(cp.OH, th);
+  ht.tiles_w = (int)cdiv(cp.OW, tw);
+  const int64_t ntile = cp.n * ht.tiles_d * ht.tiles_h * ht.tiles_w;
+  ht.ncb = (int)cdiv(cp.Cg, kCB);
+  ht.mgp = (int)(cdiv(cp.Mg, bm) * bm);
+  ht.nmb = (int)cdiv(cp.Mg, bm);
+  if (ntile * ht.nmb * cp.G >= ((int64_t)1 << 31)) return false;
+  ht.ntile = (int)ntile;
+  ht.remap = (ntile % 8) == 0;
+  ht.vec_x = (cp.W % 8) == 0;
+  return true;
+}
+
+// Pick BN and the output tile (BM = 128); false if nothing fits.  Tiles whose
+// two boxes fit two blocks per CU are preferred; larger boxes (3-D, strided
+// 3x3) run one block per CU.
 bool choose(const ConvParams& cp, Choice& ch) {
-  if (cp.Cg < 16) return false;
-  // BM = 256 with 4 waves spills registers: 128 output channels per block.
-  const int bm = 128;
-  const int ncb = (int)cdiv(cp.Cg, kCB);
-  const int waves = 4;
+  if (cp.Cg < 16 || cp.taps > kMaxTaps) return false;
+  const int bm = 128;  // BM = 256 with 4 waves spills registers
   const int tws[] = {16, 32, 64, 128, 256};
   int bn_first = 256;  // FUSEDCONV_HALO_BN=128 restricts the tile to 128 pixels (tuning)
   if (const char* e = getenv("FUSEDCONV_HALO_BN")) bn_first = atoi(e) == 128 ? 128 : 256;
+  for (size_t max_lds : {kLds2, kMaxLds})
   for (int bn : {256, 128}) {
     if (bn > bn_first) continue;
     // tile widths (multiples of 16; tile = bn / tw rows) in order of padded
@@ -434,28 +551,13 @@ bool choose(const ConvParams& cp, Choice& ch) {
           std::swap(order[a], order[b2]);
         }
     for (int oi = 0; oi < no; ++oi) {
-      const int tw = order[oi], th = bn / tw, td = 1;
       HaloTile ht;
-      ht.TD = td; ht.TH = th; ht.TW = tw;
-      ht.ltw = 31 - __builtin_clz((unsigned)tw);
-      ht.BD = (td - 1) * cp.sd + (cp.KD - 1) * cp.dd + 1;
-      ht.BH = (th - 1) * cp.sh + (cp.KH - 1) * cp.dh + 1;
-      ht.BW = (tw - 1) * cp.sw + (cp.KW - 1) * cp.dw + 1;
-      ht.tiles_d = (int)cdiv(cp.OD, td);
-      ht.tiles_h = (int)cdiv(cp.OH, th);
-      ht.tiles_w = (int)cdiv(cp.OW, tw);
-      ht.ncb = ncb;
-      ht.mgp = (int)(cdiv(cp.Mg, bm) * bm);
-      ht.vec_x = (cp.W % 8) == 0;
-      const int64_t bpos = (int64_t)ht.BD * ht.BH * ht.BW;
-      if (bpos > (1 << 20) || lds_bytes((int)bpos, bn) > kMaxLds) continue;
-      const int64_t blocks = cp.n * ht.tiles_d * ht.tiles_h * ht.tiles_w;
-      if (blocks >= ((int64_t)1 << 31) || cdiv(cp.Mg, bm) > 65535 || cp.G > 65535) continue;
+      if (!make_tile(cp, bm, bn, order[oi], max_lds, ht)) continue;
       // the tiles must not be mostly padding
-      if ((double)ht.tiles_d * td * ht.tiles_h * th * ht.tiles_w * tw > 2.0 * cp.out_sz) continue;
+      if ((double)ht.tiles_d * ht.TD * ht.tiles_h * ht.TH * ht.tiles_w * ht.TW > 2.0 * cp.out_sz)
+        continue;
       ch.bm = bm;
       ch.bn = bn;
-      ch.waves = waves;
       ch.ht = ht;
       return true;
     }
@@ -473,15 +575,14 @@ int launch_repack(const ConvParams& cp, const Choice& ch, const RunArgs& a) {
   return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
 }
 
-template <int BM, int BN, bool PFX>
+template <int BM, int BN, int PF, bool VEC>
 int launch_t(const Geometry& g, const Choice& ch, const RunArgs& a) {
   const ConvParams& cp = g.cp;
   hipStream_t st = (hipStream_t)a.stream;
-  const int bpos = ch.ht.BD * ch.ht.BH * ch.ht.BW;
-  const size_t lds = lds_bytes(bpos, BN);
+  const size_t lds = lds_bytes(ch.ht.box_pos, BN);
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)halo_kernel<BM, BN, PFX>,
+    if (hipFuncSetAttribute((const void*)halo_kernel<BM, BN, PF, VEC>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) !=
         hipSuccess)
       return FUSEDCONV_ERR_LAUNCH;
@@ -491,11 +592,10 @@ int launch_t(const Geometry& g, const Choice& ch, const RunArgs& a) {
     const int rc = launch_repack(cp, ch, a);
     if (rc != FUSEDCONV_OK) return rc;
   }
-  dim3 grid((unsigned)(cp.n * ch.ht.tiles_d * ch.ht.tiles_h * ch.ht.tiles_w),
-            (unsigned)cdiv(cp.Mg, BM), (unsigned)cp.G);
-  hipLaunchKernelGGL((halo_kernel<BM, BN, PFX>), grid, dim3(kThreads), lds, st, (const half_t*)a.x,
-                     (const half_t*)a.ws, (const half_t*)a.bias, (const half_t*)a.z,
-                     (half_t*)a.y, cp, ch.ht);
+  const unsigned blocks = (unsigned)((int64_t)ch.ht.ntile * ch.ht.nmb * cp.G);
+  hipLaunchKernelGGL((halo_kernel<BM, BN, PF, VEC>), dim3(blocks), dim3(kThreads), lds, st,
+                     (const half_t*)a.x, (const half_t*)a.ws, (const half_t*)a.bias,
+                     (const half_t*)a.z, (half_t*)a.y, cp, ch.ht);
   return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
 }
 
@@ -503,7 +603,7 @@ int launch_t(const Geometry& g, const Choice& ch, const RunArgs& a) {
 
 bool igemm_halo_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32_t& tile_w,
                      size_t& workspace) {
-  if (dtype != FUSEDCONV_F16 || cp.taps > 64) return false;
+  if (dtype != FUSEDCONV_F16) return false;
   Choice ch;
   if (!choose(cp, ch)) return false;
   tile_h = ch.ht.TH;
@@ -521,7 +621,9 @@ int prepare_igemm_halo(const Geometry& g, const Plan&, const RunArgs& a) {
 int launch_igemm_halo(const Geometry& g, const Plan&, const RunArgs& a) {
   Choice ch;
   if (!choose(g.cp, ch)) return FUSEDCONV_ERR_ROUTE;
-  return ch.bn == 256 ? launch_t<128, 256, true>(g, ch, a) : launch_t<128, 128, true>(g, ch, a);
+  if (ch.ht.vec_x)
+    return ch.bn == 256 ? launch_t<128, 256, 1, true>(g, ch, a) : launch_t<128, 128, 2, true>(g, ch, a);
+  return ch.bn == 256 ? launch_t<128, 256, 1, false>(g, ch, a) : launch_t<128, 128, 2, false>(g, ch, a);
 }
 
 }  // namespace fc

@@ -189,13 +189,17 @@ HALO_CASES = [
     # (x, w, attrs) for the channel-last halo route (fp16)
     ([2, 64, 16, 16], [96, 64, 3, 3], dict(pads=[1, 1, 1, 1])),            # M tail (96 < 128)
     ([2, 40, 13, 13], [64, 40, 3, 3], dict(pads=[1, 1, 1, 1])),            # partial channel
-    # block, W % 8 != 0 (scalar loader), OW % 4 != 0 (scalar epilogue)
+    # block, W % 8 != 0 (scalar loader), OW % 4 != 0 (residual in the epilogue)
     ([1, 64, 24, 24], [64, 64, 2, 2], dict(strides=[2, 2])),               # patchify, stride 2
     ([2, 64, 500], [64, 32, 5], dict(group=2, auto_pad="SAME_UPPER")),     # 1-D, 2 groups
     ([1, 32, 6, 16, 16], [48, 32, 3, 3, 3], dict(pads=[1] * 6)),           # 3-D
     ([2, 48, 21, 13], [40, 48, 3, 3], dict(dilations=[2, 1], auto_pad="SAME_LOWER")),
-    ([1, 64, 40, 40], [300, 64, 3, 3], dict(pads=[1, 1, 1, 1])),           # BM 256, 2 m tiles
+    ([1, 64, 40, 40], [300, 64, 3, 3], dict(pads=[1, 1, 1, 1])),           # 3 m blocks
     ([2, 32, 34, 70], [64, 32, 5, 7], dict(strides=[1, 2], pads=[2, 3, 2, 3])),  # 35 taps
+    ([2, 96, 16, 16], [64, 96, 1, 1], {}),                                  # 1x1: one tap per block
+    ([1, 64, 33, 40], [128, 64, 3, 3], dict(strides=[2, 2], pads=[1, 1, 1, 1])),  # stride 2 3x3
+    ([2, 16, 12, 16], [32, 16, 1, 1], {}),                                  # a single K step
+    ([1, 32, 4, 20, 32], [64, 32, 1, 3, 3], dict(strides=[1, 2, 2], pads=[0, 1, 1] * 2)),  # 3-D strided
 ]
 
 
@@ -214,6 +218,28 @@ def test_halo_route(ci):
         got = run_gpu(x, w, b, z, route="igemm_halo", **a)
         ref = oracle.fusedconv(x, w, b, z, **a)
         check(got, ref, "f16", f"halo case {ci}")
+
+
+# Grids of 1024 work units (4 blocks per CU), XCD-remapped block order, full
+# output compared; the second shape's tiles run partly past the output (12 of
+# 16 rows).
+LARGE_GRID_CASES = [
+    ([1024, 32, 16, 16], [128, 32, 3, 3], dict(pads=[1, 1, 1, 1])),
+    ([1024, 32, 12, 16], [128, 32, 3, 3], dict(pads=[1, 1, 1, 1])),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(LARGE_GRID_CASES)))
+def test_halo_large_grid(ci):
+    xs, ws, attrs = LARGE_GRID_CASES[ci]
+    h = B.Handle("f16", xs, ws, [ws[0]], None, route="igemm_halo", **attrs)
+    x, w, b, z = random_tensors([9200, ci], "f16", xs, ws, [ws[0]], h.y_shape, dist="normal",
+                                w_std=1.0 / np.sqrt(np.prod(ws[1:])))
+    a = dict(attrs, activation="QuickGelu", activation_params=f32params([1.702]))
+    log(f"CASE halo large grid {ci} x={xs} w={ws} {a}")
+    got = run_gpu(x, w, b, z, route="igemm_halo", **a)
+    ref = oracle.fusedconv(x, w, b, z, **a)
+    check(got, ref, "f16", f"halo large grid case {ci}")
 
 
 @pytest.mark.parametrize("route", ["direct", "igemm", "depthwise"])
