@@ -16,23 +16,29 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfusedconv.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["resolver.cpp", "planner.cpp", "capi.cpp", "kernels_direct.hip", "kernels_igemm.hip",
-           "kernels_depthwise.hip", "kernels_halo.hip"]
+SOURCES = ["resolver.cpp", "planner.cpp", "capi.cpp", "kernels_direct.hip", "kernels_igemm.hip"]
+# Kernels specialised per activation: compiled once per activation id
+# (-DFC_ACT=k, k = 0 .. ACT_COUNT-1); unit 0 also holds the route entry points.
+ACT_SOURCES = ["kernels_depthwise.hip", "kernels_halo.hip", "kernels_smallc.hip"]
+ACT_COUNT = 15
 ARCH = "gfx950"
 # Packed fp32 ops stay off (the compiler is not allowed to form v_pk_*_f32).
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(job) -> str:
+    src, act = job
+    stem = os.path.splitext(src)[0] + ("" if act is None else f"_a{act}")
+    obj = os.path.join(BUILD, stem + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = ["hipcc", *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    defs = [] if act is None else [f"-DFC_ACT={act}"]
+    cmd = ["hipcc", *FLAGS, *defs, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(ln for ln in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in ln)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{out}")
+        raise RuntimeError(f"hipcc failed for {stem}:\n{out}")
     if out.strip():
         print(out, file=sys.stderr)
     return obj
@@ -40,8 +46,10 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    jobs = [(f, k) for f in ACT_SOURCES for k in range(ACT_COUNT)] + [(f, None) for f in SOURCES]
+    workers = max(1, min(16, os.cpu_count() or 1))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = list(ex.map(_compile, jobs))
     tmp = LIB + ".tmp%d" % os.getpid()
     subprocess.check_call(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
                            *objs])

@@ -113,12 +113,14 @@ int fusedconv_prepare_weights(const fusedconv_handle* h, const void* w, void* wo
   if (h->plan.workspace > 0 && (!workspace || workspace_bytes < h->plan.workspace))
     return set_err(FUSEDCONV_ERR_WORKSPACE,
                    "workspace smaller than fusedconv_workspace_size() reports");
-  if (h->plan.route != FUSEDCONV_ROUTE_IGEMM_HALO) return FUSEDCONV_OK;
+  if (h->plan.route != FUSEDCONV_ROUTE_IGEMM_HALO && h->plan.route != FUSEDCONV_ROUTE_SMALLC)
+    return FUSEDCONV_OK;
   int rc = check_device();
   if (rc != FUSEDCONV_OK) return rc;
   (void)hipGetLastError();
   fc::RunArgs a{nullptr, w, nullptr, nullptr, nullptr, workspace, stream, 0u};
-  rc = fc::prepare_igemm_halo(h->geo, h->plan, a);
+  rc = h->plan.route == FUSEDCONV_ROUTE_SMALLC ? fc::prepare_smallc(h->geo, h->plan, a)
+                                                : fc::prepare_igemm_halo(h->geo, h->plan, a);
   if (rc != FUSEDCONV_OK) {
     hipError_t e = hipGetLastError();
     return set_err(rc, std::string("kernel launch failed: ") + hipGetErrorString(e));
@@ -153,6 +155,7 @@ int fusedconv_run_ex(const fusedconv_handle* h, const void* x, const void* w, co
     case FUSEDCONV_ROUTE_IGEMM: rc = fc::launch_igemm(h->geo, h->plan, a); break;
     case FUSEDCONV_ROUTE_DEPTHWISE: rc = fc::launch_depthwise(h->geo, h->plan, a); break;
     case FUSEDCONV_ROUTE_IGEMM_HALO: rc = fc::launch_igemm_halo(h->geo, h->plan, a); break;
+    case FUSEDCONV_ROUTE_SMALLC: rc = fc::launch_smallc(h->geo, h->plan, a); break;
     default: return set_err(FUSEDCONV_ERR_ROUTE, "handle has no route");
   }
   if (rc != FUSEDCONV_OK) {

@@ -19,32 +19,56 @@ typedef _Float16 half_t;
 template <typename T> __device__ __forceinline__ float to_f32(T v) { return (float)v; }
 template <typename T> __device__ __forceinline__ T from_f32(float v) { return (T)v; }
 
-// Activation A (compile-time) applied to v.  Sigmoid and QuickGelu use the
-// hardware exp2 and reciprocal (__expf, v_rcp_f32): relative error ~1e-6,
-// far inside the fp16 and fp32 tolerances, at a fraction of the cost of the
-// IEEE library division.
+// erfc-style tail of Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26: for u >= 0, erf(u) = 1 - P(t) exp(-u^2) with t = 1/(1 + p u)
+// and a fifth-degree polynomial P; |error| <= 1.5e-7.  Returns P(t) exp(-u^2),
+// i.e. 1 - erf(u), so callers form 1 + erf(x) for x < 0 without cancellation.
+__device__ __forceinline__ float erfc_as(float u) {
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * u);
+  const float poly =
+      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  return poly * __expf(-u * u);
+}
+__device__ __forceinline__ float erf_fast(float x) {
+  const float r = 1.0f - erfc_as(fabsf(x));
+  return x < 0.0f ? -r : r;
+}
+// tanh(x) = 1 - 2 / (1 + e^(2x)); saturates correctly at both ends (e^(2x)
+// -> inf gives 1, -> 0 gives -1); absolute error ~1e-7.
+__device__ __forceinline__ float tanh_fast(float x) {
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __expf(2.0f * x));
+}
+
+// Activation A (compile-time) applied to v.  The exp-based ones use the
+// hardware exp2 and reciprocal (__expf, v_rcp_f32) and the erf / tanh forms
+// above: errors of order 1e-7 absolute, far inside the fp16 and fp32
+// tolerances, at a fraction of the cost of the library routines.
 template <int A>
 __device__ __forceinline__ float act_t(float v, float a, float b) {
   if constexpr (A == ACT_NONE) return v;
   if constexpr (A == ACT_RELU) return v > 0.0f ? v : 0.0f;
   if constexpr (A == ACT_LEAKYRELU) return v >= 0.0f ? v : a * v;
   if constexpr (A == ACT_SIGMOID) return __builtin_amdgcn_rcpf(1.0f + __expf(-v));
-  if constexpr (A == ACT_TANH) return tanhf(v);
+  if constexpr (A == ACT_TANH) return tanh_fast(v);
   if constexpr (A == ACT_HARDSIGMOID) return fminf(fmaxf(a * v + b, 0.0f), 1.0f);
   if constexpr (A == ACT_HARDSWISH) return v * fminf(fmaxf(v * (1.0f / 6.0f) + 0.5f, 0.0f), 1.0f);
   if constexpr (A == ACT_CLIP) return fminf(fmaxf(v, a), b);
   if constexpr (A == ACT_QUICKGELU) return v * __builtin_amdgcn_rcpf(1.0f + __expf(-a * v));
   if constexpr (A == ACT_ELU) return v > 0.0f ? v : a * expm1f(v);
   if constexpr (A == ACT_GELU) {
-    if (a == 0.0f) return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+    if (a == 0.0f) {
+      // 0.5 v (1 + erf(v / sqrt 2)); for v < 0, 1 + erf = erfc(|v| / sqrt 2)
+      const float c = erfc_as(fabsf(v) * 0.70710678118654752f);
+      return 0.5f * v * (v < 0.0f ? c : 2.0f - c);
+    }
     // nonzero "approximate" flag: tanh form
-    return 0.5f * v * (1.0f + tanhf(0.79788456080286536f * (v + 0.044715f * v * v * v)));
+    return 0.5f * v * (1.0f + tanh_fast(0.79788456080286536f * (v + 0.044715f * v * v * v)));
   }
   if constexpr (A == ACT_FASTGELU)
-    return 0.5f * v * (1.0f + tanhf(0.79788456080286536f * (v + 0.044715f * v * v * v)));
-  if constexpr (A == ACT_SOFTPLUS) return fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v)));
+    return 0.5f * v * (1.0f + tanh_fast(0.79788456080286536f * (v + 0.044715f * v * v * v)));
+  if constexpr (A == ACT_SOFTPLUS) return fmaxf(v, 0.0f) + log1pf(__expf(-fabsf(v)));
   if constexpr (A == ACT_THRESHOLDEDRELU) return v > a ? v : 0.0f;
-  if constexpr (A == ACT_ERF) return erff(v);
+  if constexpr (A == ACT_ERF) return erf_fast(v);
   return v;
 }
 
@@ -82,6 +106,15 @@ __device__ __forceinline__ act4_t act_apply4(int act, act4_t v, float a, float b
 #pragma unroll
     for (int k = 0; k < 4; ++k) r[k] = act_t<A>(v[k], a, b);
   });
+  return r;
+}
+
+// Compile-time form for kernels specialised per activation.
+template <int A>
+__device__ __forceinline__ act4_t act4(act4_t v, float a, float b) {
+  act4_t r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r[k] = act_t<A>(v[k], a, b);
   return r;
 }
 

@@ -32,7 +32,7 @@ struct Plan {
   int32_t tile;          // route-specific variant id
   int32_t k_tiles;       // IGEMM: number of BK-wide K tiles
   int32_t k_tiles_per_split;
-  // DEPTHWISE / IGEMM_HALO: output tile extents
+  // DEPTHWISE / IGEMM_HALO / SMALLC: output tile extents
   int32_t tile_h, tile_w;
   size_t workspace;      // bytes
   char name[64];
@@ -58,11 +58,36 @@ int launch_igemm(const Geometry& g, const Plan& p, const RunArgs& a);
 int launch_depthwise(const Geometry& g, const Plan& p, const RunArgs& a);
 int launch_igemm_halo(const Geometry& g, const Plan& p, const RunArgs& a);
 int prepare_igemm_halo(const Geometry& g, const Plan& p, const RunArgs& a);
+int launch_smallc(const Geometry& g, const Plan& p, const RunArgs& a);
+int prepare_smallc(const Geometry& g, const Plan& p, const RunArgs& a);
+
+// Kernels whose activation is a compile-time parameter: the build compiles
+// their source once per activation id (FC_ACT = 0 .. ACT_COUNT-1); unit k
+// defines <name>k(g, a), and unit 0 also holds the route's entry points and
+// a table of the ACT_COUNT launchers, indexed by the resolved activation.
+typedef int (*ActLaunchFn)(const Geometry& g, const RunArgs& a);
+#define FC_CAT2(a, b) a##b
+#define FC_CAT(a, b) FC_CAT2(a, b)
+#define FC_ACT_DECLS(name)                                                                 \
+  int name##0(const Geometry&, const RunArgs&); int name##1(const Geometry&, const RunArgs&);   \
+  int name##2(const Geometry&, const RunArgs&); int name##3(const Geometry&, const RunArgs&);   \
+  int name##4(const Geometry&, const RunArgs&); int name##5(const Geometry&, const RunArgs&);   \
+  int name##6(const Geometry&, const RunArgs&); int name##7(const Geometry&, const RunArgs&);   \
+  int name##8(const Geometry&, const RunArgs&); int name##9(const Geometry&, const RunArgs&);   \
+  int name##10(const Geometry&, const RunArgs&); int name##11(const Geometry&, const RunArgs&); \
+  int name##12(const Geometry&, const RunArgs&); int name##13(const Geometry&, const RunArgs&); \
+  int name##14(const Geometry&, const RunArgs&);
+#define FC_ACT_TABLE(name)                                                                 \
+  { name##0, name##1, name##2, name##3, name##4, name##5, name##6, name##7, name##8,        \
+    name##9, name##10, name##11, name##12, name##13, name##14 }
+static_assert(ACT_COUNT == 15, "FC_ACT_DECLS / FC_ACT_TABLE list every activation id");
 
 // Depthwise planning helper (kernels_depthwise.hip knows its LDS budget).
 bool depthwise_fits(const ConvParams& cp, int32_t& tile_h, int32_t& tile_w);
 bool depthwise_fast(const ConvParams& cp, int32_t dtype);
 bool igemm_halo_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32_t& tile_w,
                      size_t& workspace);
+bool smallc_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32_t& tile_w,
+                 size_t& workspace);
 
 }  // namespace fc

@@ -23,7 +23,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kVec = 4;
-constexpr int kMaxTileBytes = 64 * 1024;
+[[maybe_unused]] constexpr int kMaxTileBytes = 64 * 1024;
 
 // LDS row pitch: covers the window of every strip, including the columns of
 // the last strip past tile_w (tile_w rounded up to kVec), so no read leaves
@@ -194,7 +194,7 @@ bool dw_fast_plan(const ConvParams& cp, DwFast& f) {
   return found;
 }
 
-template <int KS, int kR, int kV>
+template <int KS, int kR, int kV, int ACT>
 __global__ __launch_bounds__(kThreads) void dw_fast_kernel(const half_t* __restrict__ x,
                                                            const half_t* __restrict__ w,
                                                            const half_t* __restrict__ bias,
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void dw_fast_kernel(const half_t* __restr
 #pragma unroll
             for (int j = 0; j < 4; ++j) v4[j] += (float)zv[j];
           }
-          v4 = act_apply4(cp.act, v4, cp.alpha, cp.beta);
+          v4 = act4<ACT>(v4, cp.alpha, cp.beta);
           h4 out;
 #pragma unroll
           for (int j = 0; j < 4; ++j) out[j] = (half_t)v4[j];
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void dw_fast_kernel(const half_t* __restr
             const int ow = owq + cp.dw * j;
             if (ow < cp.OW && cp.has_z) v4[j] += to_f32(z[yrow + ow]);
           }
-          v4 = act_apply4(cp.act, v4, cp.alpha, cp.beta);
+          v4 = act4<ACT>(v4, cp.alpha, cp.beta);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int ow = owq + cp.dw * j;
@@ -386,7 +386,7 @@ int launch_fast(const Geometry& g, const DwFast& f, const RunArgs& a) {
   const ConvParams& cp = g.cp;
   const int64_t blocks = (cp.n * cp.M + f.pb - 1) / f.pb;
   const size_t shmem = (size_t)f.pb * f.plane_halves * 2;
-  hipLaunchKernelGGL((dw_fast_kernel<KS, R, V>), dim3((unsigned)blocks), dim3(kThreads), shmem,
+  hipLaunchKernelGGL((dw_fast_kernel<KS, R, V, FC_ACT>), dim3((unsigned)blocks), dim3(kThreads), shmem,
                      (hipStream_t)a.stream, (const half_t*)a.x, (const half_t*)a.w,
                      (const half_t*)a.bias, (const half_t*)a.z, (half_t*)a.y, cp, f);
   return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
@@ -407,6 +407,25 @@ int launch_t(const Geometry& g, const Plan& p, const RunArgs& a) {
 
 }  // namespace
 
+#ifndef FC_ACT
+#error "compiled once per activation id: -DFC_ACT=<0..ACT_COUNT-1>"
+#endif
+
+// the packed-fp16 depthwise kernel with activation FC_ACT
+int FC_CAT(launch_dwfast_act_, FC_ACT)(const Geometry& g, const RunArgs& a) {
+  DwFast f;
+  if (!dw_fast_plan(g.cp, f)) return FUSEDCONV_ERR_ROUTE;
+  switch (g.cp.KH) {
+    case 3: return launch_fast<3, 4, 4>(g, f, a);
+    case 5: return launch_fast<5, 4, 4>(g, f, a);
+    case 7: return launch_fast<7, 4, 4>(g, f, a);
+    default: return FUSEDCONV_ERR_ROUTE;
+  }
+}
+
+#if FC_ACT == 0
+FC_ACT_DECLS(launch_dwfast_act_)
+
 bool depthwise_fits(const ConvParams& cp, int32_t& tile_h, int32_t& tile_w) {
   if (cp.Cg != 1 || cp.D != 1 || cp.KD != 1) return false;
   int tw = cp.OW < 256 ? cp.OW : 256;
@@ -426,16 +445,8 @@ bool depthwise_fits(const ConvParams& cp, int32_t& tile_h, int32_t& tile_w) {
 int launch_depthwise(const Geometry& g, const Plan& p, const RunArgs& a) {
   DwFast f;
   if (p.tile == 1 && g.dtype == FUSEDCONV_F16 && dw_fast_plan(g.cp, f)) {
-#define DW_CASE(KS) \
-  case KS:          \
-    return launch_fast<KS, 4, 4>(g, f, a);
-    switch (g.cp.KH) {
-      DW_CASE(3)
-      DW_CASE(5)
-      DW_CASE(7)
-      default: break;
-    }
-#undef DW_CASE
+    static const ActLaunchFn table[ACT_COUNT] = FC_ACT_TABLE(launch_dwfast_act_);
+    return table[g.cp.act](g, a);
   }
   return g.dtype == FUSEDCONV_F16 ? launch_t<half_t>(g, p, a) : launch_t<float>(g, p, a);
 }
@@ -444,5 +455,6 @@ bool depthwise_fast(const ConvParams& cp, int32_t dtype) {
   DwFast f;
   return dtype == FUSEDCONV_F16 && dw_fast_plan(cp, f);
 }
+#endif
 
 }  // namespace fc

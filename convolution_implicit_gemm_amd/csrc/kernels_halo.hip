@@ -117,7 +117,7 @@ struct Unit {
 // block (each item = 4 channels x 8 columns of one box row, 16 registers);
 // items beyond PF * 256 are loaded and stored at the channel-block boundary.
 // VEC: W % 8 == 0, so an item's 8 columns are one aligned 16-byte load.
-template <int BM, int BN, int PF, bool VEC>
+template <int BM, int BN, int PF, bool VEC, int ACT>
 __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
                                           const half_t* __restrict__ wp,
                                           const half_t* __restrict__ bias, const half_t* z,
@@ -411,7 +411,7 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    // rolled: one activation dispatch per 4 values
+    // rolled
     for (int it = 0; it < ITER; ++it) {
       const int idx = it * 64 + lane;
       const int row = idx / GPR, p4 = (idx % GPR) * 4;
@@ -429,7 +429,7 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
         for (int r = 0; r < 4; ++r)
           if (r < nv) v4[r] += to_f32(z[yi + r]);
       }
-      v4 = act_apply4(cp.act, v4, cp.alpha, cp.beta);
+      v4 = act4<ACT>(v4, cp.alpha, cp.beta);
       half4 out;
 #pragma unroll
       for (int r = 0; r < 4; ++r) out[r] = (half_t)v4[r];
@@ -450,7 +450,7 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
 // Block -> work unit (group, tile, m block).  Blocks are dealt to the XCDs
 // round-robin; with remap the m blocks of a tile are 8 blocks apart, i.e.
 // back to back on the same XCD, so the second reads X from that XCD's L2.
-template <int BM, int BN, int PF, bool VEC>
+template <int BM, int BN, int PF, bool VEC, int ACT>
 __global__ __launch_bounds__(kThreads, 2) void halo_kernel(const half_t* __restrict__ x,
                                                            const half_t* __restrict__ wp,
                                                            const half_t* __restrict__ bias,
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(kThreads, 2) void halo_kernel(const half_t* __restr
   u.od0 = td_i * ht.TD;
   u.oh0 = th_i * ht.TH;
   u.ow0 = tw_i * ht.TW;
-  halo_tile<BM, BN, PF, VEC>(x, wp, bias, z, y, cp, ht, u);
+  halo_tile<BM, BN, PF, VEC, ACT>(x, wp, bias, z, y, cp, ht, u);
 }
 
 struct Choice {
@@ -580,10 +580,10 @@ int launch_t(const Geometry& g, const Choice& ch, const RunArgs& a) {
   const ConvParams& cp = g.cp;
   hipStream_t st = (hipStream_t)a.stream;
   const size_t lds = lds_bytes(ch.ht.box_pos, BN);
+  const void* kfn = (const void*)halo_kernel<BM, BN, PF, VEC, FC_ACT>;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)halo_kernel<BM, BN, PF, VEC>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) !=
+    if (hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) !=
         hipSuccess)
       return FUSEDCONV_ERR_LAUNCH;
     attr_set = true;
@@ -593,13 +593,29 @@ int launch_t(const Geometry& g, const Choice& ch, const RunArgs& a) {
     if (rc != FUSEDCONV_OK) return rc;
   }
   const unsigned blocks = (unsigned)((int64_t)ch.ht.ntile * ch.ht.nmb * cp.G);
-  hipLaunchKernelGGL((halo_kernel<BM, BN, PF, VEC>), dim3(blocks), dim3(kThreads), lds, st,
+  hipLaunchKernelGGL((halo_kernel<BM, BN, PF, VEC, FC_ACT>), dim3(blocks), dim3(kThreads), lds, st,
                      (const half_t*)a.x, (const half_t*)a.ws, (const half_t*)a.bias,
                      (const half_t*)a.z, (half_t*)a.y, cp, ch.ht);
   return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
 }
 
 }  // namespace
+
+#ifndef FC_ACT
+#error "compiled once per activation id: -DFC_ACT=<0..ACT_COUNT-1>"
+#endif
+
+// the halo route with activation FC_ACT
+int FC_CAT(launch_halo_act_, FC_ACT)(const Geometry& g, const RunArgs& a) {
+  Choice ch;
+  if (!choose(g.cp, ch)) return FUSEDCONV_ERR_ROUTE;
+  if (ch.ht.vec_x)
+    return ch.bn == 256 ? launch_t<128, 256, 1, true>(g, ch, a) : launch_t<128, 128, 2, true>(g, ch, a);
+  return ch.bn == 256 ? launch_t<128, 256, 1, false>(g, ch, a) : launch_t<128, 128, 2, false>(g, ch, a);
+}
+
+#if FC_ACT == 0
+FC_ACT_DECLS(launch_halo_act_)
 
 bool igemm_halo_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32_t& tile_w,
                      size_t& workspace) {
@@ -619,11 +635,9 @@ int prepare_igemm_halo(const Geometry& g, const Plan&, const RunArgs& a) {
 }
 
 int launch_igemm_halo(const Geometry& g, const Plan&, const RunArgs& a) {
-  Choice ch;
-  if (!choose(g.cp, ch)) return FUSEDCONV_ERR_ROUTE;
-  if (ch.ht.vec_x)
-    return ch.bn == 256 ? launch_t<128, 256, 1, true>(g, ch, a) : launch_t<128, 128, 2, true>(g, ch, a);
-  return ch.bn == 256 ? launch_t<128, 256, 1, false>(g, ch, a) : launch_t<128, 128, 2, false>(g, ch, a);
+  static const ActLaunchFn table[ACT_COUNT] = FC_ACT_TABLE(launch_halo_act_);
+  return table[g.cp.act](g, a);
 }
+#endif
 
 }  // namespace fc

@@ -5,7 +5,8 @@
 // derive implicitTiledWorthIt, tiledSplitK*, preferImplicitSplitK); what
 // carries over is the shape of the decision: grouped convs with one input
 // channel per group go to a direct halo kernel, dense channel counts go to an
-// implicit GEMM, and a GEMM whose output grid cannot fill the device splits
+// implicit GEMM (few input channels: the row-chunk SMALLC form), and a GEMM
+// whose output grid cannot fill the device splits
 // its reduction (split-K: raw fp32 partials, then one reduce that applies
 // bias, residual and activation once).  Thresholds here are for 256 CUs.
 #include <stdio.h>
@@ -79,7 +80,7 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
     err = "split_k must be >= 0";
     return FUSEDCONV_ERR_ROUTE;
   }
-  if (route < FUSEDCONV_ROUTE_AUTO || route > FUSEDCONV_ROUTE_IGEMM_HALO) {
+  if (route < FUSEDCONV_ROUTE_AUTO || route > FUSEDCONV_ROUTE_SMALLC) {
     err = "unknown route";
     return FUSEDCONV_ERR_ROUTE;
   }
@@ -93,6 +94,7 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
     if (split_req > 1) route = FUSEDCONV_ROUTE_IGEMM;
     else if (cp.Cg == 1 && depthwise_fits(cp, th, tw)) route = FUSEDCONV_ROUTE_DEPTHWISE;
     else if (igemm_halo_fits(cp, g.dtype, th, tw, halo_ws)) route = FUSEDCONV_ROUTE_IGEMM_HALO;
+    else if (smallc_fits(cp, g.dtype, th, tw, halo_ws)) route = FUSEDCONV_ROUTE_SMALLC;
     else if (cp.K >= 8 && cp.Mg >= 8 && igemm_grid_ok(cp, 1)) route = FUSEDCONV_ROUTE_IGEMM;
     else route = FUSEDCONV_ROUTE_DIRECT;
   }
@@ -131,6 +133,18 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
       p.tile_w = tw;
       p.workspace = halo_ws;
       snprintf(p.name, sizeof(p.name), "igemm_halo_f16_t%dx%d", th, tw);
+      return FUSEDCONV_OK;
+    case FUSEDCONV_ROUTE_SMALLC:
+      if (!smallc_fits(cp, g.dtype, th, tw, halo_ws)) {
+        err = "SMALLC needs fp16, 1 or 2 spatial dims, dilation 1 along the last axis, "
+              "C/group < 16 and C/group * KH * ceil(KW/8) <= 24";
+        return FUSEDCONV_ERR_ROUTE;
+      }
+      p.route = route;
+      p.tile_h = th;
+      p.tile_w = tw;
+      p.workspace = halo_ws;
+      snprintf(p.name, sizeof(p.name), "smallc_f16_t%dx%d", th, tw);
       return FUSEDCONV_OK;
     default:
       err = "unknown route";

@@ -55,14 +55,20 @@ typedef enum fusedconv_dtype {
  *              (C/group == 1), 1 or 2 spatial dims, LDS halo tiles.
  *   IGEMM_HALO implicit GEMM on MFMA, fp16 only, whose input tile is one
  *              channel-last halo box per 32 input channels; needs
- *              C/group >= 32 and at most 64 kernel taps.
+ *              C/group >= 16 and at most 64 kernel taps.
+ *   SMALLC     implicit GEMM on MFMA, fp16 only, for few input channels per
+ *              group (stems, patch embeddings): reduction rows of 8
+ *              consecutive kernel columns read from a channel-planar input
+ *              box; needs 1 or 2 spatial dims, dilation 1 along the last
+ *              axis, C/group < 16 and C/group * KH * ceil(KW/8) <= 24.
  */
 typedef enum fusedconv_route {
   FUSEDCONV_ROUTE_AUTO = 0,
   FUSEDCONV_ROUTE_DIRECT = 1,
   FUSEDCONV_ROUTE_IGEMM = 2,
   FUSEDCONV_ROUTE_DEPTHWISE = 3,
-  FUSEDCONV_ROUTE_IGEMM_HALO = 4
+  FUSEDCONV_ROUTE_IGEMM_HALO = 4,
+  FUSEDCONV_ROUTE_SMALLC = 5
 } fusedconv_route;
 
 /* Shape of one tensor.  present = 0 means the (optional) input is absent. */
@@ -181,7 +187,8 @@ int fusedconv_run(const fusedconv_handle* h, const void* x, const void* w, const
  * Weight preparation, for callers whose W stays the same across many runs
  * (inference): fusedconv_prepare_weights enqueues only the route's weight
  * preparation (for IGEMM_HALO a repack of W into the tap-major layout held in
- * the workspace; a no-op for the other routes), and fusedconv_run_ex with
+ * the workspace, for SMALLC a repack into rows of 8 kernel columns; a no-op
+ * for the other routes), and fusedconv_run_ex with
  * FUSEDCONV_RUN_WEIGHTS_PREPARED then skips that step and reads the prepared
  * weights from the workspace.  The caller guarantees that the workspace holds
  * the prepared form of the same W, made with the same handle; otherwise the

@@ -70,9 +70,12 @@ def test_workload_shapes_and_routes():
     for name, wl in WORKLOADS.items():
         h = B.Handle(wl["dtype"], wl["x"], wl["w"], wl["b"], wl["z"], **wl["attrs"])
         assert h.y_shape == wl["y"], name
-        assert h.route in ("direct", "igemm", "depthwise", "igemm_halo"), name
+        assert h.route in ("direct", "igemm", "depthwise", "igemm_halo", "smallc"), name
         if wl["attrs"].get("group", 1) == wl["x"][1]:
             assert h.route == "depthwise", name
+    stem = WORKLOADS["vision_stem_7x7s4_f16"]
+    h = B.Handle("f16", stem["x"], stem["w"], stem["b"], stem["z"], **stem["attrs"])
+    assert h.route == "smallc" and h.workspace_bytes == 128 * 24 * 8 * 2
 
 
 def test_readme_example():
@@ -172,6 +175,24 @@ def test_null_arguments():
     assert lib.fusedconv_run(hd._h, 16, 16, None, None, 16, None, 0, None) == -1  # bias missing
     assert lib.fusedconv_run(hd._h, 16, 16, 8, None, 16, None, 0, None) == -15    # misaligned
     lib.fusedconv_destroy(None)
+
+
+def test_smallc_route_limits():
+    h = _h([1, 3, 64, 64], [32, 3, 7, 7], strides=[4, 4], pads=[3, 3, 3, 3], dtype="f16",
+           route="smallc")
+    assert h.route == "smallc"
+    refused = [
+        dict(x=[1, 3, 64, 64], w=[32, 3, 3, 3], dilations=[1, 2], dtype="f16"),  # dilated columns
+        dict(x=[1, 3, 64, 64], w=[32, 3, 3, 3], dtype="f32"),                    # fp32
+        dict(x=[1, 16, 64, 64], w=[32, 16, 3, 3], dtype="f16"),                  # C/group = 16
+        dict(x=[1, 4, 64, 64], w=[32, 4, 7, 7], dtype="f16"),                    # 28 rows > 24
+        dict(x=[1, 3, 8, 64, 64], w=[32, 3, 3, 3, 3], dtype="f16"),              # 3-D
+    ]
+    for c in refused:
+        c = dict(c)
+        with pytest.raises(B.FusedConvError) as e:
+            _h(c.pop("x"), c.pop("w"), route="smallc", **c)
+        assert e.value.status == "FUSEDCONV_ERR_ROUTE"
 
 
 def test_forced_routes_and_split_plan():

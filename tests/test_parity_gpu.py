@@ -220,6 +220,36 @@ def test_halo_route(ci):
         check(got, ref, "f16", f"halo case {ci}")
 
 
+SMALLC_CASES = [
+    # (x, w, attrs) for the few-input-channel route (fp16)
+    ([2, 3, 64, 64], [32, 3, 7, 7], dict(strides=[4, 4], pads=[3, 3, 3, 3])),  # stem, aligned
+    ([2, 3, 63, 80], [64, 3, 3, 3], dict(strides=[2, 2], pads=[1, 1, 1, 1])),  # stride 2
+    ([2, 4, 20, 30], [40, 4, 5, 5], dict(pads=[2, 2, 2, 2])),                  # stride 1
+    ([1, 2, 16, 40], [16, 2, 3, 11], dict(pads=[1, 5, 1, 5])),                 # 2 chunks per row
+    ([2, 3, 300], [24, 3, 9], dict(auto_pad="SAME_UPPER")),                    # 1-D
+    ([2, 8, 20, 20], [32, 4, 3, 3], dict(group=2, pads=[1, 1, 1, 1])),         # groups
+    ([1, 3, 30, 30], [16, 3, 3, 3], dict(dilations=[2, 1])),                   # dilated rows
+    ([1, 3, 32, 32], [200, 3, 3, 3], dict(pads=[1, 1, 1, 1])),                 # 2 m blocks
+    ([2, 3, 27, 27], [16, 3, 3, 3], dict(strides=[2, 2])),                     # OW % 4 != 0
+]
+
+
+@pytest.mark.parametrize("ci", range(len(SMALLC_CASES)))
+def test_smallc_route(ci):
+    xs, ws, attrs = SMALLC_CASES[ci]
+    h = B.Handle("f16", xs, ws, None, None, route="smallc", **attrs)
+    for k, (bias, resid) in enumerate([(True, True), (False, False), (True, False)]):
+        act, params = ACTS[(3 * ci + 5 * k) % len(ACTS)]
+        x, w, b, z = random_tensors([9300, ci, k], "f16", xs, ws, [ws[0]] if bias else None,
+                                    h.y_shape if resid else None, dist="normal",
+                                    w_std=1.0 / np.sqrt(np.prod(ws[1:])))
+        a = dict(attrs, activation=act, activation_params=f32params(params))
+        log(f"CASE smallc {ci} x={xs} w={ws} {a} bias={bias} z={resid}")
+        got = run_gpu(x, w, b, z, route="smallc", **a)
+        ref = oracle.fusedconv(x, w, b, z, **a)
+        check(got, ref, "f16", f"smallc case {ci}")
+
+
 # Grids of 1024 work units (4 blocks per CU), XCD-remapped block order, full
 # output compared; the second shape's tiles run partly past the output (12 of
 # 16 rows).
@@ -308,9 +338,9 @@ def test_deterministic_and_inplace_residual(route):
     assert torch.equal(y3, y1)
 
 
-@pytest.mark.parametrize("route", ["igemm_halo", "igemm", "depthwise"])
+@pytest.mark.parametrize("route", ["igemm_halo", "igemm", "depthwise", "smallc"])
 def test_prepared_weights_match_plain_run(route):
-    C = 64 if route != "depthwise" else 16
+    C = {"depthwise": 16, "smallc": 3}.get(route, 64)
     M, grp = (C, C) if route == "depthwise" else (96, 1)
     xs, ws = [2, C, 16, 16], [M, C // grp, 3, 3]
     x, w, b, z = random_tensors([8100], "f16", xs, ws, [M], None, dist="normal", w_std=0.05)
