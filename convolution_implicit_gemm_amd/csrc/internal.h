@@ -85,6 +85,9 @@ static_assert(ACT_COUNT == 15, "FC_ACT_DECLS / FC_ACT_TABLE list every activatio
 // Depthwise planning helper (kernels_depthwise.hip knows its LDS budget).
 bool depthwise_fits(const ConvParams& cp, int32_t& tile_h, int32_t& tile_w);
 bool depthwise_fast(const ConvParams& cp, int32_t dtype);
+// Toeplitz-MFMA depthwise kernel (kernels_dwmfma.hip): fits / launch.
+bool depthwise_mfma_fits(const ConvParams& cp, int32_t dtype);
+int launch_depthwise_mfma(const Geometry& g, const RunArgs& a);
 bool igemm_halo_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32_t& tile_w,
                      size_t& workspace);
 bool smallc_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32_t& tile_w,

@@ -443,6 +443,7 @@ bool depthwise_fits(const ConvParams& cp, int32_t& tile_h, int32_t& tile_w) {
 }
 
 int launch_depthwise(const Geometry& g, const Plan& p, const RunArgs& a) {
+  if (p.tile == 2) return launch_depthwise_mfma(g, a);
   DwFast f;
   if (p.tile == 1 && g.dtype == FUSEDCONV_F16 && dw_fast_plan(g.cp, f)) {
     static const ActLaunchFn table[ACT_COUNT] = FC_ACT_TABLE(launch_dwfast_act_);

@@ -114,7 +114,10 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
       p.route = route;
       p.tile_h = th;
       p.tile_w = tw;
-      if (depthwise_fast(cp, g.dtype)) {
+      if (depthwise_mfma_fits(cp, g.dtype)) {
+        p.tile = 2;  // banded-matrix MFMA kernel
+        snprintf(p.name, sizeof(p.name), "depthwise_mfma_f16_k%dx%d", cp.KH, cp.KW);
+      } else if (depthwise_fast(cp, g.dtype)) {
         p.tile = 1;  // register-window dot2 kernel
         snprintf(p.name, sizeof(p.name), "depthwise_dot2_f16_k%dx%d", cp.KH, cp.KW);
       } else {

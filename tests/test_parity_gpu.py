@@ -154,8 +154,8 @@ def test_depthwise_route(dtype):
 
 DW_FAST_CASES = [
     # (n, C, mult, H, W, k, dilation, auto_pad / pads) for the fp16 dot2 depthwise kernel
-    (2, 5, 1, 56, 56, 7, 1, "SAME_UPPER"),
-    (1, 3, 1, 56, 56, 7, 2, "SAME_UPPER"),
+    (2, 5, 1, 56, 58, 7, 1, "SAME_UPPER"),     # W % 8 != 0: not the MFMA kernel
+    (1, 3, 1, 56, 50, 7, 2, "SAME_UPPER"),
     (2, 4, 2, 17, 23, 5, 1, "SAME_LOWER"),
     (1, 6, 1, 31, 9, 3, 3, "VALID"),
     (3, 2, 1, 13, 61, 7, 1, [3, 1, 2, 0]),
@@ -183,6 +183,76 @@ def test_depthwise_fast_path(ci):
         got = run_gpu(x, w, b, z, route="depthwise", **a)
         ref = oracle.fusedconv(x, w, b, z, **a)
         check(got, ref, "f16", f"dw fast case {ci}")
+
+
+DWM_CASES = [
+    # (n, C, mult, H, W, (kh, kw), (dh, dw), auto_pad / pads) for the banded-MFMA kernel
+    (2, 5, 1, 56, 56, (7, 7), (1, 1), "SAME_UPPER"),
+    (1, 3, 1, 56, 56, (7, 7), (2, 2), "SAME_UPPER"),
+    (2, 4, 2, 16, 24, (5, 5), (1, 1), "SAME_LOWER"),      # channel multiplier 2
+    (1, 6, 1, 31, 40, (3, 3), (2, 1), [2, 4, 3, 6]),     # row dilation 2 only, OW = 48
+    (3, 2, 1, 13, 64, (7, 3), (1, 2), [3, 2, 3, 2]),     # KH != KW, column dilation 2
+    (1, 2, 1, 20, 32, (3, 17), (1, 1), "SAME_UPPER"),    # widest band: 16 + 16 columns
+    (2, 3, 1, 18, 16, (5, 9), (1, 2), "SAME_UPPER"),     # dw * (KW-1) = 16
+    (1, 4, 1, 8, 8, (3, 3), (1, 1), "SAME_LOWER"),       # one tile column
+    (2, 3, 1, 61, 48, (7, 7), (1, 1), [0, 11, 0, 3]),    # large left pad, OH = 55
+]
+
+
+@pytest.mark.parametrize("ci", range(len(DWM_CASES)))
+def test_depthwise_mfma_path(ci):
+    n, C, mult, H, W, k, d, pad = DWM_CASES[ci]
+    attrs = dict(group=C, dilations=list(d))
+    if isinstance(pad, list):
+        attrs["pads"] = pad
+    else:
+        attrs["auto_pad"] = pad
+    xs, ws = [n, C, H, W], [C * mult, 1] + list(k)
+    h = B.Handle("f16", xs, ws, None, None, route="depthwise", **attrs)
+    assert h.kernel_name.startswith("depthwise_mfma"), h.kernel_name
+    for kk, (bias, resid) in enumerate([(True, False), (False, True), (True, True)]):
+        act, params = ACTS[(3 * ci + 5 * kk) % len(ACTS)]
+        x, w, b, z = random_tensors([9300, ci, kk], "f16", xs, ws, [C * mult] if bias else None,
+                                    h.y_shape if resid else None, dist="normal")
+        a = dict(attrs, activation=act, activation_params=f32params(params))
+        log(f"CASE dw mfma {ci} x={xs} w={ws} {a}")
+        got = run_gpu(x, w, b, z, route="depthwise", **a)
+        ref = oracle.fusedconv(x, w, b, z, **a)
+        check(got, ref, "f16", f"dw mfma case {ci}")
+
+
+def test_depthwise_mfma_many_images_per_block():
+    # enough planes that a block walks several images, with a ragged last run
+    xs, ws = [7, 2048, 8, 16], [2048, 1, 3, 3]
+    attrs = dict(group=2048, pads=[1, 1, 1, 1], activation="Relu")
+    h = B.Handle("f16", xs, ws, None, None, route="depthwise", **attrs)
+    assert h.kernel_name.startswith("depthwise_mfma"), h.kernel_name
+    x, w, b, z = random_tensors([9310], "f16", xs, ws, [2048], h.y_shape, dist="normal")
+    log(f"CASE dw mfma many images x={xs}")
+    got = run_gpu(x, w, b, z, route="depthwise", **attrs)
+    ref = oracle.fusedconv(x, w, b, z, **attrs)
+    check(got, ref, "f16", "dw mfma many images")
+
+
+def test_depthwise_mfma_nonfinite_input_stays_local():
+    # an infinite input reaches only the outputs whose window holds it; its
+    # plane takes the exact loop, the other planes the matrix cores
+    xs, ws = [2, 3, 24, 32], [3, 1, 5, 5]
+    attrs = dict(group=3, auto_pad="SAME_UPPER")
+    h = B.Handle("f16", xs, ws, None, None, route="depthwise", **attrs)
+    assert h.kernel_name.startswith("depthwise_mfma"), h.kernel_name
+    x, w, b, _ = random_tensors([9320], "f16", xs, ws, [3], None, dist="normal")
+    x[0, 1, 10, 20] = np.inf
+    x[1, 2, 3, 4] = -np.inf
+    log("CASE dw mfma non-finite")
+    got = run_gpu(x, w, b, None, route="depthwise", **attrs).astype(np.float64)
+    ref = oracle.fusedconv(x, w, b, None, **attrs)
+    fin = np.isfinite(ref)
+    assert (~fin).sum() == 2 * 25
+    assert np.array_equal(np.isfinite(got), fin)
+    assert np.array_equal(got[~fin], ref[~fin])
+    scale = np.max(np.abs(ref[fin]))
+    assert np.max(np.abs(got[fin] - ref[fin])) / scale <= TAU["f16"]
 
 
 HALO_CASES = [
