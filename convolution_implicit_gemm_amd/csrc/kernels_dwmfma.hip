@@ -18,8 +18,10 @@
 // (fp32 accumulation seeded by the bias).
 //
 // Layout on gfx950:
-//   * a block owns one output channel m and a run of images; the Toeplitz
-//     A fragments (KH x 8 halves per lane) are built once per block;
+//   * block b owns channel b % M and walks every k-th image, so the k*M
+//     blocks read one compact window of memory at a time; its Toeplitz
+//     fragments (KH x 8 halves per lane, from an LDS table of zero-padded
+//     kernel rows) are built once;
 //   * each input plane is copied into LDS with 16-byte loads and stores at
 //     a column shift S that puts input column 0 on an 8-column boundary, so
 //     every B fragment is one aligned ds_read_b128; the zero border (the
@@ -31,12 +33,13 @@
 //     item need only 4 + dh*(KH-1) distinct B fragments (10 instead of 28
 //     for a 7x7 kernel), which keeps LDS traffic below the HBM time;
 //   * the fp32 results go through an LDS stage so bias, residual Z and the
-//     activation run on contiguous 8-element runs with 16-byte global loads
+//     activation run on contiguous 4-element runs with 8-byte global loads
 //     and stores; the input is the A operand and the Toeplitz matrix the B
 //     operand, so a lane's accumulators are 4 rows of one output column and
 //     16 lanes write 16 consecutive stage words;
-//   * each lane holds the next plane's input in registers while the
-//     matrix cores work on the current one.
+//   * each lane holds the input of the next 3 planes in registers (3 blocks
+//     per CU: ~57 KB in flight per CU for 56 x 56 planes), enough to cover
+//     HBM latency at full bandwidth.
 // A zero entry of T times an infinite or NaN input would spread that value
 // to outputs whose window does not contain it, so a plane holding any
 // non-finite input is computed again, after the block's other planes, by an
@@ -50,13 +53,21 @@ namespace fc {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxChunks = 2;          // 16-byte chunks per lane and plane (x, and z / y)
+constexpr int kMaxChunks = 2;          // 16-byte input chunks per lane and plane
+constexpr int kMaxQuads = 4;           // 4-output quads of y per lane and plane
 constexpr int kMaxLds = 64 * 1024;     // bytes per block
 constexpr int kRG = 4;                 // interleaved row tiles per work item
+constexpr int kPre = 3;                // planes whose input is in flight per block
+
+// Word 3 of a raw buffer resource on gfx9-class GPUs: 32-bit data format,
+// untyped access (offsets past num_records read zero and drop writes).
+constexpr int kBufferWord3 = 0x00020000;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef unsigned uint4v __attribute__((ext_vector_type(4)));
+typedef unsigned uint2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
 struct DwMfma {
   int TV, TW;        // work items per plane: 64-row groups, 16-column blocks
@@ -69,9 +80,9 @@ struct DwMfma {
   int toff;          // byte offset of the zero-padded kernel rows (2 x KH x 48 halves)
   int foff;          // byte offset of the non-finite plane flags (one word)
   int lds;           // bytes per block
-  int nb;            // images per block
-  int nchunk;        // ceil(n / nb)
-  int xch, ych;      // 16-byte chunks per plane of x and of y
+  int k;             // images per step: block b owns channel b % M and images b / M + i k
+  int steps;         // steps per block, ceil(n / k) <= 32
+  int xch, yq;       // 16-byte chunks of x, 4-output quads of y per plane
 };
 
 bool dwm_try(const ConvParams& cp, DwMfma& f) {
@@ -99,17 +110,21 @@ bool dwm_try(const ConvParams& cp, DwMfma& f) {
   if (lds > kMaxLds) return false;
   f.lds = (int)lds;
   f.xch = (int)(cp.in_sz / 8);
-  f.ych = (int)(cp.out_sz / 8);
-  if (f.xch > kMaxChunks * kThreads || f.ych > kMaxChunks * kThreads) return false;
-  // about 20 blocks per CU over 256 CUs: short tails, few per-block set-ups
-  const int64_t planes = cp.n * cp.M;
-  int64_t nb = planes / (256 * 20);
-  if (nb < 1) nb = 1;
-  if (nb > 32) nb = 32;  // one bit per image in the block's non-finite mask
-  if (nb > cp.n) nb = cp.n;
-  f.nb = (int)nb;
-  f.nchunk = (int)((cp.n + nb - 1) / nb);
-  if ((int64_t)f.nchunk * cp.M >= ((int64_t)1 << 31)) return false;
+  f.yq = (int)(cp.out_sz / 4);
+  if (f.xch > kMaxChunks * kThreads || f.yq > kMaxQuads * kThreads) return false;
+  // Block b owns channel b % M (Toeplitz fragments built once) and walks
+  // images b / M, b / M + k, ...: at step i the k*M blocks read the planes
+  // i*k*M .. (i+1)*k*M - 1 of the image-major order, one compact window of
+  // memory (a grid-wide stream rather than k*M scattered ones).  About 3
+  // blocks per CU (k*M ~ 768); at most 32 steps (one bit each in the block's
+  // non-finite mask).
+  int64_t k = (768 + cp.M / 2) / cp.M;
+  if (k < 1) k = 1;
+  if (k < (cp.n + 31) / 32) k = (cp.n + 31) / 32;
+  if (k > cp.n) k = cp.n;
+  if (k * cp.M >= ((int64_t)1 << 31)) return false;
+  f.k = (int)k;
+  f.steps = (int)((cp.n + k - 1) / k);
   return true;
 }
 
@@ -143,7 +158,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 template <int KH, int DH, int ACT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void dwm_kernel(const half_t* __restrict__ x, const half_t* __restrict__ w,
                 const half_t* __restrict__ bias, const half_t* z, half_t* y, ConvParams cp,
                 DwMfma f) {
@@ -152,14 +167,17 @@ void dwm_kernel(const half_t* __restrict__ x, const half_t* __restrict__ w,
   float* stage = (float*)(smem + f.in_halves * 2);
   half_t* wl = (half_t*)(smem + f.woff);
   half_t* trow = (half_t*)(smem + f.toff);
-  unsigned* flags = (unsigned*)(smem + f.foff);  // bit n - n0: plane n has a non-finite input
+  unsigned* flags = (unsigned*)(smem + f.foff);  // bit i: step i's plane has a non-finite input
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = (int)(blockIdx.x % (unsigned)cp.M);
-  const int64_t n0 = (int64_t)(blockIdx.x / (unsigned)cp.M) * f.nb;
-  const int64_t n1 = n0 + f.nb < cp.n ? n0 + f.nb : cp.n;
-  const int ic = m / cp.Mg;
-  const int cw8 = cp.W / 8, ow8 = cp.OW / 8;
+  const int n0 = (int)(blockIdx.x / (unsigned)cp.M);
+  const int nimg = (int)cp.n;
+  // steps of this block: images n0 + i k for i < nst (steps past nst repeat
+  // the last image: same results to the same place)
+  const int nst = (nimg - n0 + f.k - 1) / f.k;
+  const int nlast = n0 + (nst - 1) * f.k;
+  const int cw8 = cp.W / 8, ow4 = cp.OW / 4;
 
   // Chunk c of a plane: input row c / cw8, columns 8 (c % cw8) .. +7.  Lanes
   // past the last chunk repeat it (same data to the same place), so loads,
@@ -167,38 +185,46 @@ void dwm_kernel(const half_t* __restrict__ x, const half_t* __restrict__ w,
   // operation makes the compiler drain every outstanding load at the join.
   int xoff[kMaxChunks], xdst[kMaxChunks];
 #pragma unroll
-  for (int k = 0; k < kMaxChunks; ++k) {
-    const int c = tid + k * kThreads;
+  for (int kk = 0; kk < kMaxChunks; ++kk) {
+    const int c = tid + kk * kThreads;
     const int cc = c < f.xch ? c : f.xch - 1;
     const int row = cc / cw8, col = cc - row * cw8;
-    xoff[k] = cc * 8;
-    xdst[k] = in_row(row + cp.ph, f.pitch) + col * 8 + cp.pw + f.S;
+    xoff[kk] = cc * 8;
+    xdst[kk] = in_row(row + cp.ph, f.pitch) + col * 8 + cp.pw + f.S;
   }
-  // y chunk c (8 outputs: row c / ow8, columns 8 (c % ow8) ..): its element
-  // offset in the plane and its stage offset
-  int yoff[kMaxChunks], soff[kMaxChunks];
+  // y quad c (4 outputs: row c / ow4, columns 4 (c % ow4) ..): its element
+  // offset in the plane and its stage offset (consecutive lanes read
+  // consecutive 16-byte stage words: no bank conflicts)
+  int yoff[kMaxQuads], soff[kMaxQuads];
 #pragma unroll
-  for (int k = 0; k < kMaxChunks; ++k) {
-    const int c = tid + k * kThreads;
-    const int cc = c < f.ych ? c : f.ych - 1;
-    const int row = cc / ow8;
-    yoff[k] = cc * 8;
-    soff[k] = stage_row(row, f.P) + (cc - row * ow8) * 8 + 8;
+  for (int kk = 0; kk < kMaxQuads; ++kk) {
+    const int c = tid + kk * kThreads;
+    const int cc = c < f.yq ? c : f.yq - 1;
+    const int row = cc / ow4;
+    yoff[kk] = cc * 4;
+    soff[kk] = stage_row(row, f.P) + (cc - row * ow4) * 4 + 8;
   }
-  const half_t* xbase = x + ic * cp.in_sz;
-  const int64_t xstride = (int64_t)cp.C * cp.in_sz;  // one image
-  auto load_plane = [&](int64_t n, uint4v (&r)[kMaxChunks]) __attribute__((always_inline)) {
-    const half_t* xp = xbase + (n < n1 ? n : n1 - 1) * xstride;
+  // image n: input plane n * C + m / Mg, output plane n * M + m
+  const half_t* xm = x + (int64_t)(m / cp.Mg) * cp.in_sz;
+  const int64_t xstride = (int64_t)cp.C * cp.in_sz;
+  auto image = [&](int i) { return i < nst ? n0 + i * f.k : nlast; };
+  auto load_x = [&](int n, uint4v (&r)[kMaxChunks]) __attribute__((always_inline)) {
+    const half_t* xp = xm + (int64_t)n * xstride;
 #pragma unroll
-    for (int k = 0; k < kMaxChunks; ++k) r[k] = *(const uint4v*)(xp + xoff[k]);
+    for (int kk = 0; kk < kMaxChunks; ++kk) r[kk] = *(const uint4v*)(xp + xoff[kk]);
   };
-  uint4v xr[kMaxChunks];
-  load_plane(n0, xr);
+  // The input of the next kPre planes is in flight in registers (rotating
+  // sets), which keeps enough bytes in flight per CU to cover HBM latency.
+  uint4v xs[kPre][kMaxChunks];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) load_x(image(i), xs[i]);
 
-  // zero the input plane (its border stays zero); weights
+  // zero the input plane once: its border stays zero for every plane;
+  // weights and bias of channel m
   for (int i = tid; i < f.in_halves / 8; i += kThreads) ((uint4v*)xin)[i] = uint4v{0, 0, 0, 0};
   for (int i = tid; i < KH * cp.KW; i += kThreads) wl[i] = w[(int64_t)m * KH * cp.KW + i];
   if (tid == 0) *flags = 0;
+  const float bv = cp.has_bias ? to_f32(bias[m]) : 0.0f;
   lds_barrier();
   // zero-padded kernel rows: trow[c][kh][i] = T entry for offset d = i + c - 16
   // (k - j = d), i.e. w[kh][d / dw] when d = dw*kw, 0 <= kw < KW, else 0;
@@ -215,58 +241,48 @@ void dwm_kernel(const half_t* __restrict__ x, const half_t* __restrict__ w,
     trow[idx] = v;
   }
   lds_barrier();
-  const float bv = cp.has_bias ? to_f32(bias[m]) : 0.0f;
 
-  // Residual of a plane (without one, chunk 0 of x as a stand-in).
-  auto load_z = [&](int64_t ybase, uint4v (&zr)[kMaxChunks]) __attribute__((always_inline)) {
-    const half_t* zp = cp.has_z ? z + ybase : x;
+  // Residual of a plane.  A buffer load whose range is empty when there is no
+  // residual: the hardware returns zeros without touching memory, with no
+  // branch around the load.
+  auto load_z = [&](int64_t ybase, uint2v (&zr)[kMaxQuads]) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t zb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(cp.has_z ? z + ybase : x), (short)0, cp.has_z ? (int)(cp.out_sz * 2) : 0,
+        kBufferWord3);
 #pragma unroll
-    for (int k = 0; k < kMaxChunks; ++k) zr[k] = *(const uint4v*)(zp + (cp.has_z ? yoff[k] : 0));
+    for (int kk = 0; kk < kMaxQuads; ++kk)
+      zr[kk] = __builtin_bit_cast(uint2v, __builtin_amdgcn_raw_buffer_load_b64(zb, yoff[kk] * 2, 0, 0));
   };
-  // bias, residual, activation over the staged plane; 16-byte stores of y
-  // (the plane is contiguous: chunk c covers y[8c .. 8c+7])
-  auto store_plane = [&](int64_t ybase, const uint4v (&zr)[kMaxChunks])
+  // bias, residual, activation over the staged plane; 8-byte stores of y
+  // (the plane is contiguous: quad c covers y[4c .. 4c+3])
+  auto store_plane = [&](int64_t ybase, const uint2v (&zr)[kMaxQuads])
       __attribute__((always_inline)) {
     lds_barrier();
     half_t* yp = y + ybase;
 #pragma unroll
-    for (int k = 0; k < kMaxChunks; ++k) {
-      {
-        const float4v s0 = *(const float4v*)(stage + soff[k]);
-        const float4v s1 = *(const float4v*)(stage + soff[k] + 4);
-        const half8 zh = __builtin_bit_cast(half8, zr[k]);
-        act4_t v0, v1;
+    for (int kk = 0; kk < kMaxQuads; ++kk) {
+      const float4v s0 = *(const float4v*)(stage + soff[kk]);
+      const half4 zh = __builtin_bit_cast(half4, zr[kk]);
+      act4_t v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v0[i] = s0[i] + bv;
-          v1[i] = s1[i] + bv;
-        }
-        if (cp.has_z) {
+      for (int i = 0; i < 4; ++i) v[i] = s0[i] + bv;
+      if (cp.has_z) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v0[i] += (float)zh[i];
-            v1[i] += (float)zh[4 + i];
-          }
-        }
-        v0 = act4<ACT>(v0, cp.alpha, cp.beta);
-        v1 = act4<ACT>(v1, cp.alpha, cp.beta);
-        half8 out;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          out[i] = (half_t)v0[i];
-          out[4 + i] = (half_t)v1[i];
-        }
-        *(half8*)(yp + yoff[k]) = out;
+        for (int i = 0; i < 4; ++i) v[i] += (float)zh[i];
       }
+      v = act4<ACT>(v, cp.alpha, cp.beta);
+      half4 out;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[i] = (half_t)v[i];
+      *(half4*)(yp + yoff[kk]) = out;
     }
   };
 
   {
-    // Toeplitz fragments (the B operand): lane holds T_kh[j][8q .. 8q+7],
-    // j = lane % 16 the output column of the tile
     const int j16 = lane & 15, q = lane >> 4;
-    // (d = 8q + e - j, e = 0..7: the 8 halves from i = 16 + 8q - j of the
-    // zero-padded row)
+    // Toeplitz fragments (the B operand): lane holds T_kh[j][8q .. 8q+7],
+    // j = lane % 16 the output column of the tile: the 8 halves from
+    // i = 16 + 8q - j of the zero-padded row
     half8 tfrag[KH];
     {
       const int i0 = 16 + 8 * q - j16;
@@ -285,25 +301,29 @@ void dwm_kernel(const half_t* __restrict__ x, const half_t* __restrict__ w,
     const int bstep = f.pitch * 2;                              // bytes per input row
     const int nitem = f.TV * f.TW;
 
-    for (int64_t n = n0; n < n1; ++n) {
+    // step i: image image(i); xr holds its input and receives the input
+    // kPre steps ahead
+    auto step = [&](int i, uint4v (&xr)[kMaxChunks]) __attribute__((always_inline)) {
       // this plane's input into LDS; flag non-finite values
       unsigned bad = 0;
 #pragma unroll
-      for (int k = 0; k < kMaxChunks; ++k) {
-        *(uint4v*)(xin + xdst[k]) = xr[k];
-        bad |= nonfinite_bits(xr[k]);
+      for (int kk = 0; kk < kMaxChunks; ++kk) {
+        *(uint4v*)(xin + xdst[kk]) = xr[kk];
+        bad |= nonfinite_bits(xr[kk]);
       }
-      if (__builtin_amdgcn_ballot_w64(bad != 0) != 0) atomicOr(flags, 1u << (unsigned)(n - n0));
-      const int64_t ybase = ((int64_t)n * cp.M + m) * cp.out_sz;
-      uint4v zr[kMaxChunks];
+      const int ir = i < nst ? i : nst - 1;
+      if (__builtin_amdgcn_ballot_w64(bad != 0) != 0) atomicOr(flags, 1u << (unsigned)ir);
+      const int64_t ybase = ((int64_t)image(i) * cp.M + m) * cp.out_sz;
+      uint2v zr[kMaxQuads];
       load_z(ybase, zr);
       lds_barrier();
-      // the next plane's input into the registers just written out
-      load_plane(n + 1, xr);
+      // the input kPre steps ahead into the registers just written out
+      load_x(image(i + kPre), xr);
       // the plane into the fp32 stage
       for (int it = wave; it < nitem; it += 4) {
         const int v = it / f.TW, t = it - v * f.TW;
-        const unsigned char* bp = (const unsigned char*)(xin + in_row(64 * v, f.pitch) + 16 * t) + brow;
+        const unsigned char* bp =
+            (const unsigned char*)(xin + in_row(64 * v, f.pitch) + 16 * t) + brow;
         float4v acc[kRG];
 #pragma unroll
         for (int p = 0; p < kRG; ++p) acc[p] = float4v{0, 0, 0, 0};
@@ -316,7 +336,7 @@ void dwm_kernel(const half_t* __restrict__ x, const half_t* __restrict__ w,
             if (p >= 0 && p < kRG)
               acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, tfrag[kh], acc[p], 0, 0, 0);
           }
-          // keep only a few B fragments in flight (registers for occupancy)
+          // keep only a few fragments in flight (registers for the prefetch)
           if (s % 3 == 2) __builtin_amdgcn_sched_barrier(0);
         }
         // lane holds D[4q + i][j16] of tile p: output row 64v + 4 (4q + i) + p,
@@ -327,9 +347,14 @@ void dwm_kernel(const half_t* __restrict__ x, const half_t* __restrict__ w,
 #pragma unroll
         for (int p = 0; p < kRG; ++p)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sq[(4 * i + p) * f.P] = acc[p][i];
+          for (int e = 0; e < 4; ++e) sq[(4 * e + p) * f.P] = acc[p][e];
       }
       store_plane(ybase, zr);
+    };
+
+    for (int i = 0; i < nst; i += kPre) {
+#pragma unroll
+      for (int u = 0; u < kPre; ++u) step(i + u, xs[u]);
     }
   }
 
@@ -340,13 +365,12 @@ void dwm_kernel(const half_t* __restrict__ x, const half_t* __restrict__ w,
   while (badmask != 0) {
     const int i = __builtin_ctz(badmask);
     badmask &= badmask - 1;
-    const int64_t n = n0 + i;
+    const int n = image(i);
     lds_barrier();  // every lane is done with the stage and the input
-    {
-      const half_t* xp = xbase + n * xstride;
+    uint4v xr[kMaxChunks];
+    load_x(n, xr);
 #pragma unroll
-      for (int k = 0; k < kMaxChunks; ++k) *(uint4v*)(xin + xdst[k]) = *(const uint4v*)(xp + xoff[k]);
-    }
+    for (int kk = 0; kk < kMaxChunks; ++kk) *(uint4v*)(xin + xdst[kk]) = xr[kk];
     lds_barrier();
     for (int idx = tid; idx < cp.OH * cp.OW; idx += kThreads) {
       const int oh = idx / cp.OW, ow = idx - oh * cp.OW;
@@ -358,7 +382,7 @@ void dwm_kernel(const half_t* __restrict__ x, const half_t* __restrict__ w,
       stage[stage_row(oh, f.P) + ow + 8] = sum;
     }
     const int64_t ybase = ((int64_t)n * cp.M + m) * cp.out_sz;
-    uint4v zr[kMaxChunks];
+    uint2v zr[kMaxQuads];
     load_z(ybase, zr);
     store_plane(ybase, zr);
   }
@@ -367,8 +391,7 @@ void dwm_kernel(const half_t* __restrict__ x, const half_t* __restrict__ w,
 template <int KH, int DH>
 int launch_kh(const Geometry& g, const DwMfma& f, const RunArgs& a) {
   const ConvParams& cp = g.cp;
-  const int64_t blocks = (int64_t)f.nchunk * cp.M;
-  hipLaunchKernelGGL((dwm_kernel<KH, DH, FC_ACT>), dim3((unsigned)blocks), dim3(kThreads),
+  hipLaunchKernelGGL((dwm_kernel<KH, DH, FC_ACT>), dim3((unsigned)(f.k * cp.M)), dim3(kThreads),
                      (size_t)f.lds, (hipStream_t)a.stream, (const half_t*)a.x, (const half_t*)a.w,
                      (const half_t*)a.bias, (const half_t*)a.z, (half_t*)a.y, cp, f);
   return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;

@@ -255,6 +255,29 @@ def test_depthwise_mfma_nonfinite_input_stays_local():
     assert np.max(np.abs(got[fin] - ref[fin])) / scale <= TAU["f16"]
 
 
+def test_depthwise_mfma_nonfinite_across_channels():
+    # runs of several planes per block that cross channels: the exact loop
+    # must take each flagged plane's own weights and bias
+    xs, ws = [2, 1500, 8, 16], [1500, 1, 3, 3]
+    attrs = dict(group=1500, pads=[1, 1, 1, 1], activation="Tanh")
+    h = B.Handle("f16", xs, ws, None, None, route="depthwise", **attrs)
+    assert h.kernel_name.startswith("depthwise_mfma"), h.kernel_name
+    x, w, b, z = random_tensors([9330], "f16", xs, ws, [1500], h.y_shape, dist="normal")
+    x[0, 1, 4, 5] = np.inf      # planes (channel 1, image 0) and (channel 0, image 1)
+    x[1, 0, 0, 0] = np.nan      # share the first block's run
+    x[1, 1499, 7, 15] = -np.inf
+    log("CASE dw mfma non-finite across channels")
+    got = run_gpu(x, w, b, z, route="depthwise", **attrs).astype(np.float64)
+    ref = oracle.fusedconv(x, w, b, z, **attrs)
+    fin = np.isfinite(ref)
+    assert (~fin).sum() > 0
+    assert np.array_equal(np.isfinite(got), fin)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[np.isinf(ref)], ref[np.isinf(ref)])
+    scale = np.max(np.abs(ref[fin]))
+    assert np.max(np.abs(got[fin] - ref[fin])) / scale <= TAU["f16"]
+
+
 HALO_CASES = [
     # (x, w, attrs) for the channel-last halo route (fp16)
     ([2, 64, 16, 16], [96, 64, 3, 3], dict(pads=[1, 1, 1, 1])),            # M tail (96 < 128)
