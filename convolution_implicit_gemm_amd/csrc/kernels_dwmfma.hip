@@ -48,6 +48,7 @@
 
 #include "epilogue.h"
 #include "internal.h"
+#include "sync.h"
 
 namespace fc {
 namespace {
@@ -146,16 +147,6 @@ __device__ __forceinline__ int in_row(int r, int pitch) { return r * pitch + 8 *
 // rows 16 apart, written by the same instruction, land 16 banks apart);
 // column ow of the output sits at stage column ow + 8.
 __device__ __forceinline__ int stage_row(int r, int P) { return r * P + 16 * (r >> 4); }
-
-// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
-// every outstanding global load and store of the wave (a workgroup-scope
-// release covers global memory), which would drain the next plane's input
-// loads and this plane's stores at each barrier.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 template <int KH, int DH, int ACT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))

@@ -33,6 +33,7 @@
 
 #include "epilogue.h"
 #include "internal.h"
+#include "sync.h"
 
 namespace fc {
 namespace {
@@ -47,6 +48,11 @@ constexpr size_t kMaxLds = 150 * 1024;  // one block per CU
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef unsigned uint2v __attribute__((ext_vector_type(2)));
+
+// Word 3 of a raw buffer resource on gfx9-class GPUs: 32-bit data format,
+// untyped access (offsets past num_records read zero and drop writes).
+constexpr int kBufferWord3 = 0x00020000;
 
 struct HaloTile {
   int TD, TH, TW;          // output tile
@@ -294,7 +300,7 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
   const bool vec_y = (cp.OW & 3) == 0;
   const int taps = cp.taps, ncb = ht.ncb, nsteps = ncb * taps;
 
-  __syncthreads();  // zero fill done before any box or table write
+  lds_barrier();  // zero fill done before any box or table write
   if (tid < cp.taps) {
     const int kw = tid % cp.KW, kh = (tid / cp.KW) % cp.KH, kd = tid / (cp.KW * cp.KH);
     const int ad = kd * cp.dd, ah = kh * cp.dh, aw = kw * cp.dw;
@@ -310,7 +316,7 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
   half8 wa[TM], wb[TM];
 #pragma unroll
   for (int j = 0; j < TM; ++j) wa[j] = *(const half8*)(wg + wl + j * 16 * kCB);
-  __syncthreads();
+  lds_barrier();
 
   // Step s = (cb, t) reads Wp tile t * ncb + cb; wnext is the Wp offset of
   // step s + 1.  After the last step of a channel block the next block's box
@@ -340,7 +346,7 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
       t = 0;                                                                              \
       if (cb + 1 < ncb) {                                                                 \
         store_box((cb + 1) & 1, cb + 1);                                                  \
-        __syncthreads();                                                                  \
+        lds_barrier();                                                                    \
         if (cb + 2 < ncb) prefetch_box(cb + 2);                                           \
       }                                                                                   \
       ++cb;                                                                               \
@@ -361,13 +367,71 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
   // staged as 16 rows of consecutive pixels; a rolled loop then applies the
   // activation and stores Y, consecutive lanes writing consecutive 8-byte
   // pieces of a row.
-  __syncthreads();
+  lds_barrier();
   constexpr int PW = BN / 2;              // pixels per wave
   constexpr int RP = PW + 4;              // fp32 row pitch (padded)
   constexpr int GPR = PW / 4;             // 4-pixel groups per row
   constexpr int ITER = 16 * GPR / 64;     // groups per lane per pass
   float* stage = (float*)lds + wave * 16 * RP;
   const int mw0 = m0 + wmi * (BM / 2);    // first channel of this wave
+  static_assert(64 % GPR == 0, "a lane's 4-pixel group must not change between passes");
+  if (vec_y && (int64_t)cp.out_sz * (BM / 2) * 2 < ((int64_t)1 << 31)) {
+    // OW % 4 == 0: pass it of block j gives lane the 4 pixels p4 .. p4+3 of
+    // stage row it*RPI + rsub (channel mw0 + 16j + row) -- the same pixels
+    // in every pass, so their output offset is computed once.  Residual
+    // loads and stores are raw buffer operations: an invalid slot gets an
+    // offset past the buffer's range (reads zero, write dropped) and a
+    // missing residual is an empty range, so no branch surrounds a memory
+    // operation and every residual load is in flight before the first use.
+    constexpr int RPI = 64 / GPR;         // stage rows per pass
+    constexpr unsigned kOff = 0x80000000u;
+    const int p4 = (lane % GPR) * 4, rsub = lane / GPR;
+    const int pl = wpi * PW + p4;
+    const int tw = pl & (ht.TW - 1), th = (pl >> ht.ltw) & (ht.TH - 1), td = pl >> (ht.ltw + ht.lth);
+    const int od = od0 + td, oh = oh0 + th, ow = ow0 + tw;
+    const bool pok = od < cp.OD && oh < cp.OH && ow < cp.OW;
+    const int pix = (od * cp.OH + oh) * cp.OW + ow;
+    const int64_t wbase = (n * cp.M + (int64_t)g * cp.Mg + mw0) * cp.out_sz;
+    const __amdgpu_buffer_rsrc_t yb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(y + wbase), (short)0, 0x7fffffff, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t zb = __builtin_amdgcn_make_buffer_rsrc(
+        cp.has_z ? (void*)(z + wbase) : (void*)y, (short)0, cp.has_z ? 0x7fffffff : 0, kBufferWord3);
+    auto voff = [&](int j, int it) __attribute__((always_inline)) {
+      const int r = j * 16 + it * RPI + rsub;  // channel relative to mw0
+      return (pok && mw0 + r < cp.Mg) ? (unsigned)((r * (int)cp.out_sz + pix) * 2) : kOff;
+    };
+    uint2v zr[TM][ITER];
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int it = 0; it < ITER; ++it)
+        zr[j][it] = __builtin_bit_cast(uint2v, __builtin_amdgcn_raw_buffer_load_b64(zb, voff(j, it), 0, 0));
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+#pragma unroll
+      for (int i = 0; i < TP; ++i) *(float4v*)(stage + r16 * RP + i * 16 + q * 4) = acc[i][j];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) {
+        const float4v sv = *(const float4v*)(stage + (it * RPI + rsub) * RP + p4);
+        const half4 zh = __builtin_bit_cast(half4, zr[j][it]);
+        act4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = sv[e] + (float)zh[e];
+        v = act4<ACT>(v, cp.alpha, cp.beta);
+        half4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = (half_t)v[e];
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, out), yb, voff(j, it), 0, 0);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    return;
+  }
   // Z (when OW % 4 == 0, a lane's 4 pixels are all in or all out of the
   // image): every value this wave needs is requested before any is used, as
   // unconditional 8-byte loads (an invalid slot reads z[0..3] and is never

@@ -26,6 +26,7 @@
 
 #include "epilogue.h"
 #include "internal.h"
+#include "sync.h"
 
 namespace fc {
 namespace {
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(kThreads, 2) void smallc_kernel(const half_t* __res
   SUnit cu = decode_unit(u, cp, st);
   box_fill(cu, lds);
   load_weights(cu.g, cu.mb);
-  __syncthreads();
+  lds_barrier();
   for (int it = 0;; ++it) {
     const int un = u + gridDim.x;
     const bool has_next = un < nunits;
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(kThreads, 2) void smallc_kernel(const half_t* __res
     if (pf) box_store(nu, 0, nbuf);
     else box_fill(nu, nbuf);
     if (nu.g != cur_g || nu.mb != cur_mb) load_weights(nu.g, nu.mb);
-    __syncthreads();
+    lds_barrier();
     u = un;
     cu = nu;
   }
