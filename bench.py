@@ -132,20 +132,26 @@ class Runner:
                        weights_prepared=True)
 
     def time(self, steps, warmup):
+        """Wall time per step over exactly `steps` steps (synchronized on both
+        sides, no per-step events), then a second, instrumented pass of the
+        same steps: HIP events on the launch stream around the weight
+        preparation and around the convolution kernel."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
         stream = torch.cuda.current_stream()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
         for i in range(steps):
             ev[i][0].record(stream)
             self.step(i, ev[i][1])
             ev[i][2].record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         # the main kernel alone (between the middle and the last event)
         kern = [a.elapsed_time(b) * 1e-3 for _, a, b in ev]
         self.prep_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))

@@ -40,7 +40,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kCB = 32;               // channels per block = MFMA K
-constexpr int kLDC = kCB + 8;         // LDS row pitch in halves (80 bytes): conflict-free b128 reads
+// LDS row pitch (halves per box position): 48 (96-byte rows), or 40 when
+// two boxes of 48 do not fit.  An operand read is 16 rows at 16-byte column
+// offsets; measured on gfx950, such a ds_read_b128 pattern runs at the full
+// LDS rate when the row pitch is 16 bytes times 2 mod 4 (96, 160, ...) and
+// at half rate for 80 bytes.
+constexpr int kLDCFast = kCB + 16;
+constexpr int kLDCSmall = kCB + 8;
 constexpr int kMaxTaps = 64;
 constexpr size_t kLds2 = 80 * 1024;    // two blocks per CU
 constexpr size_t kMaxLds = 150 * 1024;  // one block per CU
@@ -68,14 +74,15 @@ struct HaloTile {
   int mgp;                 // Wp rows per (tap, channel block): M/group rounded up to BM
   int vec_x;               // W % 8 == 0: 16-byte input loads
   int ltw, lth;            // log2(TW), log2(TH)
+  int ldc;                 // LDS row pitch in halves (kLDCFast or kLDCSmall)
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Dynamic LDS: two input boxes, or the epilogue staging area (4 waves x 16
 // channels x (BN/2 + 4) fp32) if larger.
-size_t lds_bytes(int box_pos, int bn) {
-  const size_t boxes = (size_t)2 * box_pos * kLDC * 2;
+size_t lds_bytes(int box_pos, int bn, int ldc) {
+  const size_t boxes = (size_t)2 * box_pos * ldc * 2;
   const size_t stage = (size_t)4 * 16 * (bn / 2 + 4) * 4;
   return boxes > stage ? boxes : stage;
 }
@@ -93,20 +100,25 @@ __device__ __forceinline__ int phase_index(int a, int s, int n) {
 __global__ __launch_bounds__(kThreads) void repack_w_kernel(const half_t* __restrict__ w,
                                                             half_t* __restrict__ wp,
                                                             ConvParams cp, int ncb, int mgp) {
-  const int64_t total = (int64_t)cp.G * cp.taps * ncb * mgp * kCB;
-  const int64_t step = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += step) {
-    const int cc = (int)(i % kCB);
-    int64_t r = i / kCB;
-    const int m = (int)(r % mgp);
+  // one thread per 8-channel piece of a Wp row: 8 reads of W (a stride of
+  // `taps` apart, cached), one 16-byte store; 32-bit index arithmetic
+  const int total = cp.G * cp.taps * ncb * mgp * (kCB / 8);
+  for (int i = blockIdx.x * kThreads + threadIdx.x; i < total; i += gridDim.x * kThreads) {
+    const int c8 = i & (kCB / 8 - 1);
+    int r = i / (kCB / 8);
+    const int m = r % mgp;
     r /= mgp;
-    const int cb = (int)(r % ncb);
+    const int cb = r % ncb;
     r /= ncb;
-    const int t = (int)(r % cp.taps);
-    const int g = (int)(r / cp.taps);
-    const int c = cb * kCB + cc;
-    wp[i] = (c < cp.Cg && m < cp.Mg) ? w[((int64_t)(g * cp.Mg + m) * cp.Cg + c) * cp.taps + t]
-                                     : (half_t)0;
+    const int t = r % cp.taps;
+    const int g = r / cp.taps;
+    const int c0 = cb * kCB + c8 * 8;
+    const half_t* src = w + ((int64_t)(g * cp.Mg + m) * cp.Cg + c0) * cp.taps + t;
+    half8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      v[e] = (c0 + e < cp.Cg && m < cp.Mg) ? src[e * cp.taps] : (half_t)0;
+    *(half8*)(wp + (int64_t)i * 8) = v;
   }
 }
 
@@ -132,7 +144,8 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
   constexpr int TP = BN / 32;
   constexpr int TM = BM / 32;
   extern __shared__ __attribute__((aligned(16))) half_t lds[];
-  const int box = ht.box_pos * kLDC;  // halves per input box
+  const int ldc = ht.ldc;
+  const int box = ht.box_pos * ldc;  // halves per input box
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -178,7 +191,7 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
       if (iw + e >= w_lo && iw + e < w_hi) mask |= 1 << e;
     it.goff = (id * cp.H + ih) * cp.W + iw;
     it.ldst = ((phase_index(id - bd0, cp.sd, ht.ND) * ht.LH + phase_index(ih - bh0, cp.sh, ht.NH)) *
-               ht.LW) * kLDC + cq * 4;
+               ht.LW) * ldc + cq * 4;
     it.cm = ((iw - bw0 + 8) << 8) | mask;
     return it;
   };
@@ -231,7 +244,7 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
     for (int e = 0; e < 8; ++e) {
       if (!((cm >> e) & 1)) continue;
       const int col = phase_index(aw0 + e, cp.sw, ht.NW);
-      *(half4*)(xs + it.ldst + col * kLDC) = half4{u[0][e], u[1][e], u[2][e], u[3][e]};
+      *(half4*)(xs + it.ldst + col * ldc) = half4{u[0][e], u[1][e], u[2][e], u[3][e]};
     }
   };
   auto prefetch_box = [&](int cb) __attribute__((always_inline)) {
@@ -273,7 +286,7 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
 #pragma unroll
   for (int i = 0; i < TP; ++i) {
     const int pu = wpi * (BN / 2) + i * 16;
-    aoff[i] = ((pu >> ht.ltw) * ht.LW + (pu & (ht.TW - 1)) + r16) * kLDC + q * 8;
+    aoff[i] = ((pu >> ht.ltw) * ht.LW + (pu & (ht.TW - 1)) + r16) * ldc + q * 8;
   }
   // ---- LDS offset (halves) of each tap: along every axis the tap's box
   // offset k*dilation splits into stride phase (k*dil % s) and index
@@ -281,7 +294,7 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
   // padding (channels 32..39) of box row t of buffer 0, which neither the
   // box writes nor the MFMA operand reads touch.
   int* const tap_tab = (int*)lds;
-  constexpr int kTabStride = kLDC / 2;  // ints per LDS row; entry t at int t*20 + 16
+  const int tab_stride = ldc / 2;  // ints per LDS row; entry t at int t*tab_stride + 16
 
   // ---- accumulators start at the bias: lane column r16 is output channel
   // m0 + wmi*BM/2 + j*16 + r16
@@ -304,9 +317,9 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
   if (tid < cp.taps) {
     const int kw = tid % cp.KW, kh = (tid / cp.KW) % cp.KH, kd = tid / (cp.KW * cp.KH);
     const int ad = kd * cp.dd, ah = kh * cp.dh, aw = kw * cp.dw;
-    tap_tab[tid * kTabStride + 16] =
+    tap_tab[tid * tab_stride + 16] =
         ((((ad % cp.sd) * ht.ND + ad / cp.sd) * ht.LH + (ah % cp.sh) * ht.NH + ah / cp.sh) * ht.LW +
-         (aw % cp.sw) * ht.NW + aw / cp.sw) * kLDC;
+         (aw % cp.sw) * ht.NW + aw / cp.sw) * ldc;
   }
   prefetch_box(0);
   store_box(0, 0);
@@ -351,7 +364,7 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
       }                                                                                   \
       ++cb;                                                                               \
     }                                                                                     \
-    toff = tap_tab[t * kTabStride + 16];                                                  \
+    toff = tap_tab[t * tab_stride + 16];                                                  \
     ++s;                                                                                  \
     wnext += (t == taps - 1) ? wcb : wtap;                                                \
   }
@@ -568,7 +581,10 @@ bool make_tile(const ConvParams& cp, int bm, int bn, int tw, size_t max_lds, Hal
   ht.LW = cp.sw * ht.NW;
   const int64_t bpos = (int64_t)cp.sd * ht.ND * ht.LH * ht.LW;
   // (the tap table lives in the padding of the first kMaxTaps box rows)
-  if (bpos < kMaxTaps || bpos > (1 << 16) || lds_bytes((int)bpos, bn) > max_lds) return false;
+  if (bpos < kMaxTaps || bpos > (1 << 16)) return false;
+  if (lds_bytes((int)bpos, bn, kLDCFast) <= max_lds) ht.ldc = kLDCFast;
+  else if (lds_bytes((int)bpos, bn, kLDCSmall) <= max_lds) ht.ldc = kLDCSmall;
+  else return false;
   ht.box_pos = (int)bpos;
   ht.tiles_d = (int)cdiv(cp.OD, td);
   ht.tiles_h = (int)cdiv(cp.OH, th);
@@ -578,6 +594,7 @@ bool make_tile(const ConvParams& cp, int bm, int bn, int tw, size_t max_lds, Hal
   ht.mgp = (int)(cdiv(cp.Mg, bm) * bm);
   ht.nmb = (int)cdiv(cp.Mg, bm);
   if (ntile * ht.nmb * cp.G >= ((int64_t)1 << 31)) return false;
+  if ((int64_t)cp.G * cp.taps * ht.ncb * ht.mgp * (kCB / 8) >= ((int64_t)1 << 31)) return false;
   ht.ntile = (int)ntile;
   ht.remap = (ntile % 8) == 0;
   ht.vec_x = (cp.W % 8) == 0;
@@ -630,7 +647,7 @@ bool choose(const ConvParams& cp, Choice& ch) {
 }
 
 int launch_repack(const ConvParams& cp, const Choice& ch, const RunArgs& a) {
-  const int64_t total = (int64_t)cp.G * cp.taps * ch.ht.ncb * ch.ht.mgp * kCB;
+  const int64_t total = (int64_t)cp.G * cp.taps * ch.ht.ncb * ch.ht.mgp * (kCB / 8);
   int64_t rblocks = (total + kThreads - 1) / kThreads;
   if (rblocks > 4096) rblocks = 4096;
   hipLaunchKernelGGL(repack_w_kernel, dim3((unsigned)rblocks), dim3(kThreads), 0,
@@ -643,7 +660,7 @@ template <int BM, int BN, int PF, bool VEC>
 int launch_t(const Geometry& g, const Choice& ch, const RunArgs& a) {
   const ConvParams& cp = g.cp;
   hipStream_t st = (hipStream_t)a.stream;
-  const size_t lds = lds_bytes(ch.ht.box_pos, BN);
+  const size_t lds = lds_bytes(ch.ht.box_pos, BN, ch.ht.ldc);
   const void* kfn = (const void*)halo_kernel<BM, BN, PF, VEC, FC_ACT>;
   static bool attr_set = false;
   if (!attr_set) {
