@@ -349,6 +349,9 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
       const half_t* sn_ = wg + ((HAS_NEXT) ? wnext : 0);                                  \
       _Pragma("unroll") for (int j = 0; j < TM; ++j) WN[j] = *(const half8*)(sn_ + wl + j * 16 * kCB); \
     }                                                                                     \
+    /* keep the loads here, a full step ahead of their use (the scheduler */              \
+    /* would otherwise sink them below this step's MFMAs into WC's registers) */          \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
     const half_t* xs_ = lds + (cb & 1) * box + toff;                                      \
     half8 a_[TP];                                                                         \
     _Pragma("unroll") for (int i = 0; i < TP; ++i) a_[i] = *(const half8*)(xs_ + aoff[i]);   \
