@@ -341,6 +341,16 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
   int64_t wnext = (taps > 1) ? wtap : wcb;
   int cb = 0, t = 0, s = 0;
   int toff = 0;  // tap 0 is at offset 0
+  // Operand rows of pixel tiles 0..TP/2-1 are read one half-step early: a
+  // step reads its tiles TP/2..TP-1, runs the MFMAs of tiles 0..TP/2-1,
+  // stores the next channel block's box if this was the block's last tap,
+  // then reads the next step's tiles 0..TP/2-1 into the registers just freed
+  // and runs the rest.  The early read is unconditional (its buffer and tap
+  // are selected without a branch) so that it stays between the two halves.
+  constexpr int TH = TP / 2;
+  half8 a_[TP];
+#pragma unroll
+  for (int i = 0; i < TH; ++i) a_[i] = *(const half8*)(lds + aoff[i]);
 #define HALO_STEP(WC, WN, HAS_NEXT)                                                       \
   {                                                                                       \
     {                                                                                     \
@@ -352,22 +362,28 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
     /* keep the loads here, a full step ahead of their use (the scheduler */              \
     /* would otherwise sink them below this step's MFMAs into WC's registers) */          \
     __builtin_amdgcn_sched_barrier(0);                                                    \
-    const half_t* xs_ = lds + (cb & 1) * box + toff;                                      \
-    half8 a_[TP];                                                                         \
-    _Pragma("unroll") for (int i = 0; i < TP; ++i) a_[i] = *(const half8*)(xs_ + aoff[i]);   \
-    _Pragma("unroll") for (int i = 0; i < TP; ++i)                                        \
+    const half_t* xb_ = lds + (cb & 1) * box + toff;                                      \
+    _Pragma("unroll") for (int i = TH; i < TP; ++i) a_[i] = *(const half8*)(xb_ + aoff[i]); \
+    const bool last_ = t + 1 == taps;                                                     \
+    const int tn_ = last_ ? 0 : t + 1;                                                    \
+    const int toffn_ = tap_tab[tn_ * tab_stride + 16];                                    \
+    _Pragma("unroll") for (int i = 0; i < TH; ++i)                                        \
       _Pragma("unroll") for (int j = 0; j < TM; ++j)                                      \
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_[i], WC[j], acc[i][j], 0, 0, 0); \
-    if (++t == taps) {                                                                    \
-      t = 0;                                                                              \
-      if (cb + 1 < ncb) {                                                                 \
-        store_box((cb + 1) & 1, cb + 1);                                                  \
-        lds_barrier();                                                                    \
-        if (cb + 2 < ncb) prefetch_box(cb + 2);                                           \
-      }                                                                                   \
-      ++cb;                                                                               \
+    if (last_ && cb + 1 < ncb) {                                                          \
+      store_box((cb + 1) & 1, cb + 1);                                                    \
+      lds_barrier();                                                                      \
+      if (cb + 2 < ncb) prefetch_box(cb + 2);                                             \
     }                                                                                     \
-    toff = tap_tab[t * tab_stride + 16];                                                  \
+    const int cbn_ = cb + (last_ ? 1 : 0);                                                \
+    const half_t* xn_ = lds + (cbn_ & 1) * box + toffn_;                                  \
+    _Pragma("unroll") for (int i = 0; i < TH; ++i) a_[i] = *(const half8*)(xn_ + aoff[i]); \
+    _Pragma("unroll") for (int i = TH; i < TP; ++i)                                       \
+      _Pragma("unroll") for (int j = 0; j < TM; ++j)                                      \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_[i], WC[j], acc[i][j], 0, 0, 0); \
+    t = tn_;                                                                              \
+    cb = cbn_;                                                                            \
+    toff = toffn_;                                                                        \
     ++s;                                                                                  \
     wnext += (t == taps - 1) ? wcb : wtap;                                                \
   }
