@@ -88,8 +88,10 @@ bool depthwise_fast(const ConvParams& cp, int32_t dtype);
 // Toeplitz-MFMA depthwise kernel (kernels_dwmfma.hip): fits / launch.
 bool depthwise_mfma_fits(const ConvParams& cp, int32_t dtype);
 int launch_depthwise_mfma(const Geometry& g, const RunArgs& a);
+// Halo route (kernels_halo.hip): fits, with the output tile, the weight
+// workspace and (when block_m is given) the block's output channels.
 bool igemm_halo_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32_t& tile_w,
-                     size_t& workspace);
+                     size_t& workspace, int32_t* block_m = nullptr);
 bool smallc_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32_t& tile_w,
                  size_t& workspace);
 

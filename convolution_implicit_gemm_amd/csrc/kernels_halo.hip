@@ -79,11 +79,11 @@ struct HaloTile {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Dynamic LDS: two input boxes, or the epilogue staging area (4 waves x 16
+// Dynamic LDS: two input boxes, or the epilogue staging area (nw waves x 16
 // channels x (BN/2 + 4) fp32) if larger.
-size_t lds_bytes(int box_pos, int bn, int ldc) {
+size_t lds_bytes(int box_pos, int bn, int ldc, int nw) {
   const size_t boxes = (size_t)2 * box_pos * ldc * 2;
-  const size_t stage = (size_t)4 * 16 * (bn / 2 + 4) * 4;
+  const size_t stage = (size_t)nw * 16 * (bn / 2 + 4) * 4;
   return boxes > stage ? boxes : stage;
 }
 
@@ -129,20 +129,23 @@ struct Unit {
   int g, mb, od0, oh0, ow0;
 };
 
-// Block tile BN pixels x BM channels, 4 waves as 2 x 2, each owning
-// (BN/2) x (BM/2) = TP x TM MFMA blocks of 16x16; two blocks per CU.
+// Block tile BN pixels x BM channels, 2 x NWM waves, each owning
+// (BN/2) x (BM/NWM) = TP x TM MFMA blocks of 16x16.  NWM = 2: 4 waves, two
+// blocks per CU; NWM = 4: 8 waves sharing one input box, one block per CU
+// (two waves per SIMD of the same block, half the box loads per output).
 // PF: input-box loader items per thread kept in registers across a channel
 // block (each item = 4 channels x 8 columns of one box row, 16 registers);
-// items beyond PF * 256 are loaded and stored at the channel-block boundary.
+// items beyond PF * NT are loaded and stored at the channel-block boundary.
 // VEC: W % 8 == 0, so an item's 8 columns are one aligned 16-byte load.
-template <int BM, int BN, int PF, bool VEC, int ACT>
+template <int BM, int BN, int PF, bool VEC, int NWM, int ACT>
 __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
                                           const half_t* __restrict__ wp,
                                           const half_t* __restrict__ bias, const half_t* z,
                                           half_t* y, const ConvParams& cp, const HaloTile& ht,
                                           const Unit& u) {
+  constexpr int NT = 128 * NWM;  // threads
   constexpr int TP = BN / 32;
-  constexpr int TM = BM / 32;
+  constexpr int TM = BM / (16 * NWM);
   extern __shared__ __attribute__((aligned(16))) half_t lds[];
   const int ldc = ht.ldc;
   const int box = ht.box_pos * ldc;  // halves per input box
@@ -158,7 +161,7 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
   const int bd0 = od0 * cp.sd - cp.pd, bh0 = oh0 * cp.sh - cp.ph, bw0 = ow0 * cp.sw - cp.pw;
 
   // ---- zero both input boxes: positions outside the image stay zero
-  for (int i = tid; i < 2 * box / 8; i += kThreads) ((half8*)lds)[i] = half8{};
+  for (int i = tid; i < 2 * box / 8; i += NT) ((half8*)lds)[i] = half8{};
 
   // ---- input loader.  Item i = (row of the in-image part of the box,
   // aligned 8-column group, channel quad cq = i % 8): four 16-byte loads of
@@ -198,7 +201,7 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
   Item items[PF];
 #pragma unroll
   for (int k = 0; k < PF; ++k) {
-    const int i = tid + k * kThreads;
+    const int i = tid + k * NT;
     items[k].cm = -1;
     items[k].goff = items[k].ldst = 0;
     if (i < nitems) items[k] = decode(i);
@@ -256,12 +259,12 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
     half_t* xs = lds + buf * box;
 #pragma unroll
     for (int k = 0; k < PF; ++k) store_item(items[k], cb, xs, xreg[k]);
-    for (int i0 = PF * kThreads; i0 < nitems; i0 += PF * kThreads) {
+    for (int i0 = PF * NT; i0 < nitems; i0 += PF * NT) {
       Item more[PF];
       half8 v[PF][4];
 #pragma unroll
       for (int k = 0; k < PF; ++k) {
-        const int i = i0 + tid + k * kThreads;
+        const int i = i0 + tid + k * NT;
         more[k].cm = -1;
         more[k].goff = more[k].ldst = 0;
         if (i < nitems) more[k] = decode(i);
@@ -276,7 +279,7 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
   // fragment j of step (cb, t) = 16 rows x 64 bytes, each lane reads 16 bytes
   // at a 32-bit lane offset from the step's (uniform) tile address.
   const half_t* wg = wp + (int64_t)g * cp.taps * ht.ncb * ht.mgp * kCB;
-  const int wl = (m0 + wmi * (BM / 2) + r16) * kCB + q * 8;
+  const int wl = (m0 + wmi * (BM / NWM) + r16) * kCB + q * 8;
   const int64_t wstep = (int64_t)ht.mgp * kCB;  // halves per (tap, channel block) tile
 
   // ---- LDS offset (halves) of this lane's operand row (pixel) in pixel
@@ -297,10 +300,10 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
   const int tab_stride = ldc / 2;  // ints per LDS row; entry t at int t*tab_stride + 16
 
   // ---- accumulators start at the bias: lane column r16 is output channel
-  // m0 + wmi*BM/2 + j*16 + r16
+  // m0 + wmi*BM/NWM + j*16 + r16
   float4v acc[TP][TM];
   {
-    const int mw = m0 + wmi * (BM / 2) + r16;
+    const int mw = m0 + wmi * (BM / NWM) + r16;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       float bv = 0.0f;
@@ -405,9 +408,9 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
   constexpr int GPR = PW / 4;             // 4-pixel groups per row
   constexpr int ITER = 16 * GPR / 64;     // groups per lane per pass
   float* stage = (float*)lds + wave * 16 * RP;
-  const int mw0 = m0 + wmi * (BM / 2);    // first channel of this wave
+  const int mw0 = m0 + wmi * (BM / NWM);  // first channel of this wave
   static_assert(64 % GPR == 0, "a lane's 4-pixel group must not change between passes");
-  if (vec_y && (int64_t)cp.out_sz * (BM / 2) * 2 < ((int64_t)1 << 31)) {
+  if (vec_y && (int64_t)cp.out_sz * (BM / NWM) * 2 < ((int64_t)1 << 31)) {
     // OW % 4 == 0: pass it of block j gives lane the 4 pixels p4 .. p4+3 of
     // stage row it*RPI + rsub (channel mw0 + 16j + row) -- the same pixels
     // in every pass, so their output offset is computed once.  Residual
@@ -546,8 +549,8 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
 // Block -> work unit (group, tile, m block).  Blocks are dealt to the XCDs
 // round-robin; with remap the m blocks of a tile are 8 blocks apart, i.e.
 // back to back on the same XCD, so the second reads X from that XCD's L2.
-template <int BM, int BN, int PF, bool VEC, int ACT>
-__global__ __launch_bounds__(kThreads, 2) void halo_kernel(const half_t* __restrict__ x,
+template <int BM, int BN, int PF, bool VEC, int NWM, int ACT>
+__global__ __launch_bounds__(128 * NWM, NWM == 2 ? 2 : 1) void halo_kernel(const half_t* __restrict__ x,
                                                            const half_t* __restrict__ wp,
                                                            const half_t* __restrict__ bias,
                                                            const half_t* z, half_t* y,
@@ -574,18 +577,18 @@ __global__ __launch_bounds__(kThreads, 2) void halo_kernel(const half_t* __restr
   u.od0 = td_i * ht.TD;
   u.oh0 = th_i * ht.TH;
   u.ow0 = tw_i * ht.TW;
-  halo_tile<BM, BN, PF, VEC, ACT>(x, wp, bias, z, y, cp, ht, u);
+  halo_tile<BM, BN, PF, VEC, NWM, ACT>(x, wp, bias, z, y, cp, ht, u);
 }
 
 struct Choice {
-  int bm, bn;
+  int bm, bn, nwm;  // block tile BM x BN, waves 2 x nwm
   HaloTile ht;
 };
 
 int log2i(int v) { return 31 - __builtin_clz((unsigned)v); }
 
 // Fill the tile-dependent fields; false if the box does not fit.
-bool make_tile(const ConvParams& cp, int bm, int bn, int tw, size_t max_lds, HaloTile& ht) {
+bool make_tile(const ConvParams& cp, int bm, int bn, int tw, size_t max_lds, int nw, HaloTile& ht) {
   const int th = bn / tw, td = 1;
   ht.TD = td; ht.TH = th; ht.TW = tw;
   ht.ltw = log2i(tw);
@@ -601,8 +604,8 @@ bool make_tile(const ConvParams& cp, int bm, int bn, int tw, size_t max_lds, Hal
   const int64_t bpos = (int64_t)cp.sd * ht.ND * ht.LH * ht.LW;
   // (the tap table lives in the padding of the first kMaxTaps box rows)
   if (bpos < kMaxTaps || bpos > (1 << 16)) return false;
-  if (lds_bytes((int)bpos, bn, kLDCFast) <= max_lds) ht.ldc = kLDCFast;
-  else if (lds_bytes((int)bpos, bn, kLDCSmall) <= max_lds) ht.ldc = kLDCSmall;
+  if (lds_bytes((int)bpos, bn, kLDCFast, nw) <= max_lds) ht.ldc = kLDCFast;
+  else if (lds_bytes((int)bpos, bn, kLDCSmall, nw) <= max_lds) ht.ldc = kLDCSmall;
   else return false;
   ht.box_pos = (int)bpos;
   ht.tiles_d = (int)cdiv(cp.OD, td);
@@ -620,46 +623,61 @@ bool make_tile(const ConvParams& cp, int bm, int bn, int tw, size_t max_lds, Hal
   return true;
 }
 
-// Pick BN and the output tile (BM = 128); false if nothing fits.  Tiles whose
-// two boxes fit two blocks per CU are preferred; larger boxes (3-D, strided
-// 3x3) run one block per CU.
+// Pick the block tile and the output tile; false if nothing fits.  In order
+// of preference: 8 waves with BM = 256 (one block per CU, both channel halves
+// on one input box) when the group has more than 128 output channels, the
+// input box has at least twice as many positions as the tile has pixels
+// (strided convolutions, where reading X once instead of once per 128
+// channels saves the most: measured 15% on the 2x2 stride-2 downsample, no
+// gain on stride-1 3x3, which keeps two blocks per CU overlapping their
+// epilogues) and there are enough tiles to give every CU one; then BM = 128
+// with two blocks per CU; then BM = 128 with one (larger boxes: 3-D, strided
+// 3x3).
 bool choose(const ConvParams& cp, Choice& ch) {
   if (cp.Cg < 16 || cp.taps > kMaxTaps) return false;
-  const int bm = 128;  // BM = 256 with 4 waves spills registers
   const int tws[] = {16, 32, 64, 128, 256};
   int bn_first = 256;  // FUSEDCONV_HALO_BN=128 restricts the tile to 128 pixels (tuning)
   if (const char* e = getenv("FUSEDCONV_HALO_BN")) bn_first = atoi(e) == 128 ? 128 : 256;
-  for (size_t max_lds : {kLds2, kMaxLds})
-  for (int bn : {256, 128}) {
-    if (bn > bn_first) continue;
-    // tile widths (multiples of 16; tile = bn / tw rows) in order of padded
-    // output area, ties to the wider tile; the first that fits is taken
-    int order[5], no = 0;
-    double waste[5];
-    for (int c : tws) {
-      if (c > bn) break;
-      waste[no] = (double)cdiv(cp.OH, bn / c) * (bn / c) * cdiv(cp.OW, c) * c /
-                  ((double)cp.OH * cp.OW);
-      order[no] = c;
-      ++no;
-    }
-    for (int a = 0; a < no; ++a)
-      for (int b2 = a + 1; b2 < no; ++b2)
-        if (waste[b2] < waste[a] - 1e-9 ||
-            (waste[b2] < waste[a] + 1e-9 && order[b2] > order[a])) {
-          std::swap(waste[a], waste[b2]);
-          std::swap(order[a], order[b2]);
-        }
-    for (int oi = 0; oi < no; ++oi) {
-      HaloTile ht;
-      if (!make_tile(cp, bm, bn, order[oi], max_lds, ht)) continue;
-      // the tiles must not be mostly padding
-      if ((double)ht.tiles_d * ht.TD * ht.tiles_h * ht.TH * ht.tiles_w * ht.TW > 2.0 * cp.out_sz)
-        continue;
-      ch.bm = bm;
-      ch.bn = bn;
-      ch.ht = ht;
-      return true;
+  struct Cand {
+    int bm, nwm;
+    size_t max_lds;
+  };
+  const Cand cands[] = {{256, 4, kMaxLds}, {128, 2, kLds2}, {128, 2, kMaxLds}};
+  for (const Cand& c : cands) {
+    if (c.bm == 256 && cp.Mg <= 128) continue;
+    for (int bn : {256, 128}) {
+      if (bn > bn_first) continue;
+      // tile widths (multiples of 16; tile = bn / tw rows) in order of padded
+      // output area, ties to the wider tile; the first that fits is taken
+      int order[5], no = 0;
+      double waste[5];
+      for (int w : tws) {
+        if (w > bn) break;
+        waste[no] = (double)cdiv(cp.OH, bn / w) * (bn / w) * cdiv(cp.OW, w) * w /
+                    ((double)cp.OH * cp.OW);
+        order[no] = w;
+        ++no;
+      }
+      for (int a = 0; a < no; ++a)
+        for (int b2 = a + 1; b2 < no; ++b2)
+          if (waste[b2] < waste[a] - 1e-9 ||
+              (waste[b2] < waste[a] + 1e-9 && order[b2] > order[a])) {
+            std::swap(waste[a], waste[b2]);
+            std::swap(order[a], order[b2]);
+          }
+      for (int oi = 0; oi < no; ++oi) {
+        HaloTile ht;
+        if (!make_tile(cp, c.bm, bn, order[oi], c.max_lds, 2 * c.nwm, ht)) continue;
+        // the tiles must not be mostly padding
+        if ((double)ht.tiles_d * ht.TD * ht.tiles_h * ht.TH * ht.tiles_w * ht.TW > 2.0 * cp.out_sz)
+          continue;
+        if (c.bm == 256 && ((int64_t)ht.ntile * cp.G < 256 || ht.box_pos < 2 * bn)) continue;
+        ch.bm = c.bm;
+        ch.bn = bn;
+        ch.nwm = c.nwm;
+        ch.ht = ht;
+        return true;
+      }
     }
   }
   return false;
@@ -675,12 +693,12 @@ int launch_repack(const ConvParams& cp, const Choice& ch, const RunArgs& a) {
   return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
 }
 
-template <int BM, int BN, int PF, bool VEC>
+template <int BM, int BN, int PF, bool VEC, int NWM>
 int launch_t(const Geometry& g, const Choice& ch, const RunArgs& a) {
   const ConvParams& cp = g.cp;
   hipStream_t st = (hipStream_t)a.stream;
-  const size_t lds = lds_bytes(ch.ht.box_pos, BN, ch.ht.ldc);
-  const void* kfn = (const void*)halo_kernel<BM, BN, PF, VEC, FC_ACT>;
+  const size_t lds = lds_bytes(ch.ht.box_pos, BN, ch.ht.ldc, 2 * NWM);
+  const void* kfn = (const void*)halo_kernel<BM, BN, PF, VEC, NWM, FC_ACT>;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) !=
@@ -693,7 +711,7 @@ int launch_t(const Geometry& g, const Choice& ch, const RunArgs& a) {
     if (rc != FUSEDCONV_OK) return rc;
   }
   const unsigned blocks = (unsigned)((int64_t)ch.ht.ntile * ch.ht.nmb * cp.G);
-  hipLaunchKernelGGL((halo_kernel<BM, BN, PF, VEC, FC_ACT>), dim3(blocks), dim3(kThreads), lds, st,
+  hipLaunchKernelGGL((halo_kernel<BM, BN, PF, VEC, NWM, FC_ACT>), dim3(blocks), dim3(128 * NWM), lds, st,
                      (const half_t*)a.x, (const half_t*)a.ws, (const half_t*)a.bias,
                      (const half_t*)a.z, (half_t*)a.y, cp, ch.ht);
   return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
@@ -709,21 +727,27 @@ int launch_t(const Geometry& g, const Choice& ch, const RunArgs& a) {
 int FC_CAT(launch_halo_act_, FC_ACT)(const Geometry& g, const RunArgs& a) {
   Choice ch;
   if (!choose(g.cp, ch)) return FUSEDCONV_ERR_ROUTE;
-  if (ch.ht.vec_x)
-    return ch.bn == 256 ? launch_t<128, 256, 1, true>(g, ch, a) : launch_t<128, 128, 2, true>(g, ch, a);
-  return ch.bn == 256 ? launch_t<128, 256, 1, false>(g, ch, a) : launch_t<128, 128, 2, false>(g, ch, a);
+  if (ch.ht.vec_x) {
+    if (ch.bm == 256)
+      return ch.bn == 256 ? launch_t<256, 256, 1, true, 4>(g, ch, a) : launch_t<256, 128, 1, true, 4>(g, ch, a);
+    return ch.bn == 256 ? launch_t<128, 256, 1, true, 2>(g, ch, a) : launch_t<128, 128, 2, true, 2>(g, ch, a);
+  }
+  if (ch.bm == 256)
+    return ch.bn == 256 ? launch_t<256, 256, 1, false, 4>(g, ch, a) : launch_t<256, 128, 1, false, 4>(g, ch, a);
+  return ch.bn == 256 ? launch_t<128, 256, 1, false, 2>(g, ch, a) : launch_t<128, 128, 2, false, 2>(g, ch, a);
 }
 
 #if FC_ACT == 0
 FC_ACT_DECLS(launch_halo_act_)
 
 bool igemm_halo_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32_t& tile_w,
-                     size_t& workspace) {
+                     size_t& workspace, int32_t* block_m) {
   if (dtype != FUSEDCONV_F16) return false;
   Choice ch;
   if (!choose(cp, ch)) return false;
   tile_h = ch.ht.TH;
   tile_w = ch.ht.TW;
+  if (block_m) *block_m = ch.bm;
   workspace = (size_t)cp.G * cp.taps * ch.ht.ncb * ch.ht.mgp * kCB * sizeof(half_t);
   return true;
 }

@@ -90,6 +90,7 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
   }
   int32_t th = 0, tw = 0;
   size_t halo_ws = 0;
+  int32_t bm = 0;  // halo route: output channels per block
   if (route == FUSEDCONV_ROUTE_AUTO) {
     if (split_req > 1) route = FUSEDCONV_ROUTE_IGEMM;
     else if (cp.Cg == 1 && depthwise_fits(cp, th, tw)) route = FUSEDCONV_ROUTE_DEPTHWISE;
@@ -126,7 +127,7 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
       }
       return FUSEDCONV_OK;
     case FUSEDCONV_ROUTE_IGEMM_HALO:
-      if (!igemm_halo_fits(cp, g.dtype, th, tw, halo_ws)) {
+      if (!igemm_halo_fits(cp, g.dtype, th, tw, halo_ws, &bm)) {
         err = "IGEMM_HALO needs fp16, C/group >= 32, at most 64 taps and a halo box that fits "
               "in LDS";
         return FUSEDCONV_ERR_ROUTE;
@@ -135,7 +136,9 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
       p.tile_h = th;
       p.tile_w = tw;
       p.workspace = halo_ws;
-      snprintf(p.name, sizeof(p.name), "igemm_halo_f16_t%dx%d", th, tw);
+      // blocks of 256 output channels (8 waves) are named by it
+      if (bm == 256) snprintf(p.name, sizeof(p.name), "igemm_halo_f16_m256_t%dx%d", th, tw);
+      else snprintf(p.name, sizeof(p.name), "igemm_halo_f16_t%dx%d", th, tw);
       return FUSEDCONV_OK;
     case FUSEDCONV_ROUTE_SMALLC:
       if (!smallc_fits(cp, g.dtype, th, tw, halo_ws)) {

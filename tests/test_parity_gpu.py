@@ -365,6 +365,33 @@ def test_halo_large_grid(ci):
     check(got, ref, "f16", f"halo large grid case {ci}")
 
 
+# Blocks of 256 output channels (8 waves on one input box, one block per CU):
+# more than 128 output channels per group, an input box at least twice the
+# tile (strided) and at least 256 tiles.  Full output compared.
+WIDE_CASES = [
+    ([64, 32, 32, 64], [256, 32, 2, 2], dict(strides=[2, 2])),              # BM = 256 exactly
+    ([64, 48, 32, 64], [200, 48, 2, 2], dict(strides=[2, 2])),              # M and channel tails
+    ([32, 32, 64, 64], [256, 32, 3, 3], dict(strides=[2, 2], pads=[1] * 4)),  # stride 2 3x3
+    ([64, 32, 24, 72], [256, 32, 2, 2], dict(strides=[2, 2])),              # tiles past the output
+    ([64, 64, 32, 64], [384, 32, 2, 2], dict(group=2, strides=[2, 2])),     # two groups
+    ([64, 32, 32, 60], [160, 32, 2, 2], dict(strides=[2, 2])),              # W % 8 != 0
+]
+
+
+@pytest.mark.parametrize("ci", range(len(WIDE_CASES)))
+def test_halo_wide_blocks(ci):
+    xs, ws, attrs = WIDE_CASES[ci]
+    h = B.Handle("f16", xs, ws, [ws[0]], None, route="igemm_halo", **attrs)
+    assert h.kernel_name.startswith("igemm_halo_f16_m256_"), h.kernel_name
+    x, w, b, z = random_tensors([9250, ci], "f16", xs, ws, [ws[0]], h.y_shape, dist="normal",
+                                w_std=1.0 / np.sqrt(np.prod(ws[1:])))
+    a = dict(attrs, activation="QuickGelu", activation_params=f32params([1.702]))
+    log(f"CASE halo wide {ci} x={xs} w={ws} {a}")
+    got = run_gpu(x, w, b, z, route="igemm_halo", **a)
+    ref = oracle.fusedconv(x, w, b, z, **a)
+    check(got, ref, "f16", f"halo wide case {ci}")
+
+
 @pytest.mark.parametrize("route", ["direct", "igemm", "depthwise"])
 def test_edge_shapes(route):
     cases = [
