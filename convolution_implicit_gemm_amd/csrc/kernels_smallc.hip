@@ -263,15 +263,12 @@ __global__ __launch_bounds__(kThreads, 2) void smallc_kernel(const half_t* __res
       float4v acc[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) acc[mt] = float4v{bv[mt], bv[mt], bv[mt], bv[mt]};
-#pragma unroll
-      for (int kb = 0; kb < kMaxKB; ++kb) {
-        if (kb >= st.KB) break;
+      auto read_a = [&](int kb) __attribute__((always_inline)) {
         const int o = roff[kb] + pix;
-        half8 a;
         if constexpr (A4) {
           const uint2v lo = *(const uint2v*)(buf + o);
           const uint2v hi = *(const uint2v*)(buf + o + 4);
-          a = __builtin_bit_cast(half8, (__attribute__((ext_vector_type(4))) unsigned){lo[0], lo[1], hi[0], hi[1]});
+          return __builtin_bit_cast(half8, (__attribute__((ext_vector_type(4))) unsigned){lo[0], lo[1], hi[0], hi[1]});
         } else {
           const unsigned* d = (const unsigned*)buf + (o >> 1);
           const unsigned sh = (o & 1) * 16;
@@ -281,11 +278,30 @@ __global__ __launch_bounds__(kThreads, 2) void smallc_kernel(const half_t* __res
           __attribute__((ext_vector_type(4))) unsigned uu;
 #pragma unroll
           for (int k = 0; k < 4; ++k) uu[k] = __builtin_amdgcn_alignbit(w5[k + 1], w5[k], sh);
-          a = __builtin_bit_cast(half8, uu);
+          return __builtin_bit_cast(half8, uu);
         }
+      };
+      if (st.KB == kMaxKB) {
+        // every reduction block used: all operands are read before the first
+        // product, so the tile waits for LDS once, not once per block
+        half8 af[kMaxKB];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, wf[mt][kb], acc[mt], 0, 0, 0);
+        for (int kb = 0; kb < kMaxKB; ++kb) af[kb] = read_a(kb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < kMaxKB; ++kb)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[kb], wf[mt][kb], acc[mt], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < kMaxKB; ++kb) {
+          if (kb >= st.KB) break;
+          const half8 a = read_a(kb);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, wf[mt][kb], acc[mt], 0, 0, 0);
+        }
       }
       // epilogue: lane holds pixels wpi*128 + pt*16 + 4q .. +3 (4 consecutive
       // columns of one tile row) of channel m0 + wmi*64 + mt*16 + r16
