@@ -56,13 +56,11 @@ __device__ __forceinline__ float act_t(float v, float a, float b) {
   if constexpr (A == ACT_QUICKGELU) return v * __builtin_amdgcn_rcpf(1.0f + __expf(-a * v));
   if constexpr (A == ACT_ELU) return v > 0.0f ? v : a * expm1f(v);
   if constexpr (A == ACT_GELU) {
-    if (a == 0.0f) {
-      // 0.5 v (1 + erf(v / sqrt 2)); for v < 0, 1 + erf = erfc(|v| / sqrt 2)
-      const float c = erfc_as(fabsf(v) * 0.70710678118654752f);
-      return 0.5f * v * (v < 0.0f ? c : 2.0f - c);
-    }
-    // nonzero "approximate" flag: tanh form
-    return 0.5f * v * (1.0f + tanh_fast(0.79788456080286536f * (v + 0.044715f * v * v * v)));
+    // 0.5 v (1 + erf(v / sqrt 2)); for v < 0, 1 + erf = erfc(|v| / sqrt 2).
+    // A nonzero "approximate" flag never reaches here: the resolver sends it
+    // to FastGelu, the same tanh form.
+    const float c = erfc_as(fabsf(v) * 0.70710678118654752f);
+    return 0.5f * v * (v < 0.0f ? c : 2.0f - c);
   }
   if constexpr (A == ACT_FASTGELU)
     return 0.5f * v * (1.0f + tanh_fast(0.79788456080286536f * (v + 0.044715f * v * v * v)));

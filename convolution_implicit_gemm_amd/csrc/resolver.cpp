@@ -170,6 +170,13 @@ int resolve(const fusedconv_desc& d, Geometry& g, std::string& err) {
   else if (act == ACT_ELU || act == ACT_THRESHOLDEDRELU) alpha = 1.0f;
   if (np >= 2) beta = d.activation_params[1];
   else if (act == ACT_HARDSIGMOID) beta = 0.5f;
+  // Gelu with a nonzero approximate flag is the tanh form, which is FastGelu's
+  // formula exactly; routing it there keeps Gelu's kernels free of a per-output
+  // test of the flag
+  if (act == ACT_GELU && alpha != 0.0f) {
+    act = ACT_FASTGELU;
+    alpha = 0.0f;
+  }
 
   // residual: exactly Y's shape (derive zOk)
   if (d.z.present) {
