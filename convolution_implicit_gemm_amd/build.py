@@ -20,7 +20,7 @@ SOURCES = ["resolver.cpp", "planner.cpp", "capi.cpp", "kernels_direct.hip", "ker
 # Kernels specialised per activation: compiled once per activation id
 # (-DFC_ACT=k, k = 0 .. ACT_COUNT-1); unit 0 also holds the route entry points.
 ACT_SOURCES = ["kernels_depthwise.hip", "kernels_dwmfma.hip", "kernels_halo.hip",
-               "kernels_smallc.hip"]
+               "kernels_smallc.hip", "kernels_pointwise.hip"]
 ACT_COUNT = 15
 ARCH = "gfx950"
 # Packed fp32 ops stay off (the compiler is not allowed to form v_pk_*_f32).

@@ -156,6 +156,7 @@ int fusedconv_run_ex(const fusedconv_handle* h, const void* x, const void* w, co
     case FUSEDCONV_ROUTE_DEPTHWISE: rc = fc::launch_depthwise(h->geo, h->plan, a); break;
     case FUSEDCONV_ROUTE_IGEMM_HALO: rc = fc::launch_igemm_halo(h->geo, h->plan, a); break;
     case FUSEDCONV_ROUTE_SMALLC: rc = fc::launch_smallc(h->geo, h->plan, a); break;
+    case FUSEDCONV_ROUTE_POINTWISE: rc = fc::launch_pointwise(h->geo, h->plan, a); break;
     default: return set_err(FUSEDCONV_ERR_ROUTE, "handle has no route");
   }
   if (rc != FUSEDCONV_OK) {

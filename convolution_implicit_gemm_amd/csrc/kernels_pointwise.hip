@@ -1,0 +1,358 @@
+// 1x1 convolution (stride 1, no padding) as a batched GEMM on MFMA (fp16 in,
+// fp32 accumulate): Y[n][g*Mg + m][p] = sum_c W[g*Mg + m][c] * X[n][g*Cg + c][p]
+// for every pixel p of the flattened spatial extent -- the implicit GEMM of
+// the FusedConv README with a single tap, where im2col is the identity and X
+// itself is the [C/group x pixels] operand.
+//
+// GEMM view per block: rows = 128 pixels of one image, columns = 128 output
+// channels of one group, reduction over the group's input channels in steps
+// of 64.  NCHW stores pixels, not channels, consecutively, while the MFMA
+// operand of a lane is 8 consecutive reduction elements, so X is transposed
+// on its way into LDS:
+//   * two producer waves stream X: a thread loads 4 channels x 8 pixels
+//     (four 16-byte loads) per item, keeps three steps of loads in flight in
+//     registers and writes each item as eight 8-byte pieces of channel-last
+//     LDS rows [pixel][64 channels + 16 pad] (160-byte rows: a 16-row
+//     ds_read_b128 operand read is conflict free).  A wave's memory counter
+//     completes in issue order, so a wave that waited for a weight load
+//     issued after long X loads would wait for those too; with the roles
+//     split, the producers wait only for X and the MFMA waves only for W;
+//   * four MFMA waves read the weights straight from W (C/group % 8 == 0: a
+//     lane's 8 channels are one 16-byte piece of a W row), one step ahead,
+//     as register operands: v_mfma_f32_16x16x32_f16 with pixels as rows and
+//     output channels as columns, each lane ending with 4 consecutive pixels
+//     of one output channel.  One barrier per step hands the two LDS stages
+//     between the roles;
+//   * the epilogue (bias seeds the accumulators; Z, activation, one rounding)
+//     goes through LDS one 16-channel block at a time, so every store writes
+//     whole rows of 64 consecutive pixels.
+// Reduction steps past C/group (when it is not a multiple of 64) read a valid
+// address and multiply by zero weights, so every load is unconditional and
+// the compiler can count the loads in flight exactly.
+#include <hip/hip_runtime.h>
+
+#include "epilogue.h"
+#include "internal.h"
+#include "sync.h"
+
+namespace fc {
+namespace {
+
+constexpr int kThreads = 384;  // 4 MFMA waves + 2 producer waves
+constexpr int kBN = 128;    // pixels per block
+constexpr int kBM = 128;    // output channels per block
+constexpr int kBK = 64;     // input channels per reduction step
+constexpr int kLDC = kBK + 16;  // LDS row pitch in halves (160 bytes)
+constexpr int kStage = kBN * kLDC;  // halves per LDS stage
+constexpr size_t kLds = 2 * kStage * sizeof(half_t);
+// word 3 of a raw buffer resource on gfx9-class GPUs (32-bit data format):
+// offsets past num_records read zero and drop writes
+constexpr int kBufferWord3 = 0x00020000;
+constexpr unsigned kOff = 0x80000000u;  // an offset past every range set up here
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef unsigned uint2v __attribute__((ext_vector_type(2)));
+
+struct PwTile {
+  int64_t P;       // pixels per image (flattened spatial extent)
+  int ntile;       // pixel tiles per image
+  int nmb;         // output-channel blocks per group
+  int ks;          // reduction steps: ceil(C/group / 64)
+  int64_t tiles;   // G * n * ntile
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Two blocks per CU: 12 waves, 3 per SIMD (the launch bound), 168 VGPRs each.
+// Block b -> (pixel tile, channel block).  Blocks are dealt to the 8 XCDs
+// round-robin, so the channel blocks of one pixel tile are placed 8 blocks
+// apart: they run on the same XCD at about the same time and all but the
+// first read X from that XCD's L2.
+template <int ACT>
+__global__ __launch_bounds__(kThreads, 3) void pw_kernel(const half_t* __restrict__ x,
+                                                         const half_t* __restrict__ w,
+                                                         const half_t* __restrict__ bias,
+                                                         const half_t* z, half_t* y,
+                                                         ConvParams cp, PwTile pt) {
+  extern __shared__ __attribute__((aligned(16))) half_t lds[];
+  const int b = blockIdx.x;
+  const int mb = (b >> 3) % pt.nmb;
+  const int64_t tg = (int64_t)(b / (8 * pt.nmb)) * 8 + (b & 7);
+  if (tg >= pt.tiles) return;
+  const int tile = (int)(tg % pt.ntile);
+  const int64_t gn = tg / pt.ntile;       // g * n + image
+  const int64_t n = gn % cp.n;
+  const int g = (int)(gn / cp.n);
+  const int64_t P = pt.P;
+  const int64_t p0 = (int64_t)tile * kBN;
+  const int m0 = mb * kBM;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wpi = wave & 1, wmi = wave >> 1;  // pixel half, channel half
+  const int r16 = lane & 15, q = lane >> 4;
+
+  // ---- weight fragments of step s: channel tile j (output channel
+  // m0 + wmi*64 + 16j + r16, clamped to the group), reduction half kk
+  // (input channels s*64 + 32kk + 8q .. +7).  Past C/group a lane reads its
+  // row's first 8 channels; the products zero them (a select on the loaded
+  // value right at the load would make the wave wait for it there).
+  const half_t* wrow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = min(m0 + wmi * 64 + j * 16 + r16, cp.Mg - 1);
+    wrow[j] = w + ((int64_t)g * cp.Mg + m) * cp.Cg;
+  }
+  auto load_w = [&](int s, half8 (*f)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = s * kBK + kk * 32 + q * 8;
+      const bool ok = c < cp.Cg;
+      const int cc = ok ? c : 0;  // an invalid lane reads its row's first 8 channels
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f[j][kk] = *(const half8*)(wrow[j] + cc);
+    }
+  };
+
+  // ---- accumulators start at the bias (lane column r16 = channel
+  // m0 + wmi*64 + 16j + r16)
+  float4v acc[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wmi * 64 + j * 16 + r16;
+    float bv = 0.0f;
+    if (cp.has_bias && m < cp.Mg) bv = to_f32(bias[g * cp.Mg + m]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i][j] = float4v{bv, bv, bv, bv};
+  }
+
+  // LDS offset (halves) of this lane's operand row in pixel tile i
+  int aoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) aoff[i] = (wpi * 64 + i * 16 + r16) * kLDC + q * 8;
+
+  auto mfma_step = [&](int s, half8 (*f)[2]) __attribute__((always_inline)) {
+    const half_t* st = lds + (s & 1) * kStage;
+    if (s * kBK + kBK > cp.Cg) {  // the partial last step: weights past C/group are zero
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (s * kBK + kk * 32 + q * 8 >= cp.Cg) f[j][kk] = half8{};
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      half8 a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *(const half8*)(st + aoff[i] + kk * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], f[j][kk], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  const int ks = pt.ks;
+  if (wave >= 4) {
+    // ---- producer: items (channel quad cq, pixel octet po) ptid and
+    // ptid + 128 of each step: channels 4*cq .. +3 of the step, pixels
+    // 8*po .. +7 of the tile.  Invalid pieces read x[0..7] (unconditional
+    // loads) and are written as zeros.  Step s: write X(s) into stage s&1,
+    // barrier, load X(s+3) (clamped to the last step) into the freed set.
+    const int ptid = tid - 256;
+    int cq[2], po[2];
+    bool pix_ok[2];
+    const half_t* xs[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int it = ptid + 128 * k;
+      cq[k] = it & 15;
+      po[k] = it >> 4;
+      pix_ok[k] = p0 + 8 * po[k] < P;  // P % 8 == 0: an octet is all in or all out
+      xs[k] = x + ((n * cp.C + (int64_t)g * cp.Cg) * P + p0 + 8 * po[k]);
+    }
+    auto load_x = [&](int st, half8 (*v)[4]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = st * kBK + 4 * cq[k] + j;
+          const bool ok = pix_ok[k] && c < cp.Cg;
+          v[k][j] = *(const half8*)(ok ? xs[k] + (int64_t)c * P : x);
+        }
+    };
+    auto store_x = [&](int st, half8 (*v)[4]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        half_t* dst = lds + (st & 1) * kStage + (8 * po[k]) * kLDC + 4 * cq[k];
+        const int cvalid = cp.Cg - st * kBK - 4 * cq[k];
+        half8 u[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[j] = pix_ok[k] && j < cvalid ? v[k][j] : half8{};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *(half4*)(dst + e * kLDC) = half4{u[0][e], u[1][e], u[2][e], u[3][e]};
+      }
+    };
+    half8 x0[2][4], x1[2][4], x2[2][4];
+    load_x(0, x0);
+    load_x(min(1, ks - 1), x1);
+    load_x(min(2, ks - 1), x2);
+#define PW_PROD(S, XS)                  \
+  {                                     \
+    store_x(S, XS);                     \
+    lds_barrier();                      \
+    load_x(min((S) + 3, ks - 1), XS);   \
+  }
+    int st = 0;
+    for (; st + 3 <= ks; st += 3) {
+      PW_PROD(st, x0);
+      PW_PROD(st + 1, x1);
+      PW_PROD(st + 2, x2);
+    }
+    if (st < ks) {
+      PW_PROD(st, x0);
+      if (st + 1 < ks) PW_PROD(st + 1, x1);
+    }
+#undef PW_PROD
+    lds_barrier();  // the MFMA waves' barrier before their epilogue
+    return;
+  }
+
+  // ---- MFMA waves: step s waits at the barrier for X(s) in stage s&1,
+  // loads W(s+1) (clamped) into the other register set, then multiplies.
+  // The loads stay between the previous step's products and this step's
+  // (scheduling barriers): a product waits only for W(s), issued a step
+  // earlier, and W(s+1) never overwrites registers still being read.
+  half8 wa[4][2], wb[4][2];
+  load_w(0, wa);
+#define PW_STEP(S, WC, WN)                  \
+  {                                         \
+    lds_barrier();                          \
+    __builtin_amdgcn_sched_barrier(0);      \
+    load_w(min((S) + 1, ks - 1), WN);       \
+    __builtin_amdgcn_sched_barrier(0);      \
+    mfma_step(S, WC);                       \
+  }
+  int s = 0;
+  for (; s + 2 <= ks; s += 2) {
+    PW_STEP(s, wa, wb);
+    PW_STEP(s + 1, wb, wa);
+  }
+  if (s < ks) PW_STEP(s, wa, wb);
+#undef PW_STEP
+  lds_barrier();  // every MFMA wave is done with the stages
+
+  // ---- epilogue (the stage buffers are dead now): per 16-channel block,
+  // the wave's accumulators go to LDS as 16 rows of its 64 pixels; lane
+  // (rsub, p4) then owns pixels p4 .. p4+3 of rows rsub, rsub+4, .., adds
+  // Z, applies the activation and stores 8 bytes: 16 lanes cover a row's
+  // 128 contiguous bytes.  Raw buffer operations: an invalid slot gets an
+  // offset past the range (Z reads zero, the store is dropped).
+  constexpr int RP = 64 + 4;  // fp32 stage row pitch
+  float* stage = (float*)lds + wave * 16 * RP;
+  const int mw0 = m0 + wmi * 64;  // first channel of this wave
+  const int p4 = (lane & 15) * 4, rsub = lane >> 4;
+  const int64_t pg = p0 + wpi * 64 + p4;  // image pixel of this lane
+  const bool pok = pg < P;
+  const int64_t wbase = (n * cp.M + (int64_t)g * cp.Mg + mw0) * P;
+  const __amdgpu_buffer_rsrc_t yb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(y + wbase), (short)0, 0x7fffffff, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t zb = __builtin_amdgcn_make_buffer_rsrc(
+      cp.has_z ? (void*)(z + wbase) : (void*)y, (short)0, cp.has_z ? 0x7fffffff : 0, kBufferWord3);
+  auto voff = [&](int j, int it) __attribute__((always_inline)) {
+    const int r = j * 16 + it * 4 + rsub;  // channel relative to mw0
+    return (pok && mw0 + r < cp.Mg) ? (unsigned)((r * P + pg) * 2) : kOff;
+  };
+  uint2v zr[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+      zr[j][it] = __builtin_bit_cast(uint2v, __builtin_amdgcn_raw_buffer_load_b64(zb, voff(j, it), 0, 0));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(float4v*)(stage + r16 * RP + i * 16 + q * 4) = acc[i][j];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const float4v sv = *(const float4v*)(stage + (it * 4 + rsub) * RP + p4);
+      const half4 zh = __builtin_bit_cast(half4, zr[j][it]);
+      act4_t v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = sv[e] + (float)zh[e];
+      v = act4<ACT>(v, cp.alpha, cp.beta);
+      half4 out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] = (half_t)v[e];
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, out), yb, voff(j, it), 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+bool choose(const ConvParams& cp, int32_t dtype, PwTile& pt) {
+  if (dtype != FUSEDCONV_F16) return false;
+  if (cp.KD != 1 || cp.KH != 1 || cp.KW != 1 || cp.sd != 1 || cp.sh != 1 || cp.sw != 1) return false;
+  if (cp.pd != 0 || cp.ph != 0 || cp.pw != 0) return false;
+  if (cp.OD != cp.D || cp.OH != cp.H || cp.OW != cp.W) return false;  // no end padding either
+  if (cp.Cg % 8 != 0 || cp.Cg < 16) return false;
+  pt.P = cp.out_sz;
+  if (pt.P % 8 != 0) return false;
+  // epilogue offsets: 64 channel planes of one image in 31-bit byte offsets
+  if (pt.P * 64 * 2 >= ((int64_t)1 << 31)) return false;
+  pt.ntile = (int)cdiv(pt.P, kBN);
+  pt.nmb = (int)cdiv(cp.Mg, kBM);
+  pt.ks = (int)cdiv(cp.Cg, kBK);
+  pt.tiles = (int64_t)cp.G * cp.n * pt.ntile;
+  const int64_t blocks = cdiv(pt.tiles, 8) * 8 * pt.nmb;
+  return blocks < ((int64_t)1 << 31);
+}
+
+}  // namespace
+
+#ifndef FC_ACT
+#error "compiled once per activation id: -DFC_ACT=<0..ACT_COUNT-1>"
+#endif
+
+// the POINTWISE route with activation FC_ACT
+int FC_CAT(launch_pointwise_act_, FC_ACT)(const Geometry& g, const RunArgs& a) {
+  PwTile pt;
+  if (!choose(g.cp, g.dtype, pt)) return FUSEDCONV_ERR_ROUTE;
+  const void* kfn = (const void*)pw_kernel<FC_ACT>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds) != hipSuccess)
+      return FUSEDCONV_ERR_LAUNCH;
+    attr_set = true;
+  }
+  const int64_t blocks = cdiv(pt.tiles, 8) * 8 * pt.nmb;
+  hipLaunchKernelGGL(pw_kernel<FC_ACT>, dim3((unsigned)blocks), dim3(kThreads), kLds,
+                     (hipStream_t)a.stream, (const half_t*)a.x, (const half_t*)a.w,
+                     (const half_t*)a.bias, (const half_t*)a.z, (half_t*)a.y, g.cp, pt);
+  return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
+}
+
+#if FC_ACT == 0
+FC_ACT_DECLS(launch_pointwise_act_)
+
+bool pointwise_fits(const ConvParams& cp, int32_t dtype) {
+  PwTile pt;
+  return choose(cp, dtype, pt);
+}
+
+int launch_pointwise(const Geometry& g, const Plan&, const RunArgs& a) {
+  static const ActLaunchFn table[ACT_COUNT] = FC_ACT_TABLE(launch_pointwise_act_);
+  return table[g.cp.act](g, a);
+}
+#endif
+
+}  // namespace fc

@@ -5,7 +5,8 @@
 // derive implicitTiledWorthIt, tiledSplitK*, preferImplicitSplitK); what
 // carries over is the shape of the decision: grouped convs with one input
 // channel per group go to a direct halo kernel, dense channel counts go to an
-// implicit GEMM (few input channels: the row-chunk SMALLC form), and a GEMM
+// implicit GEMM (1x1 with stride 1: a plain batched GEMM, POINTWISE; few input
+// channels: the row-chunk SMALLC form), and a GEMM
 // whose output grid cannot fill the device splits
 // its reduction (split-K: raw fp32 partials, then one reduce that applies
 // bias, residual and activation once).  Thresholds here are for 256 CUs.
@@ -80,7 +81,7 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
     err = "split_k must be >= 0";
     return FUSEDCONV_ERR_ROUTE;
   }
-  if (route < FUSEDCONV_ROUTE_AUTO || route > FUSEDCONV_ROUTE_SMALLC) {
+  if (route < FUSEDCONV_ROUTE_AUTO || route > FUSEDCONV_ROUTE_POINTWISE) {
     err = "unknown route";
     return FUSEDCONV_ERR_ROUTE;
   }
@@ -94,6 +95,9 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
   if (route == FUSEDCONV_ROUTE_AUTO) {
     if (split_req > 1) route = FUSEDCONV_ROUTE_IGEMM;
     else if (cp.Cg == 1 && depthwise_fits(cp, th, tw)) route = FUSEDCONV_ROUTE_DEPTHWISE;
+    // 1x1: the pointwise GEMM beats the halo route once the reduction is long
+    // (measured on MI355X: C/group 512, 2x; C/group 128 and 256, 10-25% slower)
+    else if (cp.Cg >= 512 && pointwise_fits(cp, g.dtype)) route = FUSEDCONV_ROUTE_POINTWISE;
     else if (igemm_halo_fits(cp, g.dtype, th, tw, halo_ws)) route = FUSEDCONV_ROUTE_IGEMM_HALO;
     else if (smallc_fits(cp, g.dtype, th, tw, halo_ws)) route = FUSEDCONV_ROUTE_SMALLC;
     else if (cp.K >= 8 && cp.Mg >= 8 && igemm_grid_ok(cp, 1)) route = FUSEDCONV_ROUTE_IGEMM;
@@ -151,6 +155,15 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
       p.tile_w = tw;
       p.workspace = halo_ws;
       snprintf(p.name, sizeof(p.name), "smallc_f16_t%dx%d", th, tw);
+      return FUSEDCONV_OK;
+    case FUSEDCONV_ROUTE_POINTWISE:
+      if (!pointwise_fits(cp, g.dtype)) {
+        err = "POINTWISE needs fp16, kernel 1, stride 1, no padding, C/group % 8 == 0, "
+              "C/group >= 16 and a pixel count per image that is a multiple of 8";
+        return FUSEDCONV_ERR_ROUTE;
+      }
+      p.route = route;
+      snprintf(p.name, sizeof(p.name), "pointwise_f16_m128_n128");
       return FUSEDCONV_OK;
     default:
       err = "unknown route";

@@ -61,6 +61,11 @@ typedef enum fusedconv_dtype {
  *              consecutive kernel columns read from a channel-planar input
  *              box; needs 1 or 2 spatial dims, dilation 1 along the last
  *              axis, C/group < 16 and C/group * KH * ceil(KW/8) <= 24.
+ *   POINTWISE  1x1 convolution as a batched GEMM on MFMA, fp16 only (the
+ *              FusedConv README's implicit GEMM with one tap, X itself the
+ *              reduction operand): needs kernel 1, stride 1, no padding,
+ *              C/group % 8 == 0, C/group >= 16 and a pixel count per image
+ *              that is a multiple of 8.
  */
 typedef enum fusedconv_route {
   FUSEDCONV_ROUTE_AUTO = 0,
@@ -68,7 +73,8 @@ typedef enum fusedconv_route {
   FUSEDCONV_ROUTE_IGEMM = 2,
   FUSEDCONV_ROUTE_DEPTHWISE = 3,
   FUSEDCONV_ROUTE_IGEMM_HALO = 4,
-  FUSEDCONV_ROUTE_SMALLC = 5
+  FUSEDCONV_ROUTE_SMALLC = 5,
+  FUSEDCONV_ROUTE_POINTWISE = 6
 } fusedconv_route;
 
 /* Shape of one tensor.  present = 0 means the (optional) input is absent. */

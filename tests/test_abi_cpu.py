@@ -70,7 +70,8 @@ def test_workload_shapes_and_routes():
     for name, wl in WORKLOADS.items():
         h = B.Handle(wl["dtype"], wl["x"], wl["w"], wl["b"], wl["z"], **wl["attrs"])
         assert h.y_shape == wl["y"], name
-        assert h.route in ("direct", "igemm", "depthwise", "igemm_halo", "smallc"), name
+        assert h.route in ("direct", "igemm", "depthwise", "igemm_halo", "smallc",
+                           "pointwise"), name
         if wl["attrs"].get("group", 1) == wl["x"][1]:
             assert h.route == "depthwise", name
     stem = WORKLOADS["vision_stem_7x7s4_f16"]
@@ -192,6 +193,36 @@ def test_smallc_route_limits():
         c = dict(c)
         with pytest.raises(B.FusedConvError) as e:
             _h(c.pop("x"), c.pop("w"), route="smallc", **c)
+        assert e.value.status == "FUSEDCONV_ERR_ROUTE"
+
+
+def test_pointwise_route_limits():
+    # fp16 1x1 convs with stride 1 and no padding take the pointwise route
+    # (the planner picks it by itself from C/group 512 on)
+    for xs, ws, kw in [([2, 64, 16, 16], [96, 64, 1, 1], {}),
+                       ([2, 128, 72], [128, 128, 1], {}),
+                       ([1, 32, 4, 8, 8], [48, 32, 1, 1, 1], {}),
+                       ([2, 64, 8, 8], [64, 32, 1, 1], dict(group=2)),
+                       ([1, 16, 8, 8], [32, 16, 1, 1], dict(dilations=[2, 3]))]:
+        h = _h(xs, ws, dtype="f16", route="pointwise", **kw)
+        assert h.route == "pointwise" and h.workspace_bytes == 0, (xs, ws, kw)
+        assert h.kernel_name == "pointwise_f16_m128_n128"
+    assert _h([2, 512, 8, 8], [64, 512, 1, 1], dtype="f16").route == "pointwise"
+    assert _h([2, 256, 8, 8], [64, 256, 1, 1], dtype="f16").route == "igemm_halo"
+    refused = [
+        dict(x=[1, 64, 16, 16], w=[64, 64, 1, 1], dtype="f32"),                     # fp32
+        dict(x=[1, 64, 16, 16], w=[64, 64, 1, 1], strides=[2, 2], dtype="f16"),     # stride 2
+        dict(x=[1, 64, 16, 16], w=[64, 64, 1, 1], pads=[1, 1, 1, 1], dtype="f16"),  # padded
+        dict(x=[1, 64, 16, 16], w=[64, 64, 1, 1], pads=[0, 0, 0, 1], dtype="f16"),  # end pad
+        dict(x=[1, 60, 16, 16], w=[64, 60, 1, 1], dtype="f16"),                     # C % 8 != 0
+        dict(x=[1, 8, 16, 16], w=[64, 8, 1, 1], dtype="f16"),                       # C/group < 16
+        dict(x=[1, 64, 14, 14], w=[64, 64, 1, 1], dtype="f16"),                     # 196 pixels
+        dict(x=[1, 64, 16, 16], w=[64, 64, 3, 3], dtype="f16"),                     # 3x3
+    ]
+    for c in refused:
+        c = dict(c)
+        with pytest.raises(B.FusedConvError) as e:
+            _h(c.pop("x"), c.pop("w"), route="pointwise", **c)
         assert e.value.status == "FUSEDCONV_ERR_ROUTE"
 
 

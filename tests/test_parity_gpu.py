@@ -458,6 +458,38 @@ def test_deterministic_and_inplace_residual(route):
     assert torch.equal(y3, y1)
 
 
+POINTWISE_CASES = [
+    # (x, w, attrs) for the 1x1 route (fp16): ragged pixel tiles, partial
+    # channel blocks, odd and partial reduction steps, groups, 1-D and 3-D
+    ([2, 64, 16, 16], [96, 64, 1, 1], {}),                  # Mg < 128, 2 pixel tiles
+    ([2, 256, 14, 16], [256, 256, 1, 1], {}),               # 224 pixels: a partial tile; 2 m blocks
+    ([2, 64, 8, 8], [64, 32, 1, 1], dict(group=2)),         # groups
+    ([1, 40, 12, 12], [200, 40, 1, 1], {}),                 # C/group 40: one partial step
+    ([2, 136, 8, 16], [64, 136, 1, 1], {}),                 # 3 steps, the last partial
+    ([2, 128, 72], [128, 128, 1], {}),                      # 1-D
+    ([1, 32, 4, 8, 8], [48, 32, 1, 1, 1], {}),              # 3-D
+    ([1, 16, 8, 8], [32, 16, 1, 1], dict(dilations=[2, 2])),  # C/group 16; dilation is moot
+    ([1, 1024, 8, 8], [64, 1024, 1, 1], {}),                # 16 steps
+]
+
+
+@pytest.mark.parametrize("ci", range(len(POINTWISE_CASES)))
+def test_pointwise_route(ci):
+    xs, ws, attrs = POINTWISE_CASES[ci]
+    h = B.Handle("f16", xs, ws, None, None, route="pointwise", **attrs)
+    assert h.route == "pointwise"
+    for k, (bias, resid) in enumerate([(True, True), (False, False), (True, False)]):
+        act, params = ACTS[(3 * ci + 5 * k) % len(ACTS)]
+        x, w, b, z = random_tensors([9400, ci, k], "f16", xs, ws, [ws[0]] if bias else None,
+                                    h.y_shape if resid else None, dist="normal",
+                                    w_std=1.0 / np.sqrt(np.prod(ws[1:])))
+        a = dict(attrs, activation=act, activation_params=f32params(params))
+        log(f"CASE pointwise {ci} x={xs} w={ws} {a} bias={bias} z={resid}")
+        got = run_gpu(x, w, b, z, route="pointwise", **a)
+        ref = oracle.fusedconv(x, w, b, z, **a)
+        check(got, ref, "f16", f"pointwise case {ci}")
+
+
 @pytest.mark.parametrize("route", ["igemm_halo", "igemm", "depthwise", "smallc"])
 def test_prepared_weights_match_plain_run(route):
     C = {"depthwise": 16, "smallc": 3}.get(route, 64)
