@@ -61,6 +61,7 @@ int prepare_igemm_halo(const Geometry& g, const Plan& p, const RunArgs& a);
 int launch_smallc(const Geometry& g, const Plan& p, const RunArgs& a);
 int prepare_smallc(const Geometry& g, const Plan& p, const RunArgs& a);
 int launch_pointwise(const Geometry& g, const Plan& p, const RunArgs& a);
+int prepare_pointwise(const Geometry& g, const Plan& p, const RunArgs& a);
 
 // Kernels whose activation is a compile-time parameter: the build compiles
 // their source once per activation id (FC_ACT = 0 .. ACT_COUNT-1); unit k
@@ -95,7 +96,8 @@ bool igemm_halo_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32
                      size_t& workspace, int32_t* block_m = nullptr);
 bool smallc_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32_t& tile_w,
                  size_t& workspace);
-// 1x1 route (kernels_pointwise.hip): kernel 1, stride 1, no padding, fp16.
-bool pointwise_fits(const ConvParams& cp, int32_t dtype);
+// 1x1 route (kernels_pointwise.hip): kernel 1, stride 1, no padding, fp16;
+// optionally the bytes of its repacked-weight workspace.
+bool pointwise_fits(const ConvParams& cp, int32_t dtype, size_t* workspace = nullptr);
 
 }  // namespace fc

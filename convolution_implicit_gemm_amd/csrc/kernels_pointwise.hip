@@ -12,23 +12,30 @@
 //   * two producer waves stream X: a thread loads 4 channels x 8 pixels
 //     (four 16-byte loads) per item, keeps three steps of loads in flight in
 //     registers and writes each item as eight 8-byte pieces of channel-last
-//     LDS rows [pixel][64 channels + 16 pad] (160-byte rows: a 16-row
-//     ds_read_b128 operand read is conflict free).  A wave's memory counter
+//     LDS rows [pixel][64 channels + 16 pad].  The 16 lanes of a load pass
+//     cover 2 channel quads x 8 pixel octets, i.e. whole 128-byte pieces of
+//     2 channel rows (a pass that touches 16 rows costs the address unit 8x
+//     more); so that those lanes' transposed writes do not collide in the
+//     LDS banks, the 16-byte columns of a row are XOR-swizzled by the row's
+//     pixel octet (the operand reads apply the same swizzle and stay
+//     conflict free on the 160-byte rows).  A wave's memory counter
 //     completes in issue order, so a wave that waited for a weight load
 //     issued after long X loads would wait for those too; with the roles
 //     split, the producers wait only for X and the MFMA waves only for W;
-//   * four MFMA waves read the weights straight from W (C/group % 8 == 0: a
-//     lane's 8 channels are one 16-byte piece of a W row), one step ahead,
-//     as register operands: v_mfma_f32_16x16x32_f16 with pixels as rows and
+//   * four MFMA waves read the weights, one step ahead, from a copy of W
+//     repacked in fragment order (fusedconv_prepare_weights, or at the start
+//     of every run): each 16-byte lane piece of an operand is contiguous
+//     with its neighbours', zero past C/group and M/group, as register
+//     operands: v_mfma_f32_16x16x32_f16 with pixels as rows and
 //     output channels as columns, each lane ending with 4 consecutive pixels
 //     of one output channel.  One barrier per step hands the two LDS stages
 //     between the roles;
 //   * the epilogue (bias seeds the accumulators; Z, activation, one rounding)
 //     goes through LDS one 16-channel block at a time, so every store writes
 //     whole rows of 64 consecutive pixels.
-// Reduction steps past C/group (when it is not a multiple of 64) read a valid
-// address and multiply by zero weights, so every load is unconditional and
-// the compiler can count the loads in flight exactly.
+// Every load is unconditional (invalid X pieces read a valid address and are
+// written as zeros; the repacked weights are zero-padded), so the compiler can
+// count the loads in flight exactly.
 #include <hip/hip_runtime.h>
 
 #include "epilogue.h"
@@ -65,6 +72,35 @@ struct PwTile {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Weights in fragment order: Wf[((((g*nmb + mb)*ks + s)*2 + kk)*4 + j)*2 + wmi]
+// [lane][e] = W[g*Mg + m][c] with m = mb*128 + wmi*64 + j*16 + lane%16 and
+// c = s*64 + kk*32 + (lane/16)*8 + e; zero for m >= M/group or c >= C/group.
+constexpr int kFragHalves = 2 * 4 * 2 * 64 * 8;  // halves per (group, m block, step)
+__global__ __launch_bounds__(256) void repack_frag_kernel(const half_t* __restrict__ w,
+                                                          half_t* __restrict__ wf, ConvParams cp,
+                                                          PwTile pt) {
+  const int64_t total = (int64_t)cp.G * pt.nmb * pt.ks * kFragHalves;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
+    const int e = (int)(i & 7);
+    const int lane = (int)((i >> 3) & 63);
+    int64_t t = i >> 9;
+    const int wmi = (int)(t & 1);
+    t >>= 1;
+    const int j = (int)(t & 3);
+    t >>= 2;
+    const int kk = (int)(t & 1);
+    t >>= 1;
+    const int s = (int)(t % pt.ks);
+    t /= pt.ks;
+    const int mb = (int)(t % pt.nmb);
+    const int g = (int)(t / pt.nmb);
+    const int m = mb * kBM + wmi * 64 + j * 16 + (lane & 15);
+    const int c = s * kBK + kk * 32 + (lane >> 4) * 8 + e;
+    wf[i] = (m < cp.Mg && c < cp.Cg) ? w[((int64_t)g * cp.Mg + m) * cp.Cg + c] : (half_t)0;
+  }
+}
+
 // Two blocks per CU: 12 waves, 3 per SIMD (the launch bound), 168 VGPRs each.
 // Block b -> (pixel tile, channel block).  Blocks are dealt to the 8 XCDs
 // round-robin, so the channel blocks of one pixel tile are placed 8 blocks
@@ -72,7 +108,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // first read X from that XCD's L2.
 template <int ACT>
 __global__ __launch_bounds__(kThreads, 3) void pw_kernel(const half_t* __restrict__ x,
-                                                         const half_t* __restrict__ w,
+                                                         const half_t* __restrict__ wf,
                                                          const half_t* __restrict__ bias,
                                                          const half_t* z, half_t* y,
                                                          ConvParams cp, PwTile pt) {
@@ -94,26 +130,15 @@ __global__ __launch_bounds__(kThreads, 3) void pw_kernel(const half_t* __restric
   const int wpi = wave & 1, wmi = wave >> 1;  // pixel half, channel half
   const int r16 = lane & 15, q = lane >> 4;
 
-  // ---- weight fragments of step s: channel tile j (output channel
-  // m0 + wmi*64 + 16j + r16, clamped to the group), reduction half kk
-  // (input channels s*64 + 32kk + 8q .. +7).  Past C/group a lane reads its
-  // row's first 8 channels; the products zero them (a select on the loaded
-  // value right at the load would make the wave wait for it there).
-  const half_t* wrow[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = min(m0 + wmi * 64 + j * 16 + r16, cp.Mg - 1);
-    wrow[j] = w + ((int64_t)g * cp.Mg + m) * cp.Cg;
-  }
+  // ---- weight fragments of step s: channel tile j, reduction half kk, one
+  // contiguous 1 KB piece of Wf per (step, kk, j, wave) and 16 bytes per lane
+  const half_t* wfb = wf + ((int64_t)g * pt.nmb + mb) * pt.ks * kFragHalves + wmi * 512 + lane * 8;
   auto load_w = [&](int s, half8 (*f)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int c = s * kBK + kk * 32 + q * 8;
-      const bool ok = c < cp.Cg;
-      const int cc = ok ? c : 0;  // an invalid lane reads its row's first 8 channels
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) f[j][kk] = *(const half8*)(wrow[j] + cc);
-    }
+      for (int j = 0; j < 4; ++j)
+        f[j][kk] = *(const half8*)(wfb + (int64_t)s * kFragHalves + (kk * 4 + j) * 1024);
   };
 
   // ---- accumulators start at the bias (lane column r16 = channel
@@ -128,25 +153,24 @@ __global__ __launch_bounds__(kThreads, 3) void pw_kernel(const half_t* __restric
     for (int i = 0; i < 4; ++i) acc[i][j] = float4v{bv, bv, bv, bv};
   }
 
-  // LDS offset (halves) of this lane's operand row in pixel tile i
-  int aoff[4];
+  // LDS offset (halves) of this lane's operand in pixel tile i, reduction
+  // half kk: row wpi*64 + 16i + r16, 16-byte column 4kk + q swizzled by the
+  // row's pixel octet
+  int aoff[4][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) aoff[i] = (wpi * 64 + i * 16 + r16) * kLDC + q * 8;
+  for (int i = 0; i < 4; ++i) {
+    const int row = wpi * 64 + i * 16 + r16;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) aoff[i][kk] = row * kLDC + (((kk * 4 + q) ^ ((row >> 3) & 7)) * 8);
+  }
 
   auto mfma_step = [&](int s, half8 (*f)[2]) __attribute__((always_inline)) {
     const half_t* st = lds + (s & 1) * kStage;
-    if (s * kBK + kBK > cp.Cg) {  // the partial last step: weights past C/group are zero
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (s * kBK + kk * 32 + q * 8 >= cp.Cg) f[j][kk] = half8{};
-    }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       half8 a[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *(const half8*)(st + aoff[i] + kk * 32);
+      for (int i = 0; i < 4; ++i) a[i] = *(const half8*)(st + aoff[i][kk]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -157,11 +181,13 @@ __global__ __launch_bounds__(kThreads, 3) void pw_kernel(const half_t* __restric
 
   const int ks = pt.ks;
   if (wave >= 4) {
-    // ---- producer: items (channel quad cq, pixel octet po) ptid and
-    // ptid + 128 of each step: channels 4*cq .. +3 of the step, pixels
-    // 8*po .. +7 of the tile.  Invalid pieces read x[0..7] (unconditional
-    // loads) and are written as zeros.  Step s: write X(s) into stage s&1,
-    // barrier, load X(s+3) (clamped to the last step) into the freed set.
+    // ---- producer: items it = ptid and ptid + 128 of each step, item it =
+    // (channel quad cq, pixel octet po) with po = (it & 7) + 8*((it >> 4) & 1),
+    // cq = ((it >> 3) & 1) + 2*(it >> 5): channels 4*cq .. +3 of the step,
+    // pixels 8*po .. +7 of the tile (a 16-lane pass: 2 quads x 8 octets).
+    // Invalid pieces read x[0..7] (unconditional loads) and are written as
+    // zeros.  Step s: write X(s) into stage s&1, barrier, load X(s+3)
+    // (clamped to the last step) into the freed set.
     const int ptid = tid - 256;
     int cq[2], po[2];
     bool pix_ok[2];
@@ -169,8 +195,8 @@ __global__ __launch_bounds__(kThreads, 3) void pw_kernel(const half_t* __restric
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int it = ptid + 128 * k;
-      cq[k] = it & 15;
-      po[k] = it >> 4;
+      po[k] = (it & 7) + 8 * ((it >> 4) & 1);
+      cq[k] = ((it >> 3) & 1) + 2 * (it >> 5);
       pix_ok[k] = p0 + 8 * po[k] < P;  // P % 8 == 0: an octet is all in or all out
       xs[k] = x + ((n * cp.C + (int64_t)g * cp.Cg) * P + p0 + 8 * po[k]);
     }
@@ -187,7 +213,8 @@ __global__ __launch_bounds__(kThreads, 3) void pw_kernel(const half_t* __restric
     auto store_x = [&](int st, half8 (*v)[4]) __attribute__((always_inline)) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        half_t* dst = lds + (st & 1) * kStage + (8 * po[k]) * kLDC + 4 * cq[k];
+        // row 8*po + e, bytes 8*cq .. +7 of the row's channels, swizzled
+        half_t* dst = lds + (st & 1) * kStage + (8 * po[k]) * kLDC + ((8 * cq[k]) ^ ((po[k] & 7) << 4)) / 2;
         const int cvalid = cp.Cg - st * kBK - 4 * cq[k];
         half8 u[4];
 #pragma unroll
@@ -317,6 +344,15 @@ bool choose(const ConvParams& cp, int32_t dtype, PwTile& pt) {
   return blocks < ((int64_t)1 << 31);
 }
 
+int launch_repack(const ConvParams& cp, const PwTile& pt, const RunArgs& a) {
+  const int64_t total = (int64_t)cp.G * pt.nmb * pt.ks * kFragHalves;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(repack_frag_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)a.stream,
+                     (const half_t*)a.w, (half_t*)a.ws, cp, pt);
+  return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
+}
+
 }  // namespace
 
 #ifndef FC_ACT
@@ -327,6 +363,10 @@ bool choose(const ConvParams& cp, int32_t dtype, PwTile& pt) {
 int FC_CAT(launch_pointwise_act_, FC_ACT)(const Geometry& g, const RunArgs& a) {
   PwTile pt;
   if (!choose(g.cp, g.dtype, pt)) return FUSEDCONV_ERR_ROUTE;
+  if (!(a.flags & FUSEDCONV_RUN_WEIGHTS_PREPARED)) {
+    const int rc = launch_repack(g.cp, pt, a);
+    if (rc != FUSEDCONV_OK) return rc;
+  }
   const void* kfn = (const void*)pw_kernel<FC_ACT>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -336,7 +376,7 @@ int FC_CAT(launch_pointwise_act_, FC_ACT)(const Geometry& g, const RunArgs& a) {
   }
   const int64_t blocks = cdiv(pt.tiles, 8) * 8 * pt.nmb;
   hipLaunchKernelGGL(pw_kernel<FC_ACT>, dim3((unsigned)blocks), dim3(kThreads), kLds,
-                     (hipStream_t)a.stream, (const half_t*)a.x, (const half_t*)a.w,
+                     (hipStream_t)a.stream, (const half_t*)a.x, (const half_t*)a.ws,
                      (const half_t*)a.bias, (const half_t*)a.z, (half_t*)a.y, g.cp, pt);
   return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
 }
@@ -344,9 +384,17 @@ int FC_CAT(launch_pointwise_act_, FC_ACT)(const Geometry& g, const RunArgs& a) {
 #if FC_ACT == 0
 FC_ACT_DECLS(launch_pointwise_act_)
 
-bool pointwise_fits(const ConvParams& cp, int32_t dtype) {
+bool pointwise_fits(const ConvParams& cp, int32_t dtype, size_t* workspace) {
   PwTile pt;
-  return choose(cp, dtype, pt);
+  if (!choose(cp, dtype, pt)) return false;
+  if (workspace) *workspace = (size_t)cp.G * pt.nmb * pt.ks * kFragHalves * sizeof(half_t);
+  return true;
+}
+
+int prepare_pointwise(const Geometry& g, const Plan&, const RunArgs& a) {
+  PwTile pt;
+  if (!choose(g.cp, g.dtype, pt)) return FUSEDCONV_ERR_ROUTE;
+  return launch_repack(g.cp, pt, a);
 }
 
 int launch_pointwise(const Geometry& g, const Plan&, const RunArgs& a) {

@@ -95,9 +95,9 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
   if (route == FUSEDCONV_ROUTE_AUTO) {
     if (split_req > 1) route = FUSEDCONV_ROUTE_IGEMM;
     else if (cp.Cg == 1 && depthwise_fits(cp, th, tw)) route = FUSEDCONV_ROUTE_DEPTHWISE;
-    // 1x1: the pointwise GEMM beats the halo route once the reduction is long
-    // (measured on MI355X: C/group 512, 2x; C/group 128 and 256, 10-25% slower)
-    else if (cp.Cg >= 512 && pointwise_fits(cp, g.dtype)) route = FUSEDCONV_ROUTE_POINTWISE;
+    // 1x1: the pointwise GEMM (measured on MI355X against the halo route:
+    // C/group 512 2.6x faster, 256 8-9%, 128 on par)
+    else if (pointwise_fits(cp, g.dtype)) route = FUSEDCONV_ROUTE_POINTWISE;
     else if (igemm_halo_fits(cp, g.dtype, th, tw, halo_ws)) route = FUSEDCONV_ROUTE_IGEMM_HALO;
     else if (smallc_fits(cp, g.dtype, th, tw, halo_ws)) route = FUSEDCONV_ROUTE_SMALLC;
     else if (cp.K >= 8 && cp.Mg >= 8 && igemm_grid_ok(cp, 1)) route = FUSEDCONV_ROUTE_IGEMM;
@@ -157,12 +157,13 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
       snprintf(p.name, sizeof(p.name), "smallc_f16_t%dx%d", th, tw);
       return FUSEDCONV_OK;
     case FUSEDCONV_ROUTE_POINTWISE:
-      if (!pointwise_fits(cp, g.dtype)) {
+      if (!pointwise_fits(cp, g.dtype, &halo_ws)) {
         err = "POINTWISE needs fp16, kernel 1, stride 1, no padding, C/group % 8 == 0, "
               "C/group >= 16 and a pixel count per image that is a multiple of 8";
         return FUSEDCONV_ERR_ROUTE;
       }
       p.route = route;
+      p.workspace = halo_ws;
       snprintf(p.name, sizeof(p.name), "pointwise_f16_m128_n128");
       return FUSEDCONV_OK;
     default:

@@ -193,8 +193,9 @@ int fusedconv_run(const fusedconv_handle* h, const void* x, const void* w, const
  * Weight preparation, for callers whose W stays the same across many runs
  * (inference): fusedconv_prepare_weights enqueues only the route's weight
  * preparation (for IGEMM_HALO a repack of W into the tap-major layout held in
- * the workspace, for SMALLC a repack into rows of 8 kernel columns; a no-op
- * for the other routes), and fusedconv_run_ex with
+ * the workspace, for SMALLC a repack into rows of 8 kernel columns, for
+ * POINTWISE a repack into MFMA fragment order; a no-op for the other
+ * routes), and fusedconv_run_ex with
  * FUSEDCONV_RUN_WEIGHTS_PREPARED then skips that step and reads the prepared
  * weights from the workspace.  The caller guarantees that the workspace holds
  * the prepared form of the same W, made with the same handle; otherwise the

@@ -490,13 +490,15 @@ def test_pointwise_route(ci):
         check(got, ref, "f16", f"pointwise case {ci}")
 
 
-@pytest.mark.parametrize("route", ["igemm_halo", "igemm", "depthwise", "smallc"])
+@pytest.mark.parametrize("route", ["igemm_halo", "igemm", "depthwise", "smallc", "pointwise"])
 def test_prepared_weights_match_plain_run(route):
     C = {"depthwise": 16, "smallc": 3}.get(route, 64)
     M, grp = (C, C) if route == "depthwise" else (96, 1)
-    xs, ws = [2, C, 16, 16], [M, C // grp, 3, 3]
+    k = 1 if route == "pointwise" else 3
+    xs, ws = [2, C, 16, 16], [M, C // grp, k, k]
     x, w, b, z = random_tensors([8100], "f16", xs, ws, [M], None, dist="normal", w_std=0.05)
-    attrs = dict(group=grp, pads=[1, 1, 1, 1], activation="Relu", route=route)
+    attrs = dict(group=grp, pads=[1, 1, 1, 1] if k == 3 else [0, 0, 0, 0], activation="Relu",
+                 route=route)
     op = fc.FusedConv(xs, ws, "f16", True, False, **attrs)
     xd, wd, bd = dev(x), dev(w), dev(b)
     ws_t = torch.empty(max(op.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
