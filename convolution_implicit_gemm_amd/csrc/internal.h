@@ -96,8 +96,10 @@ bool igemm_halo_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32
                      size_t& workspace, int32_t* block_m = nullptr);
 bool smallc_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32_t& tile_w,
                  size_t& workspace);
-// 1x1 route (kernels_pointwise.hip): kernel 1, stride 1, no padding, fp16;
-// optionally the bytes of its repacked-weight workspace.
-bool pointwise_fits(const ConvParams& cp, int32_t dtype, size_t* workspace = nullptr);
+// Pointwise route (kernels_pointwise.hip), fp16: 1x1 with stride 1, or 2x2
+// with stride 2 (patch 2), no padding; optionally the bytes of its
+// repacked-weight workspace and the patch size.
+bool pointwise_fits(const ConvParams& cp, int32_t dtype, size_t* workspace = nullptr,
+                    int32_t* patch = nullptr);
 
 }  // namespace fc

@@ -33,6 +33,12 @@
 //   * the epilogue (bias seeds the accumulators; Z, activation, one rounding)
 //     goes through LDS one 16-channel block at a time, so every store writes
 //     whole rows of 64 consecutive pixels.
+// The same kernel runs 2x2 convolutions with stride 2 and no padding (patch
+// embeddings, downsampling): ordered as k = c*4 + kh*2 + kw (W's own memory
+// order), the reduction's 4 consecutive elements of one producer item are the
+// 4 taps of one input channel, and its 8 output pixels read 16 consecutive
+// columns of 2 input rows (two 32-byte pieces per row), split into even (kw 0)
+// and odd (kw 1) columns -- the same number of loads as a 1x1 item.
 // Every load is unconditional (invalid X pieces read a valid address and are
 // written as zeros; the repacked weights are zero-padded), so the compiler can
 // count the loads in flight exactly.
@@ -63,18 +69,20 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef unsigned uint2v __attribute__((ext_vector_type(2)));
 
 struct PwTile {
-  int64_t P;       // pixels per image (flattened spatial extent)
+  int64_t P;       // output pixels per image (flattened spatial extent)
+  int kp;          // reduction length per group: C/group * taps (taps 1 or 4)
   int ntile;       // pixel tiles per image
   int nmb;         // output-channel blocks per group
-  int ks;          // reduction steps: ceil(C/group / 64)
+  int ks;          // reduction steps: ceil(kp / 64)
   int64_t tiles;   // G * n * ntile
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Weights in fragment order: Wf[((((g*nmb + mb)*ks + s)*2 + kk)*4 + j)*2 + wmi]
-// [lane][e] = W[g*Mg + m][c] with m = mb*128 + wmi*64 + j*16 + lane%16 and
-// c = s*64 + kk*32 + (lane/16)*8 + e; zero for m >= M/group or c >= C/group.
+// [lane][e] = W[g*Mg + m][k] (W as [M][C/group * taps], its memory order) with
+// m = mb*128 + wmi*64 + j*16 + lane%16 and k = s*64 + kk*32 + (lane/16)*8 + e;
+// zero for m >= M/group or k >= C/group * taps.
 constexpr int kFragHalves = 2 * 4 * 2 * 64 * 8;  // halves per (group, m block, step)
 __global__ __launch_bounds__(256) void repack_frag_kernel(const half_t* __restrict__ w,
                                                           half_t* __restrict__ wf, ConvParams cp,
@@ -97,7 +105,7 @@ __global__ __launch_bounds__(256) void repack_frag_kernel(const half_t* __restri
     const int g = (int)(t / pt.nmb);
     const int m = mb * kBM + wmi * 64 + j * 16 + (lane & 15);
     const int c = s * kBK + kk * 32 + (lane >> 4) * 8 + e;
-    wf[i] = (m < cp.Mg && c < cp.Cg) ? w[((int64_t)g * cp.Mg + m) * cp.Cg + c] : (half_t)0;
+    wf[i] = (m < cp.Mg && c < pt.kp) ? w[((int64_t)g * cp.Mg + m) * pt.kp + c] : (half_t)0;
   }
 }
 
@@ -106,7 +114,7 @@ __global__ __launch_bounds__(256) void repack_frag_kernel(const half_t* __restri
 // round-robin, so the channel blocks of one pixel tile are placed 8 blocks
 // apart: they run on the same XCD at about the same time and all but the
 // first read X from that XCD's L2.
-template <int ACT>
+template <int ACT, int PATCH>
 __global__ __launch_bounds__(kThreads, 3) void pw_kernel(const half_t* __restrict__ x,
                                                          const half_t* __restrict__ wf,
                                                          const half_t* __restrict__ bias,
@@ -197,17 +205,33 @@ __global__ __launch_bounds__(kThreads, 3) void pw_kernel(const half_t* __restric
       const int it = ptid + 128 * k;
       po[k] = (it & 7) + 8 * ((it >> 4) & 1);
       cq[k] = ((it >> 3) & 1) + 2 * (it >> 5);
-      pix_ok[k] = p0 + 8 * po[k] < P;  // P % 8 == 0: an octet is all in or all out
-      xs[k] = x + ((n * cp.C + (int64_t)g * cp.Cg) * P + p0 + 8 * po[k]);
+      const int64_t pp = p0 + 8 * po[k];
+      pix_ok[k] = pp < P;  // P (and OW for a patch conv) % 8 == 0: an octet is all in or all out
+      const half_t* img = x + (n * cp.C + (int64_t)g * cp.Cg) * cp.in_sz;
+      if constexpr (PATCH == 1) {
+        xs[k] = img + pp;
+      } else {  // first input column of the octet's 2x2 patches in input row 2*oh
+        const int64_t oh = pp / cp.OW, ow = pp - oh * cp.OW;
+        xs[k] = img + (2 * oh) * cp.W + 2 * ow;
+      }
     }
+    // 1x1: loads j = channels 4*cq + j of the step, 8 pixels each.  2x2: the
+    // item is input channel st*16 + cq; loads j = (input row 2*oh + j/2,
+    // columns 8*(j%2) .. +7 of the octet's 16)
     auto load_x = [&](int st, half8 (*v)[4]) __attribute__((always_inline)) {
 #pragma unroll
       for (int k = 0; k < 2; ++k)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int c = st * kBK + 4 * cq[k] + j;
-          const bool ok = pix_ok[k] && c < cp.Cg;
-          v[k][j] = *(const half8*)(ok ? xs[k] + (int64_t)c * P : x);
+          if constexpr (PATCH == 1) {
+            const int c = st * kBK + 4 * cq[k] + j;
+            const bool ok = pix_ok[k] && c < cp.Cg;
+            v[k][j] = *(const half8*)(ok ? xs[k] + (int64_t)c * P : x);
+          } else {
+            const int c = st * (kBK / 4) + cq[k];
+            const bool ok = pix_ok[k] && c < cp.Cg;
+            v[k][j] = *(const half8*)(ok ? xs[k] + (int64_t)c * cp.in_sz + (j >> 1) * cp.W + (j & 1) * 8 : x);
+          }
         }
     };
     auto store_x = [&](int st, half8 (*v)[4]) __attribute__((always_inline)) {
@@ -215,10 +239,24 @@ __global__ __launch_bounds__(kThreads, 3) void pw_kernel(const half_t* __restric
       for (int k = 0; k < 2; ++k) {
         // row 8*po + e, bytes 8*cq .. +7 of the row's channels, swizzled
         half_t* dst = lds + (st & 1) * kStage + (8 * po[k]) * kLDC + ((8 * cq[k]) ^ ((po[k] & 7) << 4)) / 2;
-        const int cvalid = cp.Cg - st * kBK - 4 * cq[k];
         half8 u[4];
+        if constexpr (PATCH == 1) {
+          const int cvalid = cp.Cg - st * kBK - 4 * cq[k];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) u[j] = pix_ok[k] && j < cvalid ? v[k][j] : half8{};
+          for (int j = 0; j < 4; ++j) u[j] = pix_ok[k] && j < cvalid ? v[k][j] : half8{};
+        } else {
+          // reduction rows (kh, kw) = (0,0), (0,1), (1,0), (1,1): even and odd
+          // columns of the two input rows
+          const bool ok = pix_ok[k] && st * (kBK / 4) + cq[k] < cp.Cg;
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) {
+            const half8 a = v[k][2 * kh], b = v[k][2 * kh + 1];
+            const half8 ev = {a[0], a[2], a[4], a[6], b[0], b[2], b[4], b[6]};
+            const half8 od = {a[1], a[3], a[5], a[7], b[1], b[3], b[5], b[7]};
+            u[2 * kh] = ok ? ev : half8{};
+            u[2 * kh + 1] = ok ? od : half8{};
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           *(half4*)(dst + e * kLDC) = half4{u[0][e], u[1][e], u[2][e], u[3][e]};
@@ -326,19 +364,33 @@ __global__ __launch_bounds__(kThreads, 3) void pw_kernel(const half_t* __restric
   }
 }
 
+// PATCH 1: kernel 1, stride 1, no padding.  PATCH 2: 2-D, kernel 2x2, stride
+// 2, dilation 1, no padding, OW % 8 == 0 and W % 8 == 0 (16-byte row pieces).
+int patch_of(const ConvParams& cp) {
+  const bool nopad = cp.pd == 0 && cp.ph == 0 && cp.pw == 0;
+  if (cp.KD == 1 && cp.KH == 1 && cp.KW == 1 && cp.sd == 1 && cp.sh == 1 && cp.sw == 1 && nopad &&
+      cp.OD == cp.D && cp.OH == cp.H && cp.OW == cp.W)
+    return 1;
+  if (cp.D == 1 && cp.KD == 1 && cp.KH == 2 && cp.KW == 2 && cp.sh == 2 && cp.sw == 2 &&
+      cp.dh == 1 && cp.dw == 1 && nopad && cp.OH == cp.H / 2 && cp.OW == cp.W / 2 &&
+      cp.OW % 8 == 0 && cp.W % 8 == 0)
+    return 2;
+  return 0;
+}
+
 bool choose(const ConvParams& cp, int32_t dtype, PwTile& pt) {
   if (dtype != FUSEDCONV_F16) return false;
-  if (cp.KD != 1 || cp.KH != 1 || cp.KW != 1 || cp.sd != 1 || cp.sh != 1 || cp.sw != 1) return false;
-  if (cp.pd != 0 || cp.ph != 0 || cp.pw != 0) return false;
-  if (cp.OD != cp.D || cp.OH != cp.H || cp.OW != cp.W) return false;  // no end padding either
-  if (cp.Cg % 8 != 0 || cp.Cg < 16) return false;
+  const int patch = patch_of(cp);
+  if (patch == 0) return false;
+  pt.kp = cp.Cg * patch * patch;
+  if (pt.kp % 8 != 0 || pt.kp < 16) return false;
   pt.P = cp.out_sz;
   if (pt.P % 8 != 0) return false;
   // epilogue offsets: 64 channel planes of one image in 31-bit byte offsets
   if (pt.P * 64 * 2 >= ((int64_t)1 << 31)) return false;
   pt.ntile = (int)cdiv(pt.P, kBN);
   pt.nmb = (int)cdiv(cp.Mg, kBM);
-  pt.ks = (int)cdiv(cp.Cg, kBK);
+  pt.ks = (int)cdiv(pt.kp, kBK);
   pt.tiles = (int64_t)cp.G * cp.n * pt.ntile;
   const int64_t blocks = cdiv(pt.tiles, 8) * 8 * pt.nmb;
   return blocks < ((int64_t)1 << 31);
@@ -367,27 +419,27 @@ int FC_CAT(launch_pointwise_act_, FC_ACT)(const Geometry& g, const RunArgs& a) {
     const int rc = launch_repack(g.cp, pt, a);
     if (rc != FUSEDCONV_OK) return rc;
   }
-  const void* kfn = (const void*)pw_kernel<FC_ACT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds) != hipSuccess)
-      return FUSEDCONV_ERR_LAUNCH;
-    attr_set = true;
-  }
   const int64_t blocks = cdiv(pt.tiles, 8) * 8 * pt.nmb;
-  hipLaunchKernelGGL(pw_kernel<FC_ACT>, dim3((unsigned)blocks), dim3(kThreads), kLds,
-                     (hipStream_t)a.stream, (const half_t*)a.x, (const half_t*)a.ws,
-                     (const half_t*)a.bias, (const half_t*)a.z, (half_t*)a.y, g.cp, pt);
+  if (patch_of(g.cp) == 1) {
+    hipLaunchKernelGGL((pw_kernel<FC_ACT, 1>), dim3((unsigned)blocks), dim3(kThreads), kLds,
+                       (hipStream_t)a.stream, (const half_t*)a.x, (const half_t*)a.ws,
+                       (const half_t*)a.bias, (const half_t*)a.z, (half_t*)a.y, g.cp, pt);
+  } else {
+    hipLaunchKernelGGL((pw_kernel<FC_ACT, 2>), dim3((unsigned)blocks), dim3(kThreads), kLds,
+                       (hipStream_t)a.stream, (const half_t*)a.x, (const half_t*)a.ws,
+                       (const half_t*)a.bias, (const half_t*)a.z, (half_t*)a.y, g.cp, pt);
+  }
   return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
 }
 
 #if FC_ACT == 0
 FC_ACT_DECLS(launch_pointwise_act_)
 
-bool pointwise_fits(const ConvParams& cp, int32_t dtype, size_t* workspace) {
+bool pointwise_fits(const ConvParams& cp, int32_t dtype, size_t* workspace, int32_t* patch) {
   PwTile pt;
   if (!choose(cp, dtype, pt)) return false;
   if (workspace) *workspace = (size_t)cp.G * pt.nmb * pt.ks * kFragHalves * sizeof(half_t);
+  if (patch) *patch = patch_of(cp);
   return true;
 }
 

@@ -95,8 +95,9 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
   if (route == FUSEDCONV_ROUTE_AUTO) {
     if (split_req > 1) route = FUSEDCONV_ROUTE_IGEMM;
     else if (cp.Cg == 1 && depthwise_fits(cp, th, tw)) route = FUSEDCONV_ROUTE_DEPTHWISE;
-    // 1x1: the pointwise GEMM (measured on MI355X against the halo route:
-    // C/group 512 2.6x faster, 256 8-9%, 128 on par)
+    // 1x1, and 2x2 with stride 2: the pointwise GEMM (measured on MI355X
+    // against the halo route: 1x1 at C/group 512 2.6x faster, 256 8-9%, 128 on
+    // par)
     else if (pointwise_fits(cp, g.dtype)) route = FUSEDCONV_ROUTE_POINTWISE;
     else if (igemm_halo_fits(cp, g.dtype, th, tw, halo_ws)) route = FUSEDCONV_ROUTE_IGEMM_HALO;
     else if (smallc_fits(cp, g.dtype, th, tw, halo_ws)) route = FUSEDCONV_ROUTE_SMALLC;
@@ -157,14 +158,16 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
       snprintf(p.name, sizeof(p.name), "smallc_f16_t%dx%d", th, tw);
       return FUSEDCONV_OK;
     case FUSEDCONV_ROUTE_POINTWISE:
-      if (!pointwise_fits(cp, g.dtype, &halo_ws)) {
-        err = "POINTWISE needs fp16, kernel 1, stride 1, no padding, C/group % 8 == 0, "
-              "C/group >= 16 and a pixel count per image that is a multiple of 8";
+      if (!pointwise_fits(cp, g.dtype, &halo_ws, &bm)) {
+        err = "POINTWISE needs fp16, no padding, and either kernel 1 with stride 1 or a 2-D "
+              "2x2 kernel with stride 2 (OW and W multiples of 8); C/group * taps a multiple "
+              "of 8 and >= 16, and a pixel count per image that is a multiple of 8";
         return FUSEDCONV_ERR_ROUTE;
       }
       p.route = route;
       p.workspace = halo_ws;
-      snprintf(p.name, sizeof(p.name), "pointwise_f16_m128_n128");
+      if (bm == 2) snprintf(p.name, sizeof(p.name), "pointwise_f16_patch2x2_m128_n128");
+      else snprintf(p.name, sizeof(p.name), "pointwise_f16_m128_n128");
       return FUSEDCONV_OK;
     default:
       err = "unknown route";

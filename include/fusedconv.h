@@ -65,7 +65,10 @@ typedef enum fusedconv_dtype {
  *              FusedConv README's implicit GEMM with one tap, X itself the
  *              reduction operand): needs kernel 1, stride 1, no padding,
  *              C/group % 8 == 0, C/group >= 16 and a pixel count per image
- *              that is a multiple of 8.
+ *              that is a multiple of 8.  Also 2-D 2x2 convolutions with
+ *              stride 2, dilation 1 and no padding (patch embeddings,
+ *              downsampling) whose W and OW are multiples of 8, with
+ *              C/group even and >= 4.
  */
 typedef enum fusedconv_route {
   FUSEDCONV_ROUTE_AUTO = 0,

@@ -221,7 +221,14 @@ def test_pointwise_route_limits():
         dict(x=[1, 8, 16, 16], w=[64, 8, 1, 1], dtype="f16"),                       # C/group < 16
         dict(x=[1, 64, 14, 14], w=[64, 64, 1, 1], dtype="f16"),                     # 196 pixels
         dict(x=[1, 64, 16, 16], w=[64, 64, 3, 3], dtype="f16"),                     # 3x3
+        dict(x=[1, 64, 12, 12], w=[64, 64, 2, 2], strides=[2, 2], dtype="f16"),     # OW 6
+        dict(x=[1, 64, 16, 16], w=[64, 64, 2, 2], strides=[2, 2], pads=[1, 1, 1, 1], dtype="f16"),
+        dict(x=[1, 64, 16, 16], w=[64, 64, 2, 2], strides=[1, 1], dtype="f16"),     # stride 1
+        dict(x=[1, 64, 16, 16], w=[64, 64, 2, 2], strides=[2, 2], dilations=[2, 2], dtype="f16"),
     ]
+    # 2x2 convs with stride 2 (OW 8, W 16 here) take it too
+    h = _h([1, 64, 16, 16], [64, 64, 2, 2], strides=[2, 2], dtype="f16")
+    assert h.route == "pointwise" and h.kernel_name == "pointwise_f16_patch2x2_m128_n128"
     for c in refused:
         c = dict(c)
         with pytest.raises(B.FusedConvError) as e:

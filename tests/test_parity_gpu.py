@@ -470,6 +470,12 @@ POINTWISE_CASES = [
     ([1, 32, 4, 8, 8], [48, 32, 1, 1, 1], {}),              # 3-D
     ([1, 16, 8, 8], [32, 16, 1, 1], dict(dilations=[2, 2])),  # C/group 16; dilation is moot
     ([1, 1024, 8, 8], [64, 1024, 1, 1], {}),                # 16 steps
+    # 2x2 with stride 2 (patch form): reduction k = c*4 + kh*2 + kw
+    ([2, 64, 32, 32], [96, 64, 2, 2], dict(strides=[2, 2])),            # 256 pixels, 4 steps
+    ([1, 40, 20, 48], [64, 40, 2, 2], dict(strides=[2, 2])),            # 240 pixels; 2.5 steps
+    ([2, 16, 17, 16], [32, 16, 2, 2], dict(strides=[2, 2])),            # odd H (last row unused)
+    ([1, 32, 16, 16], [32, 8, 2, 2], dict(strides=[2, 2], group=4)),    # groups, C/group 8
+    ([1, 128, 32, 64], [256, 128, 2, 2], dict(strides=[2, 2])),         # 2 m blocks, 8 steps
 ]
 
 
