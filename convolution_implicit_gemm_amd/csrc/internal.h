@@ -98,8 +98,8 @@ bool smallc_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32_t& 
                  size_t& workspace);
 // Pointwise route (kernels_pointwise.hip), fp16: 1x1 with stride 1, or 2x2
 // with stride 2 (patch 2), no padding; optionally the bytes of its
-// repacked-weight workspace and the patch size.
+// repacked-weight workspace, the patch size and the block's output channels.
 bool pointwise_fits(const ConvParams& cp, int32_t dtype, size_t* workspace = nullptr,
-                    int32_t* patch = nullptr);
+                    int32_t* patch = nullptr, int32_t* block_m = nullptr);
 
 }  // namespace fc

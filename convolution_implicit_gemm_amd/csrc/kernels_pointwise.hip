@@ -4,9 +4,10 @@
 // the FusedConv README with a single tap, where im2col is the identity and X
 // itself is the [C/group x pixels] operand.
 //
-// GEMM view per block: rows = 128 pixels of one image, columns = 128 output
-// channels of one group, reduction over the group's input channels in steps
-// of 64.  NCHW stores pixels, not channels, consecutively, while the MFMA
+// GEMM view per block: rows = 128 pixels of one image, columns = 64*NWM
+// output channels of one group (128, or 256 when M/group > 128: X is then
+// streamed once per pixel tile), reduction over the group's input channels in
+// steps of 64.  NCHW stores pixels, not channels, consecutively, while the MFMA
 // operand of a lane is 8 consecutive reduction elements, so X is transposed
 // on its way into LDS:
 //   * two producer waves stream X: a thread loads 4 channels x 8 pixels
@@ -22,7 +23,7 @@
 //     completes in issue order, so a wave that waited for a weight load
 //     issued after long X loads would wait for those too; with the roles
 //     split, the producers wait only for X and the MFMA waves only for W;
-//   * four MFMA waves read the weights, one step ahead, from a copy of W
+//   * 2*NWM MFMA waves read the weights, one step ahead, from a copy of W
 //     repacked in fragment order (fusedconv_prepare_weights, or at the start
 //     of every run): each 16-byte lane piece of an operand is contiguous
 //     with its neighbours', zero past C/group and M/group, as register
@@ -51,9 +52,7 @@
 namespace fc {
 namespace {
 
-constexpr int kThreads = 384;  // 4 MFMA waves + 2 producer waves
 constexpr int kBN = 128;    // pixels per block
-constexpr int kBM = 128;    // output channels per block
 constexpr int kBK = 64;     // input channels per reduction step
 constexpr int kLDC = kBK + 16;  // LDS row pitch in halves (160 bytes)
 constexpr int kStage = kBN * kLDC;  // halves per LDS stage
@@ -74,27 +73,28 @@ struct PwTile {
   int ntile;       // pixel tiles per image
   int nmb;         // output-channel blocks per group
   int ks;          // reduction steps: ceil(kp / 64)
+  int nwm;         // MFMA waves along the output channels: 2 (128 per block) or 4 (256)
   int64_t tiles;   // G * n * ntile
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Weights in fragment order: Wf[((((g*nmb + mb)*ks + s)*2 + kk)*4 + j)*2 + wmi]
+// Weights in fragment order: Wf[((((g*nmb + mb)*ks + s)*2 + kk)*4 + j)*nwm + wmi]
 // [lane][e] = W[g*Mg + m][k] (W as [M][C/group * taps], its memory order) with
-// m = mb*128 + wmi*64 + j*16 + lane%16 and k = s*64 + kk*32 + (lane/16)*8 + e;
+// m = mb*64*nwm + wmi*64 + j*16 + lane%16 and k = s*64 + kk*32 + (lane/16)*8 + e;
 // zero for m >= M/group or k >= C/group * taps.
-constexpr int kFragHalves = 2 * 4 * 2 * 64 * 8;  // halves per (group, m block, step)
+constexpr int kFragPerWave = 2 * 4 * 64 * 8;  // halves per (group, m block, step, wave)
 __global__ __launch_bounds__(256) void repack_frag_kernel(const half_t* __restrict__ w,
                                                           half_t* __restrict__ wf, ConvParams cp,
                                                           PwTile pt) {
-  const int64_t total = (int64_t)cp.G * pt.nmb * pt.ks * kFragHalves;
+  const int64_t total = (int64_t)cp.G * pt.nmb * pt.ks * kFragPerWave * pt.nwm;
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
     const int e = (int)(i & 7);
     const int lane = (int)((i >> 3) & 63);
     int64_t t = i >> 9;
-    const int wmi = (int)(t & 1);
-    t >>= 1;
+    const int wmi = (int)(t % pt.nwm);
+    t /= pt.nwm;
     const int j = (int)(t & 3);
     t >>= 2;
     const int kk = (int)(t & 1);
@@ -103,19 +103,20 @@ __global__ __launch_bounds__(256) void repack_frag_kernel(const half_t* __restri
     t /= pt.ks;
     const int mb = (int)(t % pt.nmb);
     const int g = (int)(t / pt.nmb);
-    const int m = mb * kBM + wmi * 64 + j * 16 + (lane & 15);
+    const int m = mb * 64 * pt.nwm + wmi * 64 + j * 16 + (lane & 15);
     const int c = s * kBK + kk * 32 + (lane >> 4) * 8 + e;
     wf[i] = (m < cp.Mg && c < pt.kp) ? w[((int64_t)g * cp.Mg + m) * pt.kp + c] : (half_t)0;
   }
 }
 
-// Two blocks per CU: 12 waves, 3 per SIMD (the launch bound), 168 VGPRs each.
+// NWM 2: two blocks of 6 waves per CU; NWM 4: one block of 10 waves; either way
+// at most 3 waves per SIMD (the launch bound), 168 VGPRs each.
 // Block b -> (pixel tile, channel block).  Blocks are dealt to the 8 XCDs
 // round-robin, so the channel blocks of one pixel tile are placed 8 blocks
 // apart: they run on the same XCD at about the same time and all but the
 // first read X from that XCD's L2.
-template <int ACT, int PATCH>
-__global__ __launch_bounds__(kThreads, 3) void pw_kernel(const half_t* __restrict__ x,
+template <int ACT, int PATCH, int NWM>
+__global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t* __restrict__ x,
                                                          const half_t* __restrict__ wf,
                                                          const half_t* __restrict__ bias,
                                                          const half_t* z, half_t* y,
@@ -131,7 +132,8 @@ __global__ __launch_bounds__(kThreads, 3) void pw_kernel(const half_t* __restric
   const int g = (int)(gn / cp.n);
   const int64_t P = pt.P;
   const int64_t p0 = (int64_t)tile * kBN;
-  const int m0 = mb * kBM;
+  constexpr int BM = 64 * NWM;
+  const int m0 = mb * BM;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -140,13 +142,14 @@ __global__ __launch_bounds__(kThreads, 3) void pw_kernel(const half_t* __restric
 
   // ---- weight fragments of step s: channel tile j, reduction half kk, one
   // contiguous 1 KB piece of Wf per (step, kk, j, wave) and 16 bytes per lane
-  const half_t* wfb = wf + ((int64_t)g * pt.nmb + mb) * pt.ks * kFragHalves + wmi * 512 + lane * 8;
+  constexpr int kFrag = kFragPerWave * NWM;  // halves per (group, m block, step)
+  const half_t* wfb = wf + ((int64_t)g * pt.nmb + mb) * pt.ks * kFrag + wmi * 512 + lane * 8;
   auto load_w = [&](int s, half8 (*f)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        f[j][kk] = *(const half8*)(wfb + (int64_t)s * kFragHalves + (kk * 4 + j) * 1024);
+        f[j][kk] = *(const half8*)(wfb + (int64_t)s * kFrag + (kk * 4 + j) * (NWM * 512));
   };
 
   // ---- accumulators start at the bias (lane column r16 = channel
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(kThreads, 3) void pw_kernel(const half_t* __restric
   };
 
   const int ks = pt.ks;
-  if (wave >= 4) {
+  if (wave >= 2 * NWM) {
     // ---- producer: items it = ptid and ptid + 128 of each step, item it =
     // (channel quad cq, pixel octet po) with po = (it & 7) + 8*((it >> 4) & 1),
     // cq = ((it >> 3) & 1) + 2*(it >> 5): channels 4*cq .. +3 of the step,
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(kThreads, 3) void pw_kernel(const half_t* __restric
     // Invalid pieces read x[0..7] (unconditional loads) and are written as
     // zeros.  Step s: write X(s) into stage s&1, barrier, load X(s+3)
     // (clamped to the last step) into the freed set.
-    const int ptid = tid - 256;
+    const int ptid = tid - 128 * NWM;
     int cq[2], po[2];
     bool pix_ok[2];
     const half_t* xs[2];
@@ -389,7 +392,8 @@ bool choose(const ConvParams& cp, int32_t dtype, PwTile& pt) {
   // epilogue offsets: 64 channel planes of one image in 31-bit byte offsets
   if (pt.P * 64 * 2 >= ((int64_t)1 << 31)) return false;
   pt.ntile = (int)cdiv(pt.P, kBN);
-  pt.nmb = (int)cdiv(cp.Mg, kBM);
+  pt.nwm = cp.Mg > 128 ? 4 : 2;
+  pt.nmb = (int)cdiv(cp.Mg, 64 * pt.nwm);
   pt.ks = (int)cdiv(pt.kp, kBK);
   pt.tiles = (int64_t)cp.G * cp.n * pt.ntile;
   const int64_t blocks = cdiv(pt.tiles, 8) * 8 * pt.nmb;
@@ -397,7 +401,7 @@ bool choose(const ConvParams& cp, int32_t dtype, PwTile& pt) {
 }
 
 int launch_repack(const ConvParams& cp, const PwTile& pt, const RunArgs& a) {
-  const int64_t total = (int64_t)cp.G * pt.nmb * pt.ks * kFragHalves;
+  const int64_t total = (int64_t)cp.G * pt.nmb * pt.ks * kFragPerWave * pt.nwm;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(repack_frag_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)a.stream,
@@ -420,14 +424,17 @@ int FC_CAT(launch_pointwise_act_, FC_ACT)(const Geometry& g, const RunArgs& a) {
     if (rc != FUSEDCONV_OK) return rc;
   }
   const int64_t blocks = cdiv(pt.tiles, 8) * 8 * pt.nmb;
-  if (patch_of(g.cp) == 1) {
-    hipLaunchKernelGGL((pw_kernel<FC_ACT, 1>), dim3((unsigned)blocks), dim3(kThreads), kLds,
-                       (hipStream_t)a.stream, (const half_t*)a.x, (const half_t*)a.ws,
-                       (const half_t*)a.bias, (const half_t*)a.z, (half_t*)a.y, g.cp, pt);
+  const bool p1 = patch_of(g.cp) == 1;
+  const half_t *x = (const half_t*)a.x, *wf = (const half_t*)a.ws, *b = (const half_t*)a.bias,
+               *z = (const half_t*)a.z;
+  half_t* y = (half_t*)a.y;
+  const hipStream_t st = (hipStream_t)a.stream;
+  if (pt.nwm == 2) {
+    if (p1) hipLaunchKernelGGL((pw_kernel<FC_ACT, 1, 2>), dim3((unsigned)blocks), dim3(384), kLds, st, x, wf, b, z, y, g.cp, pt);
+    else hipLaunchKernelGGL((pw_kernel<FC_ACT, 2, 2>), dim3((unsigned)blocks), dim3(384), kLds, st, x, wf, b, z, y, g.cp, pt);
   } else {
-    hipLaunchKernelGGL((pw_kernel<FC_ACT, 2>), dim3((unsigned)blocks), dim3(kThreads), kLds,
-                       (hipStream_t)a.stream, (const half_t*)a.x, (const half_t*)a.ws,
-                       (const half_t*)a.bias, (const half_t*)a.z, (half_t*)a.y, g.cp, pt);
+    if (p1) hipLaunchKernelGGL((pw_kernel<FC_ACT, 1, 4>), dim3((unsigned)blocks), dim3(640), kLds, st, x, wf, b, z, y, g.cp, pt);
+    else hipLaunchKernelGGL((pw_kernel<FC_ACT, 2, 4>), dim3((unsigned)blocks), dim3(640), kLds, st, x, wf, b, z, y, g.cp, pt);
   }
   return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
 }
@@ -435,11 +442,13 @@ int FC_CAT(launch_pointwise_act_, FC_ACT)(const Geometry& g, const RunArgs& a) {
 #if FC_ACT == 0
 FC_ACT_DECLS(launch_pointwise_act_)
 
-bool pointwise_fits(const ConvParams& cp, int32_t dtype, size_t* workspace, int32_t* patch) {
+bool pointwise_fits(const ConvParams& cp, int32_t dtype, size_t* workspace, int32_t* patch,
+                    int32_t* block_m) {
   PwTile pt;
   if (!choose(cp, dtype, pt)) return false;
-  if (workspace) *workspace = (size_t)cp.G * pt.nmb * pt.ks * kFragHalves * sizeof(half_t);
+  if (workspace) *workspace = (size_t)cp.G * pt.nmb * pt.ks * kFragPerWave * pt.nwm * sizeof(half_t);
   if (patch) *patch = patch_of(cp);
+  if (block_m) *block_m = 64 * pt.nwm;
   return true;
 }
 

@@ -91,7 +91,8 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
   }
   int32_t th = 0, tw = 0;
   size_t halo_ws = 0;
-  int32_t bm = 0;  // halo route: output channels per block
+  int32_t bm = 0;  // halo and pointwise routes: output channels per block
+  int32_t patch = 1;  // pointwise route: 1 (1x1) or 2 (2x2 with stride 2)
   if (route == FUSEDCONV_ROUTE_AUTO) {
     if (split_req > 1) route = FUSEDCONV_ROUTE_IGEMM;
     else if (cp.Cg == 1 && depthwise_fits(cp, th, tw)) route = FUSEDCONV_ROUTE_DEPTHWISE;
@@ -158,7 +159,7 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
       snprintf(p.name, sizeof(p.name), "smallc_f16_t%dx%d", th, tw);
       return FUSEDCONV_OK;
     case FUSEDCONV_ROUTE_POINTWISE:
-      if (!pointwise_fits(cp, g.dtype, &halo_ws, &bm)) {
+      if (!pointwise_fits(cp, g.dtype, &halo_ws, &patch, &bm)) {
         err = "POINTWISE needs fp16, no padding, and either kernel 1 with stride 1 or a 2-D "
               "2x2 kernel with stride 2 (OW and W multiples of 8); C/group * taps a multiple "
               "of 8 and >= 16, and a pixel count per image that is a multiple of 8";
@@ -166,8 +167,8 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
       }
       p.route = route;
       p.workspace = halo_ws;
-      if (bm == 2) snprintf(p.name, sizeof(p.name), "pointwise_f16_patch2x2_m128_n128");
-      else snprintf(p.name, sizeof(p.name), "pointwise_f16_m128_n128");
+      snprintf(p.name, sizeof(p.name), "pointwise_f16_%sm%d_n128", patch == 2 ? "patch2x2_" : "",
+               (int)bm);
       return FUSEDCONV_OK;
     default:
       err = "unknown route";

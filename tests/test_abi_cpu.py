@@ -211,6 +211,9 @@ def test_pointwise_route_limits():
     # fragment-ordered weights: 1 group x 1 m block x 8 steps x 8192 halves
     assert h.route == "pointwise" and h.workspace_bytes == 8 * 8192 * 2
     assert _h([2, 256, 8, 8], [64, 256, 1, 1], dtype="f16").route == "pointwise"
+    # more than 128 channels per group: blocks of 256 (4 MFMA waves along M)
+    h = _h([2, 64, 8, 8], [200, 64, 1, 1], dtype="f16")
+    assert h.kernel_name == "pointwise_f16_m256_n128" and h.workspace_bytes == 1 * 16384 * 2
     assert _h([2, 256, 8, 8], [64, 256, 1, 1], dtype="f16", strides=[2, 2]).route != "pointwise"
     refused = [
         dict(x=[1, 64, 16, 16], w=[64, 64, 1, 1], dtype="f32"),                     # fp32
