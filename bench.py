@@ -69,7 +69,7 @@ def bound_of(wl, flop, nbytes):
 KERNEL_SOURCES = {"halo_kernel": "kernels_halo.hip", "dw_fast_kernel": "kernels_depthwise.hip",
                   "depthwise_kernel": "kernels_depthwise.hip", "igemm_kernel": "kernels_igemm.hip",
                   "direct_kernel": "kernels_direct.hip", "smallc_kernel": "kernels_smallc.hip",
-                  "dwm_kernel": "kernels_dwmfma.hip"}
+                  "dwm_kernel": "kernels_dwmfma.hip", "pw_kernel": "kernels_pointwise.hip"}
 
 
 def sources_hash(kernel_pat):
