@@ -100,25 +100,23 @@ __device__ __forceinline__ int phase_index(int a, int s, int n) {
 __global__ __launch_bounds__(kThreads) void repack_w_kernel(const half_t* __restrict__ w,
                                                             half_t* __restrict__ wp,
                                                             ConvParams cp, int ncb, int mgp) {
-  // one thread per 8-channel piece of a Wp row: 8 reads of W (a stride of
-  // `taps` apart, cached), one 16-byte store; 32-bit index arithmetic
-  const int total = cp.G * cp.taps * ncb * mgp * (kCB / 8);
+  // one thread per (group, row m, channel c): it reads the `taps` weights of
+  // (m, c), which are contiguous in W and follow those of (m, c - 1), so a
+  // wave reads one contiguous run; it writes one half per tap, and the
+  // threads of consecutive channels write consecutive halves of a Wp row.
+  // 32-bit index arithmetic.
+  const int cpad = ncb * kCB;
+  const int total = cp.G * mgp * cpad;
   for (int i = blockIdx.x * kThreads + threadIdx.x; i < total; i += gridDim.x * kThreads) {
-    const int c8 = i & (kCB / 8 - 1);
-    int r = i / (kCB / 8);
+    const int c = i % cpad;
+    int r = i / cpad;
     const int m = r % mgp;
-    r /= mgp;
-    const int cb = r % ncb;
-    r /= ncb;
-    const int t = r % cp.taps;
-    const int g = r / cp.taps;
-    const int c0 = cb * kCB + c8 * 8;
-    const half_t* src = w + ((int64_t)(g * cp.Mg + m) * cp.Cg + c0) * cp.taps + t;
-    half8 v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      v[e] = (c0 + e < cp.Cg && m < cp.Mg) ? src[e * cp.taps] : (half_t)0;
-    *(half8*)(wp + (int64_t)i * 8) = v;
+    const int g = r / mgp;
+    const bool ok = c < cp.Cg && m < cp.Mg;
+    const half_t* src = w + ((int64_t)(g * cp.Mg + (ok ? m : 0)) * cp.Cg + (ok ? c : 0)) * cp.taps;
+    half_t* dst = wp + (((int64_t)g * cp.taps * ncb + c / kCB) * mgp + m) * kCB + c % kCB;
+    for (int t = 0; t < cp.taps; ++t)
+      dst[(int64_t)t * ncb * mgp * kCB] = ok ? src[t] : (half_t)0;
   }
 }
 
@@ -684,7 +682,7 @@ bool choose(const ConvParams& cp, Choice& ch) {
 }
 
 int launch_repack(const ConvParams& cp, const Choice& ch, const RunArgs& a) {
-  const int64_t total = (int64_t)cp.G * cp.taps * ch.ht.ncb * ch.ht.mgp * (kCB / 8);
+  const int64_t total = (int64_t)cp.G * ch.ht.ncb * ch.ht.mgp * kCB;
   int64_t rblocks = (total + kThreads - 1) / kThreads;
   if (rblocks > 4096) rblocks = 4096;
   hipLaunchKernelGGL(repack_w_kernel, dim3((unsigned)rblocks), dim3(kThreads), 0,
