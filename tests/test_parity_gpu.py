@@ -516,6 +516,38 @@ def test_prepared_weights_match_plain_run(route):
     assert torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("route", ["igemm_halo", "pointwise"])
+def test_graph_replay_matches_eager(route):
+    """A captured call (weight preparation + convolution, as bench.py times
+    it) replayed several times, with eager work and synchronizations between
+    the replays, gives the eager result every time."""
+    k = 1 if route == "pointwise" else 3
+    xs, ws = [4, 64, 16, 16], [96, 64, k, k]
+    x, w, b, z = random_tensors([8200, k], "f16", xs, ws, [96], [4, 96, 16, 16], dist="normal",
+                                w_std=0.05)
+    attrs = dict(pads=[1, 1, 1, 1] if k == 3 else [0, 0, 0, 0], activation="QuickGelu",
+                 activation_params=f32params([1.702]), route=route)
+    op = fc.FusedConv(xs, ws, "f16", True, True, **attrs)
+    xd, wd, bd, zd = dev(x), dev(w), dev(b), dev(z)
+    ws_t = torch.empty(max(op.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    log(f"CASE graph replay route={route}")
+    ref = op(xd, wd, bd, zd, workspace=ws_t)
+    torch.cuda.synchronize()
+    y = torch.empty_like(ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        op.prepare_weights(wd, ws_t)
+        op(xd, wd, bd, zd, out=y, workspace=ws_t, weights_prepared=True)
+    for rep in range(4):
+        y.zero_()
+        other = op(xd, wd, bd, zd, workspace=ws_t)  # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), f"replay {rep}"
+        assert torch.equal(other, ref)
+
+
 def test_run_errors_on_device():
     h = B.Handle("f32", [1, 3, 8, 8], [4, 3, 3, 3], None, None)
     x = torch.zeros(1 * 3 * 8 * 8 + 4, device="cuda")
