@@ -6,6 +6,9 @@ shares no code with the HIP library (see the header of fusedconv_oracle.c).
 
 All inputs are converted to float64 exactly (float16 and float32 values are
 representable in double), and results come back as float64 arrays.
+conv_transpose() (the transposed convolution) is written here in numpy,
+float64, and pinned in the tests against torch's CPU routine, the adjoint
+identity with fusedconv() and a closed form.
 Attribute conventions follow the FusedConv README "Attributes" table:
 ``pads`` in ONNX order [begins..., ends...], ``strides``/``dilations`` one
 entry per spatial axis, ``auto_pad`` one of NOTSET/SAME_UPPER/SAME_LOWER/VALID.
@@ -168,3 +171,65 @@ def activation(name, v, params=None):
     lib.oracle_activation_array(act_id(name), rp, len(prm), vp, va.size,
                                 out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     return out.reshape(np.shape(v))
+
+
+def conv_transpose(x, w, b=None, z=None, *, group=1, strides=None, dilations=None, pads=None,
+                   output_padding=None, activation=None, activation_params=None):
+    """Transposed convolution with the FusedConv epilogue, as float64.
+
+    The reading (the pages name the transposed form of aten.convolution, the
+    ExecuTorch conv page's entry point, without writing it out): the adjoint
+    of the cross-correlation that fusedconv() computes.  X is [n, C, in...],
+    W is [C, M/group, k...] (for input channel c of group g = c // (C/group)
+    and output channel g*(M/group) + m), and every input element scatters
+        Y[n, g*(M/group) + m, i*s - pad_begin + k*d] += X[n, c, i] * W[c, m, k]
+    for all kernel taps k; positions outside the output are dropped.  Output
+    size per axis: s*(in - 1) + output_padding + (k - 1)*d + 1 - pad_begin
+    - pad_end.  Then Y = act(Y + B[m] + Z), as in fusedconv().
+
+    Plain loops over groups and taps; each tap is one channel contraction
+    (numpy einsum over the group's input channels) added into the strided
+    output positions it reaches.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    nsp = x.ndim - 2
+    n, C = x.shape[:2]
+    insp = list(x.shape[2:])
+    ksp = list(w.shape[2:])
+    Cg, Mg = C // group, w.shape[1]
+    M = Mg * group
+    s = list(strides) if strides is not None else [1] * nsp
+    d = list(dilations) if dilations is not None else [1] * nsp
+    p = list(pads) if pads is not None else [0] * (2 * nsp)
+    op = list(output_padding) if output_padding is not None else [0] * nsp
+    out = [s[i] * (insp[i] - 1) + op[i] + (ksp[i] - 1) * d[i] + 1 - p[i] - p[nsp + i]
+           for i in range(nsp)]
+    if min(out) < 1:
+        raise ValueError("oracle: output size not positive")
+    # scatter into a buffer that also holds the positions before pad_begin and
+    # past the end, then cut the output window out of it
+    full = [s[i] * (insp[i] - 1) + (ksp[i] - 1) * d[i] + 1 + op[i] for i in range(nsp)]
+    buf = np.zeros([n, M] + full, np.float64)
+    for g in range(group):
+        xg = x[:, g * Cg:(g + 1) * Cg]
+        wg = w[g * Cg:(g + 1) * Cg]
+        for tap in np.ndindex(*ksp):
+            contrib = np.einsum("nc...,cm->nm...", xg, wg[(slice(None), slice(None)) + tap])
+            sl = tuple(slice(tap[i] * d[i], tap[i] * d[i] + s[i] * (insp[i] - 1) + 1, s[i])
+                       for i in range(nsp))
+            buf[(slice(None), slice(g * Mg, (g + 1) * Mg)) + sl] += contrib
+    win = tuple(slice(p[i], p[i] + out[i]) for i in range(nsp))
+    y = buf[(slice(None), slice(None)) + win].copy()
+    if b is not None:
+        y += np.asarray(b, dtype=np.float64).reshape([1, M] + [1] * nsp)
+    if z is not None:
+        y += np.asarray(z, dtype=np.float64)
+    if activation is not None:
+        y = activation_fn(activation, y, activation_params)
+    return y
+
+
+def activation_fn(name, v, params=None):
+    """activation() under a name that conv_transpose's argument does not shadow."""
+    return activation(name, v, params)

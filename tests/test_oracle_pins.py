@@ -402,3 +402,81 @@ def test_points_match_full_output():
     np.testing.assert_array_equal(oracle.fusedconv_at(x, w, b, z, idx=idx, **kw), full.ravel()[idx])
     part = oracle.fusedconv(x, w, b, z, batches=(1, 2), **kw)
     np.testing.assert_array_equal(part, full[1:2])
+
+
+# ---- transposed convolution (oracle.conv_transpose) ------------------------
+
+CONVT_CASES = [
+    # (x shape, w shape [C, M/group, k...], attrs)
+    ([2, 4, 5, 6], [4, 3, 3, 2], dict(strides=[2, 3], pads=[1, 0, 2, 1], dilations=[1, 2],
+                                      output_padding=[1, 2])),
+    ([1, 6, 7], [6, 2, 4], dict(group=3, strides=[2], pads=[1, 2])),
+    ([2, 4, 3, 4, 3], [4, 2, 2, 3, 2], dict(group=2, strides=[1, 2, 2], pads=[0, 1, 0, 1, 0, 1],
+                                           output_padding=[0, 1, 1])),
+    ([1, 3, 4, 4], [3, 5, 2, 2], dict(strides=[2, 2])),                     # patch upsampling
+    ([2, 2, 6], [2, 3, 3], dict(dilations=[3], pads=[2, 1])),
+]
+
+
+def _torch_convt(x, w, group=1, strides=None, dilations=None, pads=None, output_padding=None):
+    """torch's CPU conv_transpose in float64 (symmetric-pad API): run it without
+    padding, then cut [pad_begin, full - pad_end + output_padding), zero past
+    the full extent (where output padding reaches beyond every tap)."""
+    nsp = x.ndim - 2
+    f = {1: F.conv_transpose1d, 2: F.conv_transpose2d, 3: F.conv_transpose3d}[nsp]
+    full = f(torch.from_numpy(x), torch.from_numpy(w), stride=strides or [1] * nsp,
+             dilation=dilations or [1] * nsp, groups=group).numpy()
+    p = pads or [0] * (2 * nsp)
+    op = output_padding or [0] * nsp
+    out = [full.shape[2 + i] - p[i] - p[nsp + i] + op[i] for i in range(nsp)]
+    y = np.zeros(list(full.shape[:2]) + out)
+    src = tuple(slice(p[i], min(full.shape[2 + i], p[i] + out[i])) for i in range(nsp))
+    cut = full[(slice(None), slice(None)) + src]
+    y[(slice(None), slice(None)) + tuple(slice(0, c) for c in cut.shape[2:])] = cut
+    return y
+
+
+@pytest.mark.parametrize("ci", range(len(CONVT_CASES)))
+def test_conv_transpose_matches_torch_fp64(ci):
+    xs, ws, kw = CONVT_CASES[ci]
+    rng = np.random.default_rng([700, ci])
+    x, w = rng.standard_normal(xs), rng.standard_normal(ws)
+    np.testing.assert_allclose(oracle.conv_transpose(x, w, **kw), _torch_convt(x, w, **kw),
+                               rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("ci", range(len(CONVT_CASES)))
+def test_conv_transpose_is_the_adjoint_of_the_conv(ci):
+    # <convT(x; W), y> = <x, conv(y; W)> with W read as a [C, M/group, k] conv weight
+    xs, ws, kw = CONVT_CASES[ci]
+    rng = np.random.default_rng([701, ci])
+    x, w = rng.standard_normal(xs), rng.standard_normal(ws)
+    yt = oracle.conv_transpose(x, w, **kw)
+    y = rng.standard_normal(yt.shape)
+    fw = {k: v for k, v in kw.items() if k in ("group", "strides", "dilations", "pads")}
+    back = oracle.fusedconv(y, w, **fw)
+    assert back.shape == x.shape
+    lhs, rhs = float(np.sum(yt * y)), float(np.sum(x * back))
+    assert abs(lhs - rhs) <= 1e-10 * max(1.0, abs(lhs))
+
+
+def test_conv_transpose_1x1_is_zero_insertion_upsampling():
+    rng = np.random.default_rng(702)
+    x, w = rng.standard_normal([2, 5, 3, 4]), rng.standard_normal([5, 6, 1, 1])
+    y = oracle.conv_transpose(x, w, strides=[3, 2], output_padding=[1, 1])
+    assert y.shape == (2, 6, 8, 8)
+    ref = np.zeros(y.shape)
+    ref[:, :, ::3, ::2][:, :, :3, :4] = np.einsum("ncij,cm->nmij", x, w[:, :, 0, 0])
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-13)
+
+
+def test_conv_transpose_epilogue():
+    rng = np.random.default_rng(703)
+    x, w = rng.standard_normal([1, 4, 3, 3]), rng.standard_normal([4, 2, 2, 2])
+    b = rng.standard_normal([2])
+    core = oracle.conv_transpose(x, w, strides=[2, 2])
+    z = rng.standard_normal(core.shape)
+    y = oracle.conv_transpose(x, w, b, z, strides=[2, 2], activation="LeakyRelu",
+                              activation_params=[0.1])
+    pre = core + b.reshape(1, 2, 1, 1) + z
+    np.testing.assert_allclose(y, np.where(pre >= 0, pre, 0.1 * pre), rtol=0, atol=1e-13)
