@@ -49,6 +49,9 @@ def work(wl, y_shape):
     os_ = int(np.prod(y_shape[2:]))
     K = int(np.prod(wl["w"][1:]))
     flop = 2.0 * n * M * os_ * K
+    if wl["attrs"].get("transposed"):
+        # every X element times M/group outputs and every tap: 2*|X|*(M/group)*prod(k)
+        flop = 2.0 * float(np.prod(wl["x"])) * wl["w"][1] * float(np.prod(wl["w"][2:]))
     esz = 2 if wl["dtype"] == "f16" else 4
     elems = np.prod(wl["x"]) + np.prod(wl["w"]) + np.prod(y_shape)
     if wl["b"]:
@@ -172,6 +175,14 @@ class Runner:
         torch.cuda.synchronize()
         yh = y.cpu().numpy().ravel()
         rng = np.random.default_rng(123)
+        if self.attrs.get("transposed"):
+            # the transposed oracle on the first image, all its outputs
+            kw = {k: v for k, v in self.attrs_oracle().items() if k != "transposed"}
+            z0 = self.inp["z"][:1] if self.inp["z"] is not None else None
+            ref = oracle.conv_transpose(self.inp["x"][:1], self.inp["w"], self.inp["b"], z0,
+                                        **kw).ravel()
+            got = yh[:ref.size].astype(np.float64)
+            return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
         idx = rng.integers(0, yh.size, n_points)
         ref = oracle.fusedconv_at(self.inp["x"], self.inp["w"], self.inp["b"], self.inp["z"],
                                   idx=idx, **self.attrs_oracle())

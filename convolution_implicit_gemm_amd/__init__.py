@@ -28,12 +28,14 @@ class FusedConv:
 
     def __init__(self, x_shape, w_shape, dtype, has_bias=False, has_z=False, **attrs):
         self.attrs = attrs
+        # B has M entries: W.shape[0], or W.shape[1] * group for a transposed conv
+        m = w_shape[1] * attrs.get("group", 1) if attrs.get("transposed") else w_shape[0]
         z_shape = None
         if has_z:
             # Z must have Y's shape; resolve Y first with a probe handle.
-            z_shape = Handle(dtype, x_shape, w_shape, [w_shape[0]] if has_bias else None,
+            z_shape = Handle(dtype, x_shape, w_shape, [m] if has_bias else None,
                              None, **attrs).y_shape
-        self.handle = Handle(dtype, x_shape, w_shape, [w_shape[0]] if has_bias else None,
+        self.handle = Handle(dtype, x_shape, w_shape, [m] if has_bias else None,
                              z_shape, **attrs)
         self.y_shape = self.handle.y_shape
         self.workspace_bytes = self.handle.workspace_bytes
@@ -71,11 +73,15 @@ class FusedConv:
 
 def fused_conv(x, w, bias=None, z=None, *, auto_pad=None, group=1, kernel_shape=None,
                strides=None, dilations=None, pads=None, activation=None,
-               activation_params=None, route="auto", split_k=0):
-    """Y = act(conv(x, w) + bias + z) on the current stream; Y is allocated with torch."""
+               activation_params=None, route="auto", split_k=0, transposed=False,
+               output_padding=None):
+    """Y = act(conv(x, w) + bias + z) on the current stream; Y is allocated with torch.
+    transposed=True: the transposed conv (W as [C, M/group, k...], output_padding)."""
     attrs = dict(auto_pad=auto_pad, group=group, kernel_shape=kernel_shape, strides=strides,
                  dilations=dilations, pads=pads, activation=activation,
                  activation_params=activation_params, route=route, split_k=split_k)
+    if transposed:
+        attrs.update(transposed=True, output_padding=output_padding)
     key = (tuple(x.shape), tuple(w.shape), x.dtype, bias is not None, z is not None,
            tuple((k, tuple(v) if isinstance(v, (list, tuple)) else v)
                  for k, v in sorted(attrs.items())))

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libfusedconv.so")
 MAX_RANK = 8
 F32, F16 = 0, 1
 ROUTES = {"auto": 0, "direct": 1, "igemm": 2, "depthwise": 3, "igemm_halo": 4, "smallc": 5,
-          "pointwise": 6}
+          "pointwise": 6, "transposed": 7}
 ROUTE_NAMES = {v: k for k, v in ROUTES.items()}
 
 STATUS = {
@@ -30,7 +30,8 @@ STATUS = {
 }
 
 # Every symbol include/fusedconv.h declares.
-EXPORTS = ["fusedconv_desc_init", "fusedconv_create", "fusedconv_output_shape",
+EXPORTS = ["fusedconv_desc_init", "fusedconv_create", "fusedconv_create_transposed",
+           "fusedconv_output_shape",
            "fusedconv_workspace_size", "fusedconv_plan_info", "fusedconv_run",
            "fusedconv_prepare_weights", "fusedconv_run_ex", "fusedconv_destroy",
            "fusedconv_status_string", "fusedconv_last_error"]
@@ -83,6 +84,10 @@ def load():
         lib.fusedconv_desc_init.restype = None
         lib.fusedconv_create.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(vp)]
         lib.fusedconv_create.restype = ctypes.c_int
+        lib.fusedconv_create_transposed.argtypes = [ctypes.POINTER(Desc),
+                                                    ctypes.POINTER(ctypes.c_int64), ctypes.c_int32,
+                                                    ctypes.POINTER(vp)]
+        lib.fusedconv_create_transposed.restype = ctypes.c_int
         lib.fusedconv_output_shape.argtypes = [vp, ctypes.POINTER(ctypes.c_int64),
                                                ctypes.POINTER(ctypes.c_int32)]
         lib.fusedconv_output_shape.restype = ctypes.c_int
@@ -136,7 +141,8 @@ class Handle:
 
     def __init__(self, dtype, x_shape, w_shape, bias_shape=None, z_shape=None, *,
                  auto_pad=None, group=1, kernel_shape=None, strides=None, dilations=None,
-                 pads=None, activation=None, activation_params=None, route="auto", split_k=0):
+                 pads=None, activation=None, activation_params=None, route="auto", split_k=0,
+                 transposed=False, output_padding=None):
         lib = load()
         d = Desc()
         lib.fusedconv_desc_init(ctypes.byref(d))
@@ -166,7 +172,11 @@ class Handle:
         d.route = ROUTES[route] if isinstance(route, str) else int(route)
         d.split_k = int(split_k)
         h = ctypes.c_void_p()
-        rc = lib.fusedconv_create(ctypes.byref(d), ctypes.byref(h))
+        if transposed:
+            op, nop = _i64list(output_padding, keep)
+            rc = lib.fusedconv_create_transposed(ctypes.byref(d), op, nop, ctypes.byref(h))
+        else:
+            rc = lib.fusedconv_create(ctypes.byref(d), ctypes.byref(h))
         if rc != 0:
             raise FusedConvError(rc, lib.fusedconv_last_error().decode())
         self._lib = lib

@@ -73,6 +73,24 @@ int fusedconv_create(const fusedconv_desc* d, fusedconv_handle** out) {
   return FUSEDCONV_OK;
 }
 
+int fusedconv_create_transposed(const fusedconv_desc* d, const int64_t* output_padding,
+                                int32_t n_output_padding, fusedconv_handle** out) {
+  if (out) *out = nullptr;
+  if (!d || !out) return set_err(FUSEDCONV_ERR_NULL_ARG, "desc and out must not be NULL");
+  fusedconv_handle* h = new (std::nothrow) fusedconv_handle;
+  if (!h) return set_err(FUSEDCONV_ERR_ALLOC, "out of host memory");
+  std::string err;
+  int rc = fc::resolve_transposed(*d, output_padding, n_output_padding, h->geo, err);
+  if (rc == FUSEDCONV_OK) rc = fc::make_plan(h->geo, d->route, d->split_k, h->plan, err);
+  if (rc != FUSEDCONV_OK) {
+    delete h;
+    return set_err(rc, err);
+  }
+  *out = h;
+  t_last_error.clear();
+  return FUSEDCONV_OK;
+}
+
 int fusedconv_output_shape(const fusedconv_handle* h, int64_t dims[FUSEDCONV_MAX_RANK],
                            int32_t* rank) {
   if (!h || !dims || !rank) return set_err(FUSEDCONV_ERR_NULL_ARG, "NULL argument");
@@ -159,6 +177,7 @@ int fusedconv_run_ex(const fusedconv_handle* h, const void* x, const void* w, co
     case FUSEDCONV_ROUTE_IGEMM_HALO: rc = fc::launch_igemm_halo(h->geo, h->plan, a); break;
     case FUSEDCONV_ROUTE_SMALLC: rc = fc::launch_smallc(h->geo, h->plan, a); break;
     case FUSEDCONV_ROUTE_POINTWISE: rc = fc::launch_pointwise(h->geo, h->plan, a); break;
+    case FUSEDCONV_ROUTE_TRANSPOSED: rc = fc::launch_transposed(h->geo, h->plan, a); break;
     default: return set_err(FUSEDCONV_ERR_ROUTE, "handle has no route");
   }
   if (rc != FUSEDCONV_OK) {

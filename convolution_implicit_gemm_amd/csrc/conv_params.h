@@ -36,6 +36,10 @@ struct ConvParams {
   int32_t act;          // Act
   float alpha, beta;    // activation parameters after defaulting
   int32_t has_bias, has_z;
+  // 1: transposed convolution (fusedconv_create_transposed).  Then C and Cg
+  // count X's channels, M and Mg Y's, W is [C][M/G][k...], (D, H, W) is X's
+  // extent and (OD, OH, OW) Y's, and the pads are Y's begin offsets.
+  int32_t transposed;
 };
 
 }  // namespace fc

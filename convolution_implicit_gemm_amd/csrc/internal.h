@@ -39,6 +39,11 @@ struct Plan {
 };
 
 int resolve(const fusedconv_desc& d, Geometry& g, std::string& err);
+// Transposed convolution (fusedconv_create_transposed): d describes X, W as
+// [C, M/group, k...], B of length M and Z of Y's shape; output_padding has
+// one entry per spatial axis (NULL: zeros).
+int resolve_transposed(const fusedconv_desc& d, const int64_t* output_padding,
+                       int32_t n_output_padding, Geometry& g, std::string& err);
 int make_plan(const Geometry& g, int32_t route, int32_t split_k, Plan& p, std::string& err);
 
 // Device launchers (kernels_*.hip).  Return 0 or FUSEDCONV_ERR_LAUNCH.
@@ -61,6 +66,7 @@ int prepare_igemm_halo(const Geometry& g, const Plan& p, const RunArgs& a);
 int launch_smallc(const Geometry& g, const Plan& p, const RunArgs& a);
 int prepare_smallc(const Geometry& g, const Plan& p, const RunArgs& a);
 int launch_pointwise(const Geometry& g, const Plan& p, const RunArgs& a);
+int launch_transposed(const Geometry& g, const Plan& p, const RunArgs& a);
 int prepare_pointwise(const Geometry& g, const Plan& p, const RunArgs& a);
 
 // Kernels whose activation is a compile-time parameter: the build compiles

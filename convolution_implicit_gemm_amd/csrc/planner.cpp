@@ -81,13 +81,25 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
     err = "split_k must be >= 0";
     return FUSEDCONV_ERR_ROUTE;
   }
-  if (route < FUSEDCONV_ROUTE_AUTO || route > FUSEDCONV_ROUTE_POINTWISE) {
+  if (route < FUSEDCONV_ROUTE_AUTO || route > FUSEDCONV_ROUTE_TRANSPOSED) {
     err = "unknown route";
     return FUSEDCONV_ERR_ROUTE;
   }
   if (split_req > 1 && route != FUSEDCONV_ROUTE_IGEMM && route != FUSEDCONV_ROUTE_AUTO) {
     err = "split_k applies to the IGEMM route only";
     return FUSEDCONV_ERR_ROUTE;
+  }
+  if (cp.transposed || route == FUSEDCONV_ROUTE_TRANSPOSED) {
+    if (!cp.transposed || (route != FUSEDCONV_ROUTE_AUTO && route != FUSEDCONV_ROUTE_TRANSPOSED) ||
+        split_req > 1) {
+      err = "TRANSPOSED is the route of transposed convolutions (fusedconv_create_transposed), "
+            "and their only one";
+      return FUSEDCONV_ERR_ROUTE;
+    }
+    p.route = FUSEDCONV_ROUTE_TRANSPOSED;
+    snprintf(p.name, sizeof(p.name), "transposed_gather_%s",
+             g.dtype == FUSEDCONV_F16 ? "f16" : "f32");
+    return FUSEDCONV_OK;
   }
   int32_t th = 0, tw = 0;
   size_t halo_ws = 0;

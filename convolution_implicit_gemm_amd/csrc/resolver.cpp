@@ -222,4 +222,93 @@ int resolve(const fusedconv_desc& d, Geometry& g, std::string& err) {
   return FUSEDCONV_OK;
 }
 
+// Transposed convolution: the adjoint of the cross-correlation above (X is
+// scattered through W into Y).  Output size per axis s*(in - 1) +
+// output_padding + (k - 1)*d + 1 - pad_begin - pad_end.  Everything the
+// forward rules check is checked on the forward problem that maps Y back to
+// X with the same W (read as a [C, M/group, k...] conv weight): it must be
+// valid and give X's extent, which holds for 0 <= output_padding < stride.
+// auto_pad other than NOTSET and kernel_shape other than W's are refused.
+int resolve_transposed(const fusedconv_desc& d, const int64_t* op, int32_t nop, Geometry& g,
+                       std::string& err) {
+  memset(&g, 0, sizeof(g));
+  if (d.auto_pad && strcmp(d.auto_pad, "NOTSET") != 0)
+    return fail(err, FUSEDCONV_ERR_ATTR_VALUE, "transposed: only auto_pad NOTSET is supported");
+  if (!d.x.present || !d.w.present)
+    return fail(err, FUSEDCONV_ERR_NULL_ARG, "x and w are required inputs");
+  if (d.x.rank < 3 || d.x.rank > 5 || d.w.rank != d.x.rank)
+    return fail(err, FUSEDCONV_ERR_RANK, "x and w ranks must be equal and 3, 4 or 5");
+  const int nsp = d.x.rank - 2;
+  if ((op && nop != nsp) || (!op && nop != 0))
+    return fail(err, FUSEDCONV_ERR_ATTR_LENGTH, "output_padding needs one entry per spatial axis");
+  if ((d.strides && d.n_strides != nsp) || (d.dilations && d.n_dilations != nsp) ||
+      (d.pads && d.n_pads != 2 * nsp) || (d.kernel_shape && d.n_kernel_shape != nsp))
+    return fail(err, FUSEDCONV_ERR_ATTR_LENGTH,
+                "kernel_shape/strides/dilations need one entry per spatial axis, pads two");
+  const int64_t n = d.x.dims[0], C = d.x.dims[1], wc = d.w.dims[0], mg = d.w.dims[1];
+  if (d.group < 1) return fail(err, FUSEDCONV_ERR_GROUP, "group must be >= 1");
+  if (wc != C || C % d.group != 0)
+    return fail(err, FUSEDCONV_ERR_GROUP, "transposed: need w.shape[0] == C and C % group == 0");
+  const int64_t M = mg * d.group;
+  int64_t out[3];
+  for (int i = 0; i < nsp; ++i) {
+    const int64_t s = d.strides ? d.strides[i] : 1, dl = d.dilations ? d.dilations[i] : 1;
+    const int64_t pb = d.pads ? d.pads[i] : 0, pe = d.pads ? d.pads[nsp + i] : 0;
+    const int64_t o = op ? op[i] : 0, k = d.w.dims[2 + i];
+    if (s < 1 || dl < 1 || pb < 0 || pe < 0 || k < 1 || d.x.dims[2 + i] < 1)
+      return fail(err, FUSEDCONV_ERR_ATTR_VALUE,
+                  "strides, dilations, kernel and input extents >= 1, pads >= 0");
+    if (o < 0 || o >= s)
+      return fail(err, FUSEDCONV_ERR_ATTR_VALUE, "output_padding must be in [0, stride)");
+    out[i] = s * (d.x.dims[2 + i] - 1) + o + (k - 1) * dl + 1 - pb - pe;
+    if (out[i] < 1) return fail(err, FUSEDCONV_ERR_OUTPUT_SHAPE, "transposed output size < 1");
+  }
+  // the forward problem Y -> X, without bias and residual (their shapes are
+  // checked below), with the activation (its name and parameters)
+  fusedconv_desc f = d;
+  f.x.rank = d.x.rank;
+  f.x.dims[0] = n;
+  f.x.dims[1] = M;
+  for (int i = 0; i < nsp; ++i) f.x.dims[2 + i] = out[i];
+  f.bias.present = 0;
+  f.z.present = 0;
+  Geometry gf;
+  int rc = resolve(f, gf, err);
+  if (rc != FUSEDCONV_OK) return rc;
+  for (int i = 0; i < nsp; ++i)
+    if (gf.y_dims[2 + i] != d.x.dims[2 + i])
+      return fail(err, FUSEDCONV_ERR_OUTPUT_SHAPE, "transposed: inconsistent output size");
+  if (d.bias.present && (d.bias.rank != 1 || d.bias.dims[0] != M))
+    return fail(err, FUSEDCONV_ERR_BIAS_SHAPE, "bias must be rank 1 with M entries");
+  g.dtype = gf.dtype;
+  g.nsp = nsp;
+  g.y_rank = d.x.rank;
+  g.y_dims[0] = n;
+  g.y_dims[1] = M;
+  for (int i = 0; i < nsp; ++i) g.y_dims[2 + i] = out[i];
+  if (d.z.present) {
+    bool same = d.z.rank == g.y_rank;
+    for (int i = 0; same && i < g.y_rank; ++i) same = d.z.dims[i] == g.y_dims[i];
+    if (!same) return fail(err, FUSEDCONV_ERR_Z_SHAPE, "z must have exactly the shape of y");
+  }
+  // geometry of the transposed problem: the forward one with X and Y swapped
+  ConvParams& cp = g.cp;
+  const ConvParams& fp = gf.cp;
+  cp = fp;
+  cp.C = (int32_t)C;
+  cp.M = (int32_t)M;
+  cp.Cg = (int32_t)(C / d.group);
+  cp.Mg = (int32_t)mg;
+  cp.D = fp.OD; cp.H = fp.OH; cp.W = fp.OW;
+  cp.OD = fp.D; cp.OH = fp.H; cp.OW = fp.W;
+  cp.K = cp.Cg * cp.taps;
+  cp.in_sz = fp.out_sz;
+  cp.out_sz = fp.in_sz;
+  cp.P = n * cp.out_sz;
+  cp.has_bias = d.bias.present ? 1 : 0;
+  cp.has_z = d.z.present ? 1 : 0;
+  cp.transposed = 1;
+  return FUSEDCONV_OK;
+}
+
 }  // namespace fc

@@ -69,6 +69,10 @@ typedef enum fusedconv_dtype {
  *              stride 2, dilation 1 and no padding (patch embeddings,
  *              downsampling) whose W and OW are multiples of 8, with
  *              C/group even and >= 4.
+ *   TRANSPOSED the route of transposed convolutions (handles made with
+ *              fusedconv_create_transposed), and their only one: one output
+ *              element per lane, gathering the input elements and taps that
+ *              scatter into it; fp32 and fp16.
  */
 typedef enum fusedconv_route {
   FUSEDCONV_ROUTE_AUTO = 0,
@@ -77,7 +81,8 @@ typedef enum fusedconv_route {
   FUSEDCONV_ROUTE_DEPTHWISE = 3,
   FUSEDCONV_ROUTE_IGEMM_HALO = 4,
   FUSEDCONV_ROUTE_SMALLC = 5,
-  FUSEDCONV_ROUTE_POINTWISE = 6
+  FUSEDCONV_ROUTE_POINTWISE = 6,
+  FUSEDCONV_ROUTE_TRANSPOSED = 7
 } fusedconv_route;
 
 /* Shape of one tensor.  present = 0 means the (optional) input is absent. */
@@ -163,6 +168,28 @@ void fusedconv_desc_init(fusedconv_desc* d);
  * allocation.  On success *out owns a new handle; on failure *out is NULL.
  */
 int fusedconv_create(const fusedconv_desc* d, fusedconv_handle** out);
+
+/*
+ * Transposed convolution with the same fused epilogue:
+ *   Y = act(convT(X, W) + B + Z),
+ * convT being the adjoint of the cross-correlation fusedconv_create plans
+ * (the transposed form of the aten.convolution entry point the ExecuTorch
+ * conv page routes through): every X[n, c, i] adds X[n, c, i] * W[c, m, k]
+ * into Y[n, g*(M/group) + m, i*stride - pad_begin + k*dilation], with
+ * g = c / (C/group).  d describes X [n, C, in...], W as [C, M/group, k...],
+ * B (length M = W.shape[1] * group) and Z (Y's shape), strides, dilations,
+ * pads (ONNX order; they trim Y), group, activation; auto_pad must be NULL
+ * or "NOTSET" and kernel_shape, if given, must match W.  output_padding:
+ * n_output_padding (0 or one per spatial axis) values in [0, stride),
+ * appended to Y's end; NULL with 0 means zeros.  Y's extent per axis is
+ * stride*(in - 1) + output_padding + (k - 1)*dilation + 1 - pad_begin -
+ * pad_end.  route must be FUSEDCONV_ROUTE_AUTO or ..._TRANSPOSED.  The
+ * handle is used with every other call below exactly like one from
+ * fusedconv_create.  Errors as for fusedconv_create (output_padding out of
+ * range: FUSEDCONV_ERR_ATTR_VALUE; wrong count: ..._ATTR_LENGTH).
+ */
+int fusedconv_create_transposed(const fusedconv_desc* d, const int64_t* output_padding,
+                                int32_t n_output_padding, fusedconv_handle** out);
 
 /* Y's shape: *rank = rank of X, dims[0..rank) filled. */
 int fusedconv_output_shape(const fusedconv_handle* h, int64_t dims[FUSEDCONV_MAX_RANK],

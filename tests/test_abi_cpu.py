@@ -71,7 +71,7 @@ def test_workload_shapes_and_routes():
         h = B.Handle(wl["dtype"], wl["x"], wl["w"], wl["b"], wl["z"], **wl["attrs"])
         assert h.y_shape == wl["y"], name
         assert h.route in ("direct", "igemm", "depthwise", "igemm_halo", "smallc",
-                           "pointwise"), name
+                           "pointwise", "transposed"), name
         if wl["attrs"].get("group", 1) == wl["x"][1]:
             assert h.route == "depthwise", name
     stem = WORKLOADS["vision_stem_7x7s4_f16"]
@@ -253,3 +253,37 @@ def test_forced_routes_and_split_plan():
     assert h.split_k == 3  # K = 144 -> 5 tiles of 32 -> slices of 2, 2, 1
     h = _h([1, 16, 8, 8], [16, 16, 3, 3], route="igemm", split_k=5)
     assert h.split_k == 5
+
+
+def test_transposed_handles():
+    # shapes from the transposed oracle; one route; the forward rules still apply
+    rng = np.random.default_rng(11)
+    for xs, ws, kw in [([2, 4, 5, 6], [4, 3, 3, 2], dict(strides=[2, 3], pads=[1, 0, 2, 1],
+                                                        dilations=[1, 2], output_padding=[1, 2])),
+                       ([1, 6, 7], [6, 2, 4], dict(group=3, strides=[2], pads=[1, 2])),
+                       ([2, 4, 3, 4, 3], [4, 2, 2, 3, 2], dict(group=2, strides=[1, 2, 2]))]:
+        h = B.Handle("f32", xs, ws, None, None, transposed=True, **kw)
+        ref = oracle.conv_transpose(rng.standard_normal(xs), rng.standard_normal(ws), **kw)
+        assert h.y_shape == list(ref.shape) and h.route == "transposed", (xs, ws, kw)
+        assert h.kernel_name == "transposed_gather_f32" and h.workspace_bytes == 0
+    bad = [
+        (dict(output_padding=[2, 0]), "FUSEDCONV_ERR_ATTR_VALUE"),   # not below the stride
+        (dict(output_padding=[1]), "FUSEDCONV_ERR_ATTR_LENGTH"),
+        (dict(auto_pad="SAME_UPPER"), "FUSEDCONV_ERR_ATTR_VALUE"),
+        (dict(group=3), "FUSEDCONV_ERR_GROUP"),                      # C = 4
+        (dict(route="igemm"), "FUSEDCONV_ERR_ROUTE"),
+        (dict(pads=[9, 9, 9, 9]), "FUSEDCONV_ERR_OUTPUT_SHAPE"),
+        (dict(activation="LeakyRelu"), "FUSEDCONV_ERR_ACTIVATION_PARAMS"),
+    ]
+    for extra, status in bad:
+        kw = dict(strides=[2, 2])
+        kw.update(extra)
+        with pytest.raises(B.FusedConvError) as e:
+            B.Handle("f16", [1, 4, 5, 5], [4, 3, 3, 3], None, None, transposed=True, **kw)
+        assert e.value.status == status, (extra, e.value.status)
+    with pytest.raises(B.FusedConvError) as e:   # bias must have M = 3 entries
+        B.Handle("f16", [1, 4, 5, 5], [4, 3, 3, 3], [4], None, transposed=True)
+    assert e.value.status == "FUSEDCONV_ERR_BIAS_SHAPE"
+    with pytest.raises(B.FusedConvError) as e:   # the TRANSPOSED route needs a transposed conv
+        B.Handle("f16", [1, 4, 5, 5], [4, 4, 3, 3], None, None, route="transposed")
+    assert e.value.status == "FUSEDCONV_ERR_ROUTE"

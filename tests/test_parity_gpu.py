@@ -587,6 +587,14 @@ def test_full_size_workloads(name):
     attrs["activation_params"] = f32params(attrs.get("activation_params"))
     got = run_gpu(inp["x"], inp["w"], inp["b"], inp["z"], **attrs)
     assert list(got.shape) == wl["y"]
+    if attrs.get("transposed"):
+        # the transposed oracle on the first and the last image, every output
+        kw = {k: v for k, v in attrs.items() if k != "transposed"}
+        for i in (0, wl["x"][0] - 1):
+            zi = inp["z"][i:i + 1] if inp["z"] is not None else None
+            ref = oracle.conv_transpose(inp["x"][i:i + 1], inp["w"], inp["b"], zi, **kw)
+            check(got[i:i + 1], ref, wl["dtype"], f"{name} image {i}")
+        return
     if got.size <= 1 << 16:
         ref = oracle.fusedconv(inp["x"], inp["w"], inp["b"], inp["z"], **attrs)
         check(got, ref, wl["dtype"], name)
@@ -597,3 +605,32 @@ def test_full_size_workloads(name):
     assert np.all(np.isfinite(got)), name
     # tau relative to the largest |Y_ref| among the sampled outputs
     check(g, ref, wl["dtype"], name)
+
+
+TRANSPOSED_CASES = [
+    # (dtype, x, w [C, M/group, k...], attrs)
+    ("f32", [2, 4, 5, 6], [4, 3, 3, 2], dict(strides=[2, 3], pads=[1, 0, 2, 1], dilations=[1, 2],
+                                             output_padding=[1, 2])),
+    ("f16", [1, 6, 37], [6, 2, 4], dict(group=3, strides=[2], pads=[1, 2])),
+    ("f32", [2, 4, 3, 4, 3], [4, 2, 2, 3, 2], dict(group=2, strides=[1, 2, 2],
+                                                  pads=[0, 1, 0, 1, 0, 1], output_padding=[0, 1, 1])),
+    ("f16", [2, 32, 12, 16], [32, 24, 2, 2], dict(strides=[2, 2])),           # patch upsampling
+    ("f16", [1, 16, 9, 11], [16, 8, 3, 3], dict(strides=[1, 1], pads=[1, 1, 1, 1])),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(TRANSPOSED_CASES)))
+def test_transposed_route(ci):
+    dtype, xs, ws, attrs = TRANSPOSED_CASES[ci]
+    M = ws[1] * attrs.get("group", 1)
+    h = B.Handle(dtype, xs, ws, None, None, transposed=True, **attrs)
+    for k, (bias, resid) in enumerate([(True, True), (False, False), (True, False)]):
+        act, params = ACTS[(3 * ci + 5 * k) % len(ACTS)]
+        x, w, b, z = random_tensors([9500, ci, k], dtype, xs, ws, [M] if bias else None,
+                                    h.y_shape if resid else None, dist="normal",
+                                    w_std=1.0 / np.sqrt(ws[0]))
+        a = dict(attrs, activation=act, activation_params=f32params(params))
+        log(f"CASE transposed {ci} x={xs} w={ws} {a} bias={bias} z={resid}")
+        got = run_gpu(x, w, b, z, transposed=True, **a)
+        ref = oracle.conv_transpose(x, w, b, z, **a)
+        check(got, ref, dtype, f"transposed case {ci}")

@@ -11,8 +11,9 @@ CIFAR-ResNet 3x3 conv with residual and QuickGelu (tinygrad hlb-CIFAR10
 ConvGroup), a vision-encoder patch-embed stem and strided downsample
 (ExecuTorch conv2d PR, DaViT / SigLIP stems), a depthwise 7x7 layer
 (FusedConv manifest grouped_large_kernel variants), grouped 1-D and 3-D
-convs, and the 1x1 reduce conv of a ResNet-50 stage-3 bottleneck (the FusedConv
-README's usage example is a 1x1 conv).  No dataset, image or trained weight
+convs, the 1x1 reduce conv of a ResNet-50 stage-3 bottleneck (the FusedConv
+README's usage example is a 1x1 conv), and a 2x2 stride-2 transposed conv (the
+decoder-side inverse of the downsample).  No dataset, image or trained weight
 is used.
 
 Draw rule: numpy.random.default_rng([workload_index, sub]); tensors are
@@ -78,6 +79,10 @@ WORKLOADS = {
         z=[4, 128, 32, 32, 32], y=[4, 128, 32, 32, 32], dist="uniform", w_std=1.0,
         attrs=dict(strides=[1, 2, 2], pads=[1, 1, 1, 1, 1, 1], activation="Clip",
                    activation_params=[0.0, 6.0])),
+    "conv_transpose_2x2s2_f16": dict(
+        seed=[6, 0], dtype="f16", x=[8, 256, 96, 96], w=[256, 128, 2, 2], b=[128], z=None,
+        y=[8, 128, 192, 192], dist="normal", w_std=1.0 / math.sqrt(256),
+        attrs=dict(transposed=True, strides=[2, 2], activation="Relu")),
     "pointwise_1x1_512to128_f16": dict(
         seed=[5, 0], dtype="f16", x=[256, 512, 28, 28], w=[128, 512, 1, 1], b=[128], z=None,
         y=[256, 128, 28, 28], dist="normal", w_std=1.0 / math.sqrt(512),
