@@ -131,15 +131,16 @@ int fusedconv_prepare_weights(const fusedconv_handle* h, const void* w, void* wo
   if (h->plan.workspace > 0 && (!workspace || workspace_bytes < h->plan.workspace))
     return set_err(FUSEDCONV_ERR_WORKSPACE,
                    "workspace smaller than fusedconv_workspace_size() reports");
-  if (h->plan.route != FUSEDCONV_ROUTE_IGEMM_HALO && h->plan.route != FUSEDCONV_ROUTE_SMALLC &&
-      h->plan.route != FUSEDCONV_ROUTE_POINTWISE)
+  const bool pw = h->plan.route == FUSEDCONV_ROUTE_POINTWISE ||
+                  (h->plan.route == FUSEDCONV_ROUTE_TRANSPOSED && h->plan.tile == 1);
+  if (h->plan.route != FUSEDCONV_ROUTE_IGEMM_HALO && h->plan.route != FUSEDCONV_ROUTE_SMALLC && !pw)
     return FUSEDCONV_OK;
   int rc = check_device();
   if (rc != FUSEDCONV_OK) return rc;
   (void)hipGetLastError();
   fc::RunArgs a{nullptr, w, nullptr, nullptr, nullptr, workspace, stream, 0u};
-  rc = h->plan.route == FUSEDCONV_ROUTE_SMALLC      ? fc::prepare_smallc(h->geo, h->plan, a)
-       : h->plan.route == FUSEDCONV_ROUTE_POINTWISE ? fc::prepare_pointwise(h->geo, h->plan, a)
+  rc = h->plan.route == FUSEDCONV_ROUTE_SMALLC ? fc::prepare_smallc(h->geo, h->plan, a)
+       : pw ? fc::prepare_pointwise(h->geo, h->plan, a)
                                                     : fc::prepare_igemm_halo(h->geo, h->plan, a);
   if (rc != FUSEDCONV_OK) {
     hipError_t e = hipGetLastError();

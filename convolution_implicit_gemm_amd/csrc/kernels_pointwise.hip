@@ -41,6 +41,14 @@
 // 4 taps of one input channel, and its 8 output pixels read 16 consecutive
 // columns of 2 input rows (two 32-byte pieces per row), split into even (kw 0)
 // and odd (kw 1) columns -- the same number of loads as a 1x1 item.
+// A third form runs transposed 2x2 convolutions with stride 2 (no pads, the
+// output exactly twice the input, e.g. decoder upsampling): output pixel
+// (2i + a, 2j + b) of channel m is sum_c W[c][m][a][b] * X[c][i][j], so the
+// input pixels are the GEMM rows, the reduction is over the input channels
+// (the 1x1 producer as is) and the columns are (m, a, b) = 4m + 2a + b, W's
+// own memory order along a row of W.  The epilogue pairs the columns b = 0
+// and b = 1 of two neighbouring pixels: each lane stores 4 consecutive
+// outputs of one output row.
 // Every load is unconditional (invalid X pieces read a valid address and are
 // written as zeros; the repacked weights are zero-padded), so the compiler can
 // count the loads in flight exactly.
@@ -66,6 +74,7 @@ constexpr unsigned kOff = 0x80000000u;  // an offset past every range set up her
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 typedef unsigned uint2v __attribute__((ext_vector_type(2)));
 
 struct PwTile {
@@ -76,6 +85,7 @@ struct PwTile {
   int ks;          // reduction steps: ceil(kp / 64)
   int nwm;         // MFMA waves along the output channels: 2 (128 per block) or 4 (256)
   int64_t tiles;   // G * n * ntile
+  int wt;          // 1: W stored as [C][M/group * 4] (the transposed form)
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -83,7 +93,8 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Weights in fragment order: Wf[((((g*nmb + mb)*ks + s)*2 + kk)*4 + j)*nwm + wmi]
 // [lane][e] = W[g*Mg + m][k] (W as [M][C/group * taps], its memory order) with
 // m = mb*64*nwm + wmi*64 + j*16 + lane%16 and k = s*64 + kk*32 + (lane/16)*8 + e;
-// zero for m >= M/group or k >= C/group * taps.
+// zero for m >= M/group or k >= C/group * taps.  The transposed form passes
+// M/group * 4 as M/group and reads W[g*Cg + k][m] instead.
 constexpr int kFragPerWave = 2 * 4 * 64 * 8;  // halves per (group, m block, step, wave)
 __global__ __launch_bounds__(256) void repack_frag_kernel(const half_t* __restrict__ w,
                                                           half_t* __restrict__ wf, ConvParams cp,
@@ -106,7 +117,8 @@ __global__ __launch_bounds__(256) void repack_frag_kernel(const half_t* __restri
     const int g = (int)(t / pt.nmb);
     const int m = mb * 64 * pt.nwm + wmi * 64 + j * 16 + (lane & 15);
     const int c = s * kBK + kk * 32 + (lane >> 4) * 8 + e;
-    wf[i] = (m < cp.Mg && c < pt.kp) ? w[((int64_t)g * cp.Mg + m) * pt.kp + c] : (half_t)0;
+    const int64_t src = pt.wt ? ((int64_t)g * pt.kp + c) * cp.Mg + m : ((int64_t)g * cp.Mg + m) * pt.kp + c;
+    wf[i] = (m < cp.Mg && c < pt.kp) ? w[src] : (half_t)0;
   }
 }
 
@@ -160,7 +172,7 @@ __global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t*
   for (int j = 0; j < 4; ++j) {
     const int m = m0 + wmi * 64 + j * 16 + r16;
     float bv = 0.0f;
-    if (cp.has_bias && m < cp.Mg) bv = to_f32(bias[g * cp.Mg + m]);
+    if (cp.has_bias && m < cp.Mg) bv = to_f32(bias[PATCH == 3 ? (g * cp.Mg + m) >> 2 : g * cp.Mg + m]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i][j] = float4v{bv, bv, bv, bv};
   }
@@ -212,7 +224,7 @@ __global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t*
       const int64_t pp = p0 + 8 * po[k];
       pix_ok[k] = pp < P;  // P (and OW for a patch conv) % 8 == 0: an octet is all in or all out
       const half_t* img = x + (n * cp.C + (int64_t)g * cp.Cg) * cp.in_sz;
-      if constexpr (PATCH == 1) {
+      if constexpr (PATCH != 2) {
         xs[k] = img + pp;
       } else {  // first input column of the octet's 2x2 patches in input row 2*oh
         const int64_t oh = pp / cp.OW, ow = pp - oh * cp.OW;
@@ -227,7 +239,7 @@ __global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t*
       for (int k = 0; k < 2; ++k)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if constexpr (PATCH == 1) {
+          if constexpr (PATCH != 2) {
             const int c = st * kBK + 4 * cq[k] + j;
             const bool ok = pix_ok[k] && c < cp.Cg;
             v[k][j] = *(const half8*)(ok ? xs[k] + (int64_t)c * P : x);
@@ -244,7 +256,7 @@ __global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t*
         // row 8*po + e, bytes 8*cq .. +7 of the row's channels, swizzled
         half_t* dst = lds + (st & 1) * kStage + (8 * po[k]) * kLDC + ((8 * cq[k]) ^ ((po[k] & 7) << 4)) / 2;
         half8 u[4];
-        if constexpr (PATCH == 1) {
+        if constexpr (PATCH != 2) {
           const int cvalid = cp.Cg - st * kBK - 4 * cq[k];
 #pragma unroll
           for (int j = 0; j < 4; ++j) u[j] = pix_ok[k] && j < cvalid ? v[k][j] : half8{};
@@ -327,12 +339,29 @@ __global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t*
   const int p4 = (lane & 15) * 4, rsub = lane >> 4;
   const int64_t pg = p0 + wpi * 64 + p4;  // image pixel of this lane
   const bool pok = pg < P;
-  const int64_t wbase = (n * cp.M + (int64_t)g * cp.Mg + mw0) * P;
+  int64_t wbase = (n * cp.M + (int64_t)g * cp.Mg + mw0) * P;
+  // transposed form: lane (pr, ah) owns input pixels 2pr, 2pr+1 of the
+  // wave's 64 and output row phase a = ah; iteration it of block j is output
+  // channel 4j + it of the wave's 16 (columns 16j + 4it + 2ah + b)
+  const int pr = lane & 31, ah = lane >> 5;
+  const int64_t pp2 = p0 + wpi * 64 + 2 * pr;
+  const bool pok2 = pp2 < P;  // P % 8 == 0: a pair is all in or all out
+  const int mg_out = cp.Mg >> 2, mo0 = mw0 >> 2;
+  int64_t obase = 0;  // output offset of the lane's first value in channel mo0
+  if constexpr (PATCH == 3) {
+    const int64_t ih = pp2 / cp.W, jw = pp2 - ih * cp.W;
+    obase = (2 * ih + ah) * cp.OW + 2 * jw;
+    wbase = (n * cp.M + (int64_t)g * mg_out + mo0) * cp.out_sz;
+  }
   const __amdgpu_buffer_rsrc_t yb =
       __builtin_amdgcn_make_buffer_rsrc((void*)(y + wbase), (short)0, 0x7fffffff, kBufferWord3);
   const __amdgpu_buffer_rsrc_t zb = __builtin_amdgcn_make_buffer_rsrc(
       cp.has_z ? (void*)(z + wbase) : (void*)y, (short)0, cp.has_z ? 0x7fffffff : 0, kBufferWord3);
   auto voff = [&](int j, int it) __attribute__((always_inline)) {
+    if constexpr (PATCH == 3) {
+      const int cm = 4 * j + it;  // output channel relative to mo0
+      return (pok2 && mo0 + cm < mg_out) ? (unsigned)((cm * cp.out_sz + obase) * 2) : kOff;
+    }
     const int r = j * 16 + it * 4 + rsub;  // channel relative to mw0
     return (pok && mw0 + r < cp.Mg) ? (unsigned)((r * P + pg) * 2) : kOff;
   };
@@ -351,7 +380,14 @@ __global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t*
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const float4v sv = *(const float4v*)(stage + (it * 4 + rsub) * RP + p4);
+      float4v sv;
+      if constexpr (PATCH == 3) {  // (pixel 2pr, b 0), (2pr, 1), (2pr+1, 0), (2pr+1, 1)
+        const float2v s0 = *(const float2v*)(stage + (4 * it + 2 * ah) * RP + 2 * pr);
+        const float2v s1 = *(const float2v*)(stage + (4 * it + 2 * ah + 1) * RP + 2 * pr);
+        sv = float4v{s0[0], s1[0], s0[1], s1[1]};
+      } else {
+        sv = *(const float4v*)(stage + (it * 4 + rsub) * RP + p4);
+      }
       const half4 zh = __builtin_bit_cast(half4, zr[j][it]);
       act4_t v;
 #pragma unroll
@@ -370,8 +406,17 @@ __global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t*
 
 // PATCH 1: kernel 1, stride 1, no padding.  PATCH 2: 2-D, kernel 2x2, stride
 // 2, dilation 1, no padding, OW % 8 == 0 and W % 8 == 0 (16-byte row pieces).
+// PATCH 3: transposed, 2-D, kernel 2x2, stride 2, dilation 1, no leading pad
+// and an output of exactly 2H x 2W (trailing pads only crop output_padding),
+// W % 8 == 0.
 int patch_of(const ConvParams& cp) {
   const bool nopad = cp.pd == 0 && cp.ph == 0 && cp.pw == 0;
+  if (cp.transposed)
+    return (cp.D == 1 && cp.KD == 1 && cp.KH == 2 && cp.KW == 2 && cp.sh == 2 && cp.sw == 2 &&
+            cp.dh == 1 && cp.dw == 1 && nopad && cp.OH == 2 * cp.H && cp.OW == 2 * cp.W &&
+            cp.W % 8 == 0)
+               ? 3
+               : 0;
   if (cp.KD == 1 && cp.KH == 1 && cp.KW == 1 && cp.sd == 1 && cp.sh == 1 && cp.sw == 1 && nopad &&
       cp.OD == cp.D && cp.OH == cp.H && cp.OW == cp.W)
     return 1;
@@ -386,19 +431,32 @@ bool choose(const ConvParams& cp, int32_t dtype, PwTile& pt) {
   if (dtype != FUSEDCONV_F16) return false;
   const int patch = patch_of(cp);
   if (patch == 0) return false;
-  pt.kp = cp.Cg * patch * patch;
+  const bool tr = patch == 3;
+  pt.wt = tr ? 1 : 0;
+  pt.kp = tr ? cp.Cg : cp.Cg * patch * patch;
   if (pt.kp % 8 != 0 || pt.kp < 16) return false;
-  pt.P = cp.out_sz;
+  pt.P = tr ? cp.in_sz : cp.out_sz;
   if (pt.P % 8 != 0) return false;
-  // epilogue offsets: 64 channel planes of one image in 31-bit byte offsets
-  if (pt.P * 64 * 2 >= ((int64_t)1 << 31)) return false;
+  // epilogue offsets: 64 channel planes of one image (16 planes of 4P
+  // outputs for the transposed form) in 31-bit byte offsets
+  if (pt.P * 64 * 2 * (tr ? 2 : 1) >= ((int64_t)1 << 31)) return false;
+  const int64_t mg = tr ? 4 * (int64_t)cp.Mg : cp.Mg;  // GEMM columns per group
+  if (mg >= ((int64_t)1 << 30)) return false;
   pt.ntile = (int)cdiv(pt.P, kBN);
-  pt.nwm = cp.Mg > 128 ? 4 : 2;
-  pt.nmb = (int)cdiv(cp.Mg, 64 * pt.nwm);
+  pt.nwm = mg > 128 ? 4 : 2;
+  pt.nmb = (int)cdiv(mg, 64 * pt.nwm);
   pt.ks = (int)cdiv(pt.kp, kBK);
   pt.tiles = (int64_t)cp.G * cp.n * pt.ntile;
   const int64_t blocks = cdiv(pt.tiles, 8) * 8 * pt.nmb;
   return blocks < ((int64_t)1 << 31);
+}
+
+// the parameters the kernels see: the transposed form's GEMM has M/group * 4
+// columns per group
+ConvParams gemm_params(const ConvParams& cp) {
+  ConvParams q = cp;
+  if (patch_of(cp) == 3) q.Mg *= 4;
+  return q;
 }
 
 int launch_repack(const ConvParams& cp, const PwTile& pt, const RunArgs& a) {
@@ -420,22 +478,26 @@ int launch_repack(const ConvParams& cp, const PwTile& pt, const RunArgs& a) {
 int FC_CAT(launch_pointwise_act_, FC_ACT)(const Geometry& g, const RunArgs& a) {
   PwTile pt;
   if (!choose(g.cp, g.dtype, pt)) return FUSEDCONV_ERR_ROUTE;
+  const ConvParams cq = gemm_params(g.cp);
   if (!(a.flags & FUSEDCONV_RUN_WEIGHTS_PREPARED)) {
-    const int rc = launch_repack(g.cp, pt, a);
+    const int rc = launch_repack(cq, pt, a);
     if (rc != FUSEDCONV_OK) return rc;
   }
   const int64_t blocks = cdiv(pt.tiles, 8) * 8 * pt.nmb;
-  const bool p1 = patch_of(g.cp) == 1;
+  const int patch = patch_of(g.cp);
   const half_t *x = (const half_t*)a.x, *wf = (const half_t*)a.ws, *b = (const half_t*)a.bias,
                *z = (const half_t*)a.z;
   half_t* y = (half_t*)a.y;
   const hipStream_t st = (hipStream_t)a.stream;
+  const dim3 grid((unsigned)blocks);
   if (pt.nwm == 2) {
-    if (p1) hipLaunchKernelGGL((pw_kernel<FC_ACT, 1, 2>), dim3((unsigned)blocks), dim3(384), kLds, st, x, wf, b, z, y, g.cp, pt);
-    else hipLaunchKernelGGL((pw_kernel<FC_ACT, 2, 2>), dim3((unsigned)blocks), dim3(384), kLds, st, x, wf, b, z, y, g.cp, pt);
+    if (patch == 1) hipLaunchKernelGGL((pw_kernel<FC_ACT, 1, 2>), grid, dim3(384), kLds, st, x, wf, b, z, y, cq, pt);
+    else if (patch == 2) hipLaunchKernelGGL((pw_kernel<FC_ACT, 2, 2>), grid, dim3(384), kLds, st, x, wf, b, z, y, cq, pt);
+    else hipLaunchKernelGGL((pw_kernel<FC_ACT, 3, 2>), grid, dim3(384), kLds, st, x, wf, b, z, y, cq, pt);
   } else {
-    if (p1) hipLaunchKernelGGL((pw_kernel<FC_ACT, 1, 4>), dim3((unsigned)blocks), dim3(640), kLds, st, x, wf, b, z, y, g.cp, pt);
-    else hipLaunchKernelGGL((pw_kernel<FC_ACT, 2, 4>), dim3((unsigned)blocks), dim3(640), kLds, st, x, wf, b, z, y, g.cp, pt);
+    if (patch == 1) hipLaunchKernelGGL((pw_kernel<FC_ACT, 1, 4>), grid, dim3(640), kLds, st, x, wf, b, z, y, cq, pt);
+    else if (patch == 2) hipLaunchKernelGGL((pw_kernel<FC_ACT, 2, 4>), grid, dim3(640), kLds, st, x, wf, b, z, y, cq, pt);
+    else hipLaunchKernelGGL((pw_kernel<FC_ACT, 3, 4>), grid, dim3(640), kLds, st, x, wf, b, z, y, cq, pt);
   }
   return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
 }
@@ -456,7 +518,7 @@ bool pointwise_fits(const ConvParams& cp, int32_t dtype, size_t* workspace, int3
 int prepare_pointwise(const Geometry& g, const Plan&, const RunArgs& a) {
   PwTile pt;
   if (!choose(g.cp, g.dtype, pt)) return FUSEDCONV_ERR_ROUTE;
-  return launch_repack(g.cp, pt, a);
+  return launch_repack(gemm_params(g.cp), pt, a);
 }
 
 int launch_pointwise(const Geometry& g, const Plan&, const RunArgs& a) {

@@ -6,7 +6,8 @@
 // output is written once, with the fused epilogue (bias, residual,
 // activation; fp32 accumulation, one rounding).  A plain kernel: it
 // re-reads X for every output channel and skips the (stride - 1)/stride of
-// the taps that do not land; a phase-split GEMM form is the fast path.
+// the taps that do not land.  Transposed 2x2 convolutions with stride 2 (no
+// cropping) run as a GEMM on the pointwise kernel instead.
 #include <hip/hip_runtime.h>
 
 #include "epilogue.h"
@@ -81,7 +82,8 @@ int launch(const Geometry& g, const RunArgs& a) {
 
 }  // namespace
 
-int launch_transposed(const Geometry& g, const Plan&, const RunArgs& a) {
+int launch_transposed(const Geometry& g, const Plan& p, const RunArgs& a) {
+  if (p.tile == 1) return launch_pointwise(g, p, a);  // 2x2 stride 2: the GEMM form
   return g.dtype == FUSEDCONV_F16 ? launch<half_t>(g, a) : launch<float>(g, a);
 }
 

@@ -97,8 +97,18 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
       return FUSEDCONV_ERR_ROUTE;
     }
     p.route = FUSEDCONV_ROUTE_TRANSPOSED;
-    snprintf(p.name, sizeof(p.name), "transposed_gather_%s",
-             g.dtype == FUSEDCONV_F16 ? "f16" : "f32");
+    size_t ws = 0;
+    int32_t bmt = 0;
+    if (pointwise_fits(cp, g.dtype, &ws, nullptr, &bmt)) {
+      // 2x2 stride 2 without cropping: the pointwise GEMM kernel's transposed form
+      p.tile = 1;
+      p.workspace = ws;
+      snprintf(p.name, sizeof(p.name), "transposed_2x2s2_pointwise_f16_m%d", (int)bmt);
+    } else {
+      p.tile = 0;
+      snprintf(p.name, sizeof(p.name), "transposed_gather_%s",
+               g.dtype == FUSEDCONV_F16 ? "f16" : "f32");
+    }
     return FUSEDCONV_OK;
   }
   int32_t th = 0, tw = 0;

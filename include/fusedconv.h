@@ -72,7 +72,12 @@ typedef enum fusedconv_dtype {
  *   TRANSPOSED the route of transposed convolutions (handles made with
  *              fusedconv_create_transposed), and their only one: one output
  *              element per lane, gathering the input elements and taps that
- *              scatter into it; fp32 and fp16.
+ *              scatter into it; fp32 and fp16.  fp16 2-D 2x2 stride-2
+ *              transposed convolutions with dilation 1, no leading pad, an
+ *              output of exactly twice the input, W a multiple of 8 and
+ *              C/group a multiple of 8 (>= 16) run instead as an MFMA GEMM
+ *              (input pixels x (output channel, 2x2 phase)) with a workspace
+ *              for the repacked weights.
  */
 typedef enum fusedconv_route {
   FUSEDCONV_ROUTE_AUTO = 0,
@@ -224,7 +229,8 @@ int fusedconv_run(const fusedconv_handle* h, const void* x, const void* w, const
  * (inference): fusedconv_prepare_weights enqueues only the route's weight
  * preparation (for IGEMM_HALO a repack of W into the tap-major layout held in
  * the workspace, for SMALLC a repack into rows of 8 kernel columns, for
- * POINTWISE a repack into MFMA fragment order; a no-op for the other
+ * POINTWISE (and the GEMM form of TRANSPOSED) a repack into MFMA fragment
+ * order; a no-op for the other
  * routes), and fusedconv_run_ex with
  * FUSEDCONV_RUN_WEIGHTS_PREPARED then skips that step and reads the prepared
  * weights from the workspace.  The caller guarantees that the workspace holds

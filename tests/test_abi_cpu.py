@@ -287,3 +287,26 @@ def test_transposed_handles():
     with pytest.raises(B.FusedConvError) as e:   # the TRANSPOSED route needs a transposed conv
         B.Handle("f16", [1, 4, 5, 5], [4, 4, 3, 3], None, None, route="transposed")
     assert e.value.status == "FUSEDCONV_ERR_ROUTE"
+
+
+def test_transposed_gemm_form_limits():
+    # 2x2 stride 2 with no leading pad and an output of exactly 2H x 2W takes
+    # the GEMM form; anything else the gather kernel
+    gemm = [([1, 48, 5, 24], [48, 40, 2, 2], dict(pads=[0, 0, 1, 1], output_padding=[1, 1])),
+            ([2, 64, 8, 8], [64, 12, 2, 2], dict(group=2)),
+            ([1, 16, 16, 32], [16, 200, 2, 2], {})]
+    for xs, ws, kw in gemm:
+        h = B.Handle("f16", xs, ws, None, None, transposed=True, strides=[2, 2], **kw)
+        assert h.kernel_name.startswith("transposed_2x2s2_pointwise_f16_m"), (xs, ws, kw)
+        assert h.workspace_bytes > 0
+    gather = [("f32", [1, 16, 8, 8], [16, 8, 2, 2], {}),
+              ("f16", [1, 16, 8, 12], [16, 8, 2, 2], {}),                 # W % 8 != 0
+              ("f16", [1, 16, 8, 8], [16, 8, 2, 2], dict(pads=[1, 1, 1, 1])),
+              ("f16", [1, 16, 8, 8], [16, 8, 2, 2], dict(output_padding=[1, 1])),
+              ("f16", [1, 12, 8, 8], [12, 8, 2, 2], {}),                  # C/group % 8 != 0
+              ("f16", [1, 8, 8, 8], [8, 8, 2, 2], {}),                    # C/group < 16
+              ("f16", [1, 16, 8, 8], [16, 8, 2, 2], dict(dilations=[2, 2]))]
+    for dt, xs, ws, kw in gather:
+        h = B.Handle(dt, xs, ws, None, None, transposed=True, strides=[2, 2], **kw)
+        assert h.kernel_name.startswith("transposed_gather"), (dt, xs, ws, kw, h.kernel_name)
+        assert h.workspace_bytes == 0

@@ -616,6 +616,12 @@ TRANSPOSED_CASES = [
                                                   pads=[0, 1, 0, 1, 0, 1], output_padding=[0, 1, 1])),
     ("f16", [2, 32, 12, 16], [32, 24, 2, 2], dict(strides=[2, 2])),           # patch upsampling
     ("f16", [1, 16, 9, 11], [16, 8, 3, 3], dict(strides=[1, 1], pads=[1, 1, 1, 1])),
+    # the GEMM form (2x2 stride 2): ragged pixel tiles and column blocks,
+    # cropped output_padding, groups, 256-column blocks
+    ("f16", [1, 48, 5, 24], [48, 40, 2, 2], dict(strides=[2, 2], pads=[0, 0, 1, 1],
+                                                 output_padding=[1, 1])),
+    ("f16", [2, 64, 8, 8], [64, 12, 2, 2], dict(group=2, strides=[2, 2])),
+    ("f16", [1, 16, 16, 32], [16, 200, 2, 2], dict(strides=[2, 2])),
 ]
 
 
@@ -630,7 +636,27 @@ def test_transposed_route(ci):
                                     h.y_shape if resid else None, dist="normal",
                                     w_std=1.0 / np.sqrt(ws[0]))
         a = dict(attrs, activation=act, activation_params=f32params(params))
-        log(f"CASE transposed {ci} x={xs} w={ws} {a} bias={bias} z={resid}")
+        log(f"CASE transposed {ci} {h.kernel_name} x={xs} w={ws} {a} bias={bias} z={resid}")
         got = run_gpu(x, w, b, z, transposed=True, **a)
         ref = oracle.conv_transpose(x, w, b, z, **a)
         check(got, ref, dtype, f"transposed case {ci}")
+
+
+def test_transposed_gemm_form_prepared_weights():
+    # the GEMM form with weights prepared once and reused
+    xs, ws = [2, 32, 6, 16], [32, 24, 2, 2]
+    h = B.Handle("f16", xs, ws, [24], None, transposed=True, strides=[2, 2], activation="Relu")
+    assert h.kernel_name.startswith("transposed_2x2s2_pointwise"), h.kernel_name
+    x, w, b, _ = random_tensors([9510], "f16", xs, ws, [24], None, dist="normal")
+    dx, dw, db = dev(x), dev(w), dev(b)
+    y = torch.empty(h.y_shape, dtype=torch.float16, device="cuda")
+    wsb = torch.empty(h.workspace_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    h.prepare_weights(dw.data_ptr(), wsb.data_ptr(), h.workspace_bytes, stream)
+    ref = oracle.conv_transpose(x, w, b, strides=[2, 2], activation="Relu")
+    for _ in range(2):
+        y.zero_()
+        h.run(dx.data_ptr(), dw.data_ptr(), db.data_ptr(), None, y.data_ptr(), wsb.data_ptr(),
+              h.workspace_bytes, stream, flags=B.RUN_WEIGHTS_PREPARED)
+        torch.cuda.synchronize()
+        check(y.cpu().numpy(), ref, "f16", "transposed prepared")
