@@ -1,4 +1,6 @@
-// Transposed convolution, gather form: one output element per lane.  Output
+// Transposed convolution, gather form (the ExecuTorch WebGPU convolution pull
+// request, Implementation: the transposed kernel inverts the scatter as a
+// gather and reads W un-flipped as [C, M/group, k...]): one output per lane.  Output
 // y at position o of channel m (group g) receives X[n, c, i] * W[c, m', k]
 // for every input channel c of group g and every kernel tap k whose input
 // coordinate i = (o + pad_begin - k*dilation) / stride is an integer inside
