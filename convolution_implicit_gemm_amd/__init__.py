@@ -28,6 +28,11 @@ class FusedConv:
 
     def __init__(self, x_shape, w_shape, dtype, has_bias=False, has_z=False, **attrs):
         self.attrs = attrs
+        self.x_shape = [int(v) for v in x_shape]
+        self.w_shape = [int(v) for v in w_shape]
+        self.dtype = dtype
+        self.has_bias = bool(has_bias)
+        self.has_z = bool(has_z)
         # B has M entries: W.shape[0], or W.shape[1] * group for a transposed conv
         m = w_shape[1] * attrs.get("group", 1) if attrs.get("transposed") else w_shape[0]
         z_shape = None
@@ -35,6 +40,7 @@ class FusedConv:
             # Z must have Y's shape; resolve Y first with a probe handle.
             z_shape = Handle(dtype, x_shape, w_shape, [m] if has_bias else None,
                              None, **attrs).y_shape
+        self.m = int(m)
         self.handle = Handle(dtype, x_shape, w_shape, [m] if has_bias else None,
                              z_shape, **attrs)
         self.y_shape = self.handle.y_shape
@@ -43,20 +49,59 @@ class FusedConv:
     def prepare_weights(self, w, workspace, stream=None):
         """Enqueue only the weight preparation of this plan into `workspace`."""
         import torch
+        if not w.is_cuda or list(w.shape) != self.w_shape or not w.is_contiguous():
+            raise ValueError(f"w must be a contiguous device tensor of shape {self.w_shape}")
+        if self.workspace_bytes and (workspace is None or not workspace.is_cuda or
+                                     workspace.numel() * workspace.element_size()
+                                     < self.workspace_bytes):
+            raise FusedConvError(-14, f"prepare_weights needs a device workspace of "
+                                      f"{self.workspace_bytes} bytes")
         st = stream if stream is not None else torch.cuda.current_stream(w.device).cuda_stream
         self.handle.prepare_weights(w.data_ptr(), workspace.data_ptr() if workspace is not None
                                     else None, self.workspace_bytes, st)
 
-    def __call__(self, x, w, bias=None, z=None, out=None, workspace=None, stream=None,
-                 weights_prepared=False):
+    def _check(self, x, w, bias, z, out, workspace, weights_prepared):
+        """Raise unless every tensor has the planned shape, dtype and device: the
+        library receives bare pointers and trusts the sizes it planned."""
         import torch
-        for name, t in (("x", x), ("w", w), ("bias", bias), ("z", z), ("out", out)):
+        want = torch.float16 if self.dtype == "f16" else torch.float32
+        shapes = (("x", x, self.x_shape), ("w", w, self.w_shape),
+                  ("bias", bias, [self.m] if self.has_bias else None),
+                  ("z", z, self.y_shape if self.has_z else None), ("out", out, self.y_shape))
+        for name, t, shape in shapes:
             if t is None:
+                if shape is not None and name != "out":
+                    raise ValueError(f"{name} was planned but not given")
                 continue
+            if name in ("bias", "z") and shape is None:
+                raise ValueError(f"{name} given but not planned")
             if not t.is_cuda:
                 raise FusedConvError(-1, f"{name} must be a device tensor (no CPU path)")
             if not t.is_contiguous():
                 raise FusedConvError(-1, f"{name} must be contiguous")
+            if t.dtype != want:
+                raise ValueError(f"{name} is {t.dtype}, the plan is {want}")
+            if list(t.shape) != list(shape):
+                raise ValueError(f"{name} has shape {list(t.shape)}, the plan expects "
+                                 f"{list(shape)}")
+            if t.device != x.device:
+                raise ValueError(f"{name} is on {t.device}, x on {x.device}")
+        if workspace is not None:
+            if not workspace.is_cuda or workspace.device != x.device:
+                raise FusedConvError(-14, "workspace must be device memory on x's device")
+            if workspace.numel() * workspace.element_size() < self.workspace_bytes:
+                raise FusedConvError(-14, f"workspace holds fewer than {self.workspace_bytes} bytes")
+        elif weights_prepared and self.workspace_bytes:
+            raise FusedConvError(-14, "weights_prepared needs the workspace that "
+                                      "prepare_weights filled")
+
+    def __call__(self, x, w, bias=None, z=None, out=None, workspace=None, stream=None,
+                 weights_prepared=False, events=None):
+        """events: optional (start, stop) torch.cuda.Event pair (timing enabled, each
+        recorded once beforehand so that it exists); the convolution kernels' own
+        dispatches record them (fusedconv_run_timed)."""
+        import torch
+        self._check(x, w, bias, z, out, workspace, weights_prepared)
         y = out if out is not None else torch.empty(self.y_shape, dtype=x.dtype, device=x.device)
         ws = workspace
         if self.workspace_bytes and ws is None:
@@ -67,7 +112,8 @@ class FusedConv:
                         z.data_ptr() if z is not None else None, y.data_ptr(),
                         ws.data_ptr() if ws is not None else None,
                         self.workspace_bytes if ws is not None else 0, st,
-                        1 if weights_prepared else 0)
+                        1 if weights_prepared else 0,
+                        None if events is None else (events[0].cuda_event, events[1].cuda_event))
         return y
 
 

@@ -33,7 +33,8 @@ STATUS = {
 EXPORTS = ["fusedconv_desc_init", "fusedconv_create", "fusedconv_create_transposed",
            "fusedconv_output_shape",
            "fusedconv_workspace_size", "fusedconv_plan_info", "fusedconv_run",
-           "fusedconv_prepare_weights", "fusedconv_run_ex", "fusedconv_destroy",
+           "fusedconv_prepare_weights", "fusedconv_run_ex", "fusedconv_run_timed",
+           "fusedconv_destroy",
            "fusedconv_status_string", "fusedconv_last_error"]
 RUN_WEIGHTS_PREPARED = 1
 
@@ -104,6 +105,9 @@ def load():
         lib.fusedconv_run_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                          ctypes.c_uint, vp]
         lib.fusedconv_run_ex.restype = ctypes.c_int
+        lib.fusedconv_run_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                            ctypes.c_uint, vp, vp, vp]
+        lib.fusedconv_run_timed.restype = ctypes.c_int
         lib.fusedconv_destroy.argtypes = [vp]
         lib.fusedconv_destroy.restype = None
         lib.fusedconv_status_string.argtypes = [ctypes.c_int]
@@ -195,10 +199,17 @@ class Handle:
         self.split_k = s.value
         self.kernel_name = name.value.decode()
 
-    def run(self, x, w, bias, z, y, workspace, workspace_bytes, stream, flags=0):
-        """Raw device pointers (ints or None); stream is a hipStream_t as int (0 = default)."""
-        rc = self._lib.fusedconv_run_ex(self._h, x, w, bias, z, y, workspace, workspace_bytes,
-                                        flags, stream)
+    def run(self, x, w, bias, z, y, workspace, workspace_bytes, stream, flags=0, events=None):
+        """Raw device pointers (ints or None); stream is a hipStream_t as int (0 = default).
+        events: optional (start, stop) hipEvent_t handles recorded by the convolution
+        kernels' dispatches (fusedconv_run_timed)."""
+        if events is not None:
+            rc = self._lib.fusedconv_run_timed(self._h, x, w, bias, z, y, workspace,
+                                               workspace_bytes, flags, stream, events[0],
+                                               events[1])
+        else:
+            rc = self._lib.fusedconv_run_ex(self._h, x, w, bias, z, y, workspace,
+                                            workspace_bytes, flags, stream)
         if rc != 0:
             raise FusedConvError(rc, self._lib.fusedconv_last_error().decode())
 

@@ -4,8 +4,11 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <new>
+#include <set>
 #include <string>
+#include <tuple>
 
 #include "internal.h"
 
@@ -27,10 +30,20 @@ int set_err(int code, const std::string& msg) {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_dev_ok[kMaxDevices];
 
-int check_device() {
+// The current device must be a gfx950 GPU, and a non-default stream must
+// belong to it (kernels are launched for the current device).
+int check_device(void* stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
     return set_err(FUSEDCONV_ERR_DEVICE, "no current HIP device");
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess)
+      return set_err(FUSEDCONV_ERR_DEVICE, "hipStreamGetDevice failed for the given stream");
+    if (sdev != dev)
+      return set_err(FUSEDCONV_ERR_DEVICE, "the stream belongs to device " + std::to_string(sdev) +
+                                               ", the current device is " + std::to_string(dev));
+  }
   int st = g_dev_ok[dev].load(std::memory_order_relaxed);
   if (st == 0) {
     hipDeviceProp_t prop;
@@ -46,6 +59,24 @@ int check_device() {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
+
+namespace fc {
+
+int set_max_dynamic_lds(const void* kfn, int bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FUSEDCONV_ERR_LAUNCH;
+  static std::mutex mu;
+  static std::set<std::tuple<const void*, int, int>> done;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(kfn, dev, bytes);
+  if (done.count(key)) return FUSEDCONV_OK;
+  if (hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+    return FUSEDCONV_ERR_LAUNCH;
+  done.insert(key);
+  return FUSEDCONV_OK;
+}
+
+}  // namespace fc
 
 extern "C" {
 
@@ -135,7 +166,7 @@ int fusedconv_prepare_weights(const fusedconv_handle* h, const void* w, void* wo
                   (h->plan.route == FUSEDCONV_ROUTE_TRANSPOSED && h->plan.tile == 1);
   if (h->plan.route != FUSEDCONV_ROUTE_IGEMM_HALO && h->plan.route != FUSEDCONV_ROUTE_SMALLC && !pw)
     return FUSEDCONV_OK;
-  int rc = check_device();
+  int rc = check_device(stream);
   if (rc != FUSEDCONV_OK) return rc;
   (void)hipGetLastError();
   fc::RunArgs a{nullptr, w, nullptr, nullptr, nullptr, workspace, stream, 0u};
@@ -152,7 +183,17 @@ int fusedconv_prepare_weights(const fusedconv_handle* h, const void* w, void* wo
 int fusedconv_run_ex(const fusedconv_handle* h, const void* x, const void* w, const void* bias,
                      const void* z, void* y, void* workspace, size_t workspace_bytes,
                      unsigned flags, void* stream) {
+  return fusedconv_run_timed(h, x, w, bias, z, y, workspace, workspace_bytes, flags, stream,
+                             nullptr, nullptr);
+}
+
+int fusedconv_run_timed(const fusedconv_handle* h, const void* x, const void* w,
+                        const void* bias, const void* z, void* y, void* workspace,
+                        size_t workspace_bytes, unsigned flags, void* stream, void* start_event,
+                        void* stop_event) {
   if (!h || !x || !w || !y) return set_err(FUSEDCONV_ERR_NULL_ARG, "h, x, w and y are required");
+  if (!start_event != !stop_event)
+    return set_err(FUSEDCONV_ERR_NULL_ARG, "give both timing events or neither");
   const fc::ConvParams& cp = h->geo.cp;
   if (cp.has_bias && !bias) return set_err(FUSEDCONV_ERR_NULL_ARG, "bias declared but NULL");
   if (!cp.has_bias && bias)
@@ -165,12 +206,12 @@ int fusedconv_run_ex(const fusedconv_handle* h, const void* x, const void* w, co
   if (h->plan.workspace > 0 && (!workspace || workspace_bytes < h->plan.workspace))
     return set_err(FUSEDCONV_ERR_WORKSPACE,
                    "workspace smaller than fusedconv_workspace_size() reports");
-  int rc = check_device();
+  int rc = check_device(stream);
   if (rc != FUSEDCONV_OK) return rc;
   (void)hipGetLastError();  // drop a stale error so a launch failure is reported as ours
   if (flags & ~FUSEDCONV_RUN_WEIGHTS_PREPARED)
     return set_err(FUSEDCONV_ERR_ATTR_VALUE, "unknown run flags");
-  fc::RunArgs a{x, w, bias, z, y, workspace, stream, flags};
+  fc::RunArgs a{x, w, bias, z, y, workspace, stream, flags, start_event, stop_event};
   switch (h->plan.route) {
     case FUSEDCONV_ROUTE_DIRECT: rc = fc::launch_direct(h->geo, h->plan, a); break;
     case FUSEDCONV_ROUTE_IGEMM: rc = fc::launch_igemm(h->geo, h->plan, a); break;

@@ -42,4 +42,13 @@ struct ConvParams {
   int32_t transposed;
 };
 
+// True when the depth axis is trivial, i.e. the problem is really 1-D or 2-D:
+// one input and one output plane, a one-tap kernel and no depth pad.  Only
+// then does output plane 0 read input plane 0; a 3-D problem with D = KD = 1
+// can still have several output planes (end pads, output_padding) or read
+// the zero padding (a begin pad), which the 2-D-only kernels cannot express.
+inline bool depth_trivial(const ConvParams& cp) {
+  return cp.D == 1 && cp.KD == 1 && cp.OD == 1 && cp.pd == 0;
+}
+
 }  // namespace fc

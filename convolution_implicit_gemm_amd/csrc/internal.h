@@ -56,7 +56,13 @@ struct RunArgs {
   void* ws;
   void* stream;
   unsigned flags;   // FUSEDCONV_RUN_WEIGHTS_PREPARED
+  void* ev_start;   // timed run: hipEvent_t recorded at the first convolution kernel's begin
+  void* ev_stop;    // and at the last one's end (both NULL otherwise)
 };
+
+// Raise kernel kfn's dynamic-LDS limit to `bytes` on the current device,
+// once per (kernel, device, bytes); safe to call from several threads.
+int set_max_dynamic_lds(const void* kfn, int bytes);
 
 int launch_direct(const Geometry& g, const Plan& p, const RunArgs& a);
 int launch_igemm(const Geometry& g, const Plan& p, const RunArgs& a);

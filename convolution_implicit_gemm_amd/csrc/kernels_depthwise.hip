@@ -17,6 +17,7 @@
 
 #include "epilogue.h"
 #include "internal.h"
+#include "launch.h"
 
 namespace fc {
 namespace {
@@ -173,7 +174,7 @@ bool dw_fast_try(const ConvParams& cp, int kR, int kV, DwFast& f) {
 // Pick the lane block (rows x columns per lane) with the least padded output
 // and then the larger block (fewer windows and index computations per output).
 bool dw_fast_plan(const ConvParams& cp, DwFast& f) {
-  if (cp.sh != 1 || cp.sw != 1 || cp.D != 1 || cp.KD != 1) return false;
+  if (cp.sh != 1 || cp.sw != 1 || !depth_trivial(cp)) return false;
   if (!((cp.KH == 3 || cp.KH == 5 || cp.KH == 7) && cp.KW == cp.KH)) return false;
   // 4 x 4 measured fastest on the 56 x 56 planes (4 x 8 needs ~200 registers
   // and halves occupancy; 8 x 8 does not fully unroll and spills)
@@ -386,10 +387,9 @@ int launch_fast(const Geometry& g, const DwFast& f, const RunArgs& a) {
   const ConvParams& cp = g.cp;
   const int64_t blocks = (cp.n * cp.M + f.pb - 1) / f.pb;
   const size_t shmem = (size_t)f.pb * f.plane_halves * 2;
-  hipLaunchKernelGGL((dw_fast_kernel<KS, R, V, FC_ACT>), dim3((unsigned)blocks), dim3(kThreads), shmem,
-                     (hipStream_t)a.stream, (const half_t*)a.x, (const half_t*)a.w,
+  return launch_conv(dw_fast_kernel<KS, R, V, FC_ACT>, dim3((unsigned)blocks), dim3(kThreads), shmem,
+                     a, kEdgeBoth, (const half_t*)a.x, (const half_t*)a.w,
                      (const half_t*)a.bias, (const half_t*)a.z, (half_t*)a.y, cp, f);
-  return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
 }
 
 template <typename T>
@@ -399,10 +399,9 @@ int launch_t(const Geometry& g, const Plan& p, const RunArgs& a) {
   const int tiles_w = (cp.OW + p.tile_w - 1) / p.tile_w;
   const int64_t blocks = cp.n * cp.M * tiles_h * tiles_w;
   const size_t shmem = (size_t)halo_bytes(cp, p.tile_h, p.tile_w);
-  hipLaunchKernelGGL(depthwise_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), shmem,
-                     (hipStream_t)a.stream, (const T*)a.x, (const T*)a.w, (const T*)a.bias,
+  return launch_conv(depthwise_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), shmem, a,
+                     kEdgeBoth, (const T*)a.x, (const T*)a.w, (const T*)a.bias,
                      (const T*)a.z, (T*)a.y, cp, p.tile_h, p.tile_w, tiles_h, tiles_w);
-  return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -427,7 +426,7 @@ int FC_CAT(launch_dwfast_act_, FC_ACT)(const Geometry& g, const RunArgs& a) {
 FC_ACT_DECLS(launch_dwfast_act_)
 
 bool depthwise_fits(const ConvParams& cp, int32_t& tile_h, int32_t& tile_w) {
-  if (cp.Cg != 1 || cp.D != 1 || cp.KD != 1) return false;
+  if (cp.Cg != 1 || !depth_trivial(cp)) return false;
   int tw = cp.OW < 256 ? cp.OW : 256;
   int th = 4096 / tw;
   if (th < 1) th = 1;

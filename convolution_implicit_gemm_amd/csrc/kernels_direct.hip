@@ -7,6 +7,7 @@
 
 #include "epilogue.h"
 #include "internal.h"
+#include "launch.h"
 
 namespace fc {
 namespace {
@@ -63,10 +64,8 @@ int launch(const Geometry& g, const RunArgs& a) {
   const int64_t total = cp.n * cp.M * cp.out_sz;
   int64_t blocks = (total + kThreads - 1) / kThreads;
   if (blocks > (1 << 22)) blocks = 1 << 22;
-  hipLaunchKernelGGL(direct_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                     (hipStream_t)a.stream, (const T*)a.x, (const T*)a.w, (const T*)a.bias,
-                     (const T*)a.z, (T*)a.y, cp);
-  return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
+  return launch_conv(direct_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), 0, a, kEdgeBoth,
+                     (const T*)a.x, (const T*)a.w, (const T*)a.bias, (const T*)a.z, (T*)a.y, cp);
 }
 
 }  // namespace

@@ -48,6 +48,7 @@
 
 #include "epilogue.h"
 #include "internal.h"
+#include "launch.h"
 #include "sync.h"
 
 namespace fc {
@@ -87,7 +88,7 @@ struct DwMfma {
 };
 
 bool dwm_try(const ConvParams& cp, DwMfma& f) {
-  if (cp.Cg != 1 || cp.D != 1 || cp.KD != 1 || cp.sh != 1 || cp.sw != 1) return false;
+  if (cp.Cg != 1 || !depth_trivial(cp) || cp.sh != 1 || cp.sw != 1) return false;
   if (!(cp.KH == 3 || cp.KH == 5 || cp.KH == 7)) return false;
   if (!(cp.dh == 1 || cp.dh == 2)) return false;
   if (cp.W % 8 != 0 || cp.OW % 8 != 0) return false;
@@ -382,10 +383,9 @@ void dwm_kernel(const half_t* __restrict__ x, const half_t* __restrict__ w,
 template <int KH, int DH>
 int launch_kh(const Geometry& g, const DwMfma& f, const RunArgs& a) {
   const ConvParams& cp = g.cp;
-  hipLaunchKernelGGL((dwm_kernel<KH, DH, FC_ACT>), dim3((unsigned)(f.k * cp.M)), dim3(kThreads),
-                     (size_t)f.lds, (hipStream_t)a.stream, (const half_t*)a.x, (const half_t*)a.w,
+  return launch_conv(dwm_kernel<KH, DH, FC_ACT>, dim3((unsigned)(f.k * cp.M)), dim3(kThreads),
+                     (size_t)f.lds, a, kEdgeBoth, (const half_t*)a.x, (const half_t*)a.w,
                      (const half_t*)a.bias, (const half_t*)a.z, (half_t*)a.y, cp, f);
-  return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
 }
 
 }  // namespace

@@ -33,6 +33,7 @@
 
 #include "epilogue.h"
 #include "internal.h"
+#include "launch.h"
 #include "sync.h"
 
 namespace fc {
@@ -694,25 +695,17 @@ int launch_repack(const ConvParams& cp, const Choice& ch, const RunArgs& a) {
 template <int BM, int BN, int PF, bool VEC, int NWM>
 int launch_t(const Geometry& g, const Choice& ch, const RunArgs& a) {
   const ConvParams& cp = g.cp;
-  hipStream_t st = (hipStream_t)a.stream;
   const size_t lds = lds_bytes(ch.ht.box_pos, BN, ch.ht.ldc, 2 * NWM);
   const void* kfn = (const void*)halo_kernel<BM, BN, PF, VEC, NWM, FC_ACT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) !=
-        hipSuccess)
-      return FUSEDCONV_ERR_LAUNCH;
-    attr_set = true;
-  }
+  if (set_max_dynamic_lds(kfn, (int)kMaxLds) != FUSEDCONV_OK) return FUSEDCONV_ERR_LAUNCH;
   if (!(a.flags & FUSEDCONV_RUN_WEIGHTS_PREPARED)) {
     const int rc = launch_repack(cp, ch, a);
     if (rc != FUSEDCONV_OK) return rc;
   }
   const unsigned blocks = (unsigned)((int64_t)ch.ht.ntile * ch.ht.nmb * cp.G);
-  hipLaunchKernelGGL((halo_kernel<BM, BN, PF, VEC, NWM, FC_ACT>), dim3(blocks), dim3(128 * NWM), lds, st,
-                     (const half_t*)a.x, (const half_t*)a.ws, (const half_t*)a.bias,
+  return launch_conv(halo_kernel<BM, BN, PF, VEC, NWM, FC_ACT>, dim3(blocks), dim3(128 * NWM), lds, a,
+                     kEdgeBoth, (const half_t*)a.x, (const half_t*)a.ws, (const half_t*)a.bias,
                      (const half_t*)a.z, (half_t*)a.y, cp, ch.ht);
-  return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
 }
 
 }  // namespace

@@ -23,6 +23,7 @@
 
 #include "epilogue.h"
 #include "internal.h"
+#include "launch.h"
 
 namespace fc {
 namespace {
@@ -318,23 +319,20 @@ int launch_t(const Geometry& g, const Plan& p, const RunArgs& a) {
   dim3 grid((unsigned)((cp.P + kBN - 1) / kBN), (unsigned)((cp.Mg + BM - 1) / BM),
             (unsigned)(cp.G * p.split_k));
   const int avec = (cp.K % (16 / (int)sizeof(T))) == 0;
-  hipStream_t st = (hipStream_t)a.stream;
   if (split) {
-    hipLaunchKernelGGL((igemm_kernel<T, BM, WGM, true>), grid, dim3(kThreads), 0, st,
-                       (const T*)a.x, (const T*)a.w, (const T*)a.bias, (const T*)a.z, (T*)a.y,
-                       (float*)a.ws, cp, p.k_tiles, p.k_tiles_per_split, avec);
-    if (hipPeekAtLastError() != hipSuccess) return FUSEDCONV_ERR_LAUNCH;
+    if (launch_conv(igemm_kernel<T, BM, WGM, true>, grid, dim3(kThreads), 0, a, kEdgeFirst,
+                    (const T*)a.x, (const T*)a.w, (const T*)a.bias, (const T*)a.z, (T*)a.y,
+                    (float*)a.ws, cp, p.k_tiles, p.k_tiles_per_split, avec) != FUSEDCONV_OK)
+      return FUSEDCONV_ERR_LAUNCH;
     int64_t blocks = ((int64_t)cp.M * cp.P + kThreads - 1) / kThreads;
     if (blocks > (1 << 20)) blocks = 1 << 20;
-    hipLaunchKernelGGL(splitk_reduce_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), 0, st,
-                       (const float*)a.ws, (const T*)a.bias, (const T*)a.z, (T*)a.y, cp,
+    return launch_conv(splitk_reduce_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), 0, a,
+                       kEdgeLast, (const float*)a.ws, (const T*)a.bias, (const T*)a.z, (T*)a.y, cp,
                        p.split_k);
-  } else {
-    hipLaunchKernelGGL((igemm_kernel<T, BM, WGM, false>), grid, dim3(kThreads), 0, st,
-                       (const T*)a.x, (const T*)a.w, (const T*)a.bias, (const T*)a.z, (T*)a.y,
-                       (float*)nullptr, cp, p.k_tiles, p.k_tiles_per_split, avec);
   }
-  return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
+  return launch_conv(igemm_kernel<T, BM, WGM, false>, grid, dim3(kThreads), 0, a, kEdgeBoth,
+                     (const T*)a.x, (const T*)a.w, (const T*)a.bias, (const T*)a.z, (T*)a.y,
+                     (float*)nullptr, cp, p.k_tiles, p.k_tiles_per_split, avec);
 }
 
 }  // namespace

@@ -56,6 +56,7 @@
 
 #include "epilogue.h"
 #include "internal.h"
+#include "launch.h"
 #include "sync.h"
 
 namespace fc {
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t*
 int patch_of(const ConvParams& cp) {
   const bool nopad = cp.pd == 0 && cp.ph == 0 && cp.pw == 0;
   if (cp.transposed)
-    return (cp.D == 1 && cp.KD == 1 && cp.KH == 2 && cp.KW == 2 && cp.sh == 2 && cp.sw == 2 &&
+    return (depth_trivial(cp) && cp.KH == 2 && cp.KW == 2 && cp.sh == 2 && cp.sw == 2 &&
             cp.dh == 1 && cp.dw == 1 && nopad && cp.OH == 2 * cp.H && cp.OW == 2 * cp.W &&
             cp.W % 8 == 0)
                ? 3
@@ -420,7 +421,7 @@ int patch_of(const ConvParams& cp) {
   if (cp.KD == 1 && cp.KH == 1 && cp.KW == 1 && cp.sd == 1 && cp.sh == 1 && cp.sw == 1 && nopad &&
       cp.OD == cp.D && cp.OH == cp.H && cp.OW == cp.W)
     return 1;
-  if (cp.D == 1 && cp.KD == 1 && cp.KH == 2 && cp.KW == 2 && cp.sh == 2 && cp.sw == 2 &&
+  if (depth_trivial(cp) && cp.KH == 2 && cp.KW == 2 && cp.sh == 2 && cp.sw == 2 &&
       cp.dh == 1 && cp.dw == 1 && nopad && cp.OH == cp.H / 2 && cp.OW == cp.W / 2 &&
       cp.OW % 8 == 0 && cp.W % 8 == 0)
     return 2;
@@ -488,18 +489,18 @@ int FC_CAT(launch_pointwise_act_, FC_ACT)(const Geometry& g, const RunArgs& a) {
   const half_t *x = (const half_t*)a.x, *wf = (const half_t*)a.ws, *b = (const half_t*)a.bias,
                *z = (const half_t*)a.z;
   half_t* y = (half_t*)a.y;
-  const hipStream_t st = (hipStream_t)a.stream;
   const dim3 grid((unsigned)blocks);
+  int rc;
   if (pt.nwm == 2) {
-    if (patch == 1) hipLaunchKernelGGL((pw_kernel<FC_ACT, 1, 2>), grid, dim3(384), kLds, st, x, wf, b, z, y, cq, pt);
-    else if (patch == 2) hipLaunchKernelGGL((pw_kernel<FC_ACT, 2, 2>), grid, dim3(384), kLds, st, x, wf, b, z, y, cq, pt);
-    else hipLaunchKernelGGL((pw_kernel<FC_ACT, 3, 2>), grid, dim3(384), kLds, st, x, wf, b, z, y, cq, pt);
+    if (patch == 1) rc = launch_conv(pw_kernel<FC_ACT, 1, 2>, grid, dim3(384), kLds, a, kEdgeBoth, x, wf, b, z, y, cq, pt);
+    else if (patch == 2) rc = launch_conv(pw_kernel<FC_ACT, 2, 2>, grid, dim3(384), kLds, a, kEdgeBoth, x, wf, b, z, y, cq, pt);
+    else rc = launch_conv(pw_kernel<FC_ACT, 3, 2>, grid, dim3(384), kLds, a, kEdgeBoth, x, wf, b, z, y, cq, pt);
   } else {
-    if (patch == 1) hipLaunchKernelGGL((pw_kernel<FC_ACT, 1, 4>), grid, dim3(640), kLds, st, x, wf, b, z, y, cq, pt);
-    else if (patch == 2) hipLaunchKernelGGL((pw_kernel<FC_ACT, 2, 4>), grid, dim3(640), kLds, st, x, wf, b, z, y, cq, pt);
-    else hipLaunchKernelGGL((pw_kernel<FC_ACT, 3, 4>), grid, dim3(640), kLds, st, x, wf, b, z, y, cq, pt);
+    if (patch == 1) rc = launch_conv(pw_kernel<FC_ACT, 1, 4>, grid, dim3(640), kLds, a, kEdgeBoth, x, wf, b, z, y, cq, pt);
+    else if (patch == 2) rc = launch_conv(pw_kernel<FC_ACT, 2, 4>, grid, dim3(640), kLds, a, kEdgeBoth, x, wf, b, z, y, cq, pt);
+    else rc = launch_conv(pw_kernel<FC_ACT, 3, 4>, grid, dim3(640), kLds, a, kEdgeBoth, x, wf, b, z, y, cq, pt);
   }
-  return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
+  return rc;
 }
 
 #if FC_ACT == 0

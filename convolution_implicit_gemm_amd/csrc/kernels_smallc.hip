@@ -26,6 +26,7 @@
 
 #include "epilogue.h"
 #include "internal.h"
+#include "launch.h"
 #include "sync.h"
 
 namespace fc {
@@ -352,7 +353,7 @@ size_t lds_bytes(const ConvParams& cp, const SmallTile& st) {
 }
 
 bool choose(const ConvParams& cp, int32_t dtype, SmallTile& st) {
-  if (dtype != FUSEDCONV_F16 || cp.D != 1 || cp.KD != 1 || cp.dw != 1 || cp.Cg > 15) return false;
+  if (dtype != FUSEDCONV_F16 || !depth_trivial(cp) || cp.dw != 1 || cp.Cg > 15) return false;
   st.nchunk = (cp.KW + 7) / 8;
   st.R = cp.Cg * cp.KH * st.nchunk;
   st.KB = (st.R + 3) / 4;
@@ -403,21 +404,14 @@ int launch_repack(const ConvParams& cp, const SmallTile& st, const RunArgs& a) {
 template <bool A4, bool VEC>
 int launch_t(const ConvParams& cp, const SmallTile& st, const RunArgs& a) {
   const void* kfn = (const void*)smallc_kernel<A4, VEC, FC_ACT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) !=
-        hipSuccess)
-      return FUSEDCONV_ERR_LAUNCH;
-    attr_set = true;
-  }
+  if (set_max_dynamic_lds(kfn, (int)kMaxLds) != FUSEDCONV_OK) return FUSEDCONV_ERR_LAUNCH;
   // persistent: two blocks per CU (256 CUs), each looping over units
   const int64_t units = (int64_t)cp.G * cp.n * st.tiles_h * st.tiles_w * st.nmb;
   const unsigned blocks = (unsigned)(units < kPersistentBlocks ? units : kPersistentBlocks);
-  hipLaunchKernelGGL((smallc_kernel<A4, VEC, FC_ACT>), dim3(blocks), dim3(kThreads),
-                     lds_bytes(cp, st), (hipStream_t)a.stream, (const half_t*)a.x,
+  return launch_conv(smallc_kernel<A4, VEC, FC_ACT>, dim3(blocks), dim3(kThreads),
+                     lds_bytes(cp, st), a, kEdgeBoth, (const half_t*)a.x,
                      (const half_t*)a.ws, (const half_t*)a.bias, (const half_t*)a.z, (half_t*)a.y,
                      cp, st);
-  return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
 }
 
 }  // namespace

@@ -168,9 +168,26 @@ typedef struct fusedconv_handle fusedconv_handle;  /* opaque, host memory only *
 void fusedconv_desc_init(fusedconv_desc* d);
 
 /*
- * Validate and resolve the problem (padding, output dims, activation
- * parameters) and plan the kernels.  Host only: no device call, no device
- * allocation.  On success *out owns a new handle; on failure *out is NULL.
+ * Validate and resolve the problem and plan the kernels.
+ *
+ * Defined by: the FusedConv manifest.json "derive" rules, which give every
+ * check this call makes (spatialAttributesOk and the *RanksOk ranks; the
+ * *LengthOk and *ValuesOk attribute rules; explicitPadsOk;
+ * kernelShapeMatchesWeights; groupOk; biasOk; zOk; activationOk;
+ * activationParamsOk) and the resolved quantities (samePad* for SAME_UPPER /
+ * SAME_LOWER, expectedOutput* for the output dims, actAlpha / actBeta for
+ * the activation defaults); the FusedConv README, "Attributes" table, for
+ * the attribute meanings and defaults.  The plan (route, tile, K split,
+ * workspace bytes) is fixed here, before any device memory exists, as the
+ * ExecuTorch WebGPU conv page's im2col GEMM change computes both dispatch
+ * grids before allocating any buffer, so that a rejected problem leaks
+ * nothing.
+ *
+ * Host only: no device call, no device allocation.  d and everything it
+ * points to are read during the call only.  On success *out owns a new
+ * handle (release it with fusedconv_destroy); on failure *out is NULL and
+ * the code names the first rule that failed (FUSEDCONV_ERR_*), with details
+ * in fusedconv_last_error().
  */
 int fusedconv_create(const fusedconv_desc* d, fusedconv_handle** out);
 
@@ -196,21 +213,49 @@ int fusedconv_create(const fusedconv_desc* d, fusedconv_handle** out);
 int fusedconv_create_transposed(const fusedconv_desc* d, const int64_t* output_padding,
                                 int32_t n_output_padding, fusedconv_handle** out);
 
-/* Y's shape: *rank = rank of X, dims[0..rank) filled. */
+/*
+ * Y's shape, inferred from the inputs and attributes as the FusedConv README
+ * says outputs are ("Use with @huggingface/kernels": output shapes are
+ * inferred and result tensors allocated for the caller; "Outputs": Y has the
+ * rank of X).  The spatial dims are the manifest's expectedOutput* values
+ * (or, for a transposed handle, the adjoint extent stated at
+ * fusedconv_create_transposed); dims[0] = N, dims[1] = M.  *rank = rank of
+ * X; dims[0..rank) are filled and the rest set to 0.  The caller allocates
+ * Y (and Z, which must have this shape) from it.  Errors: NULL argument.
+ */
 int fusedconv_output_shape(const fusedconv_handle* h, int64_t dims[FUSEDCONV_MAX_RANK],
                            int32_t* rank);
 
-/* Device workspace bytes fusedconv_run needs (0 if none). */
+/*
+ * Device workspace bytes fusedconv_run needs (0 if none).  The workspace
+ * holds the intermediates the plan chose: the raw fp32 partial sums of a
+ * split reduction, which the FusedConv README's split-K variants
+ * ("Implementation variants": implicit_im2col_tiled_reg_splitk) write
+ * before one combine applies bias and activation, laid out
+ * [split][M][N * output pixels]; or a route's repacked weights (see
+ * fusedconv_prepare_weights).  The caller allocates it on the device, at
+ * least this size and 16-byte aligned.  Errors: NULL argument.
+ */
 int fusedconv_workspace_size(const fusedconv_handle* h, size_t* bytes);
 
 /*
  * Chosen plan: route (fusedconv_route), K split factor, and a short
  * NUL-terminated kernel name written into name[0..name_len) (may be NULL).
+ * The FusedConv README ("Implementation variants") selects one
+ * implementation per call from the device, the shapes and the dtypes; this
+ * reports which one the planner selected.  Errors: NULL handle.
  */
 int fusedconv_plan_info(const fusedconv_handle* h, int32_t* route, int32_t* split_k, char* name,
                         size_t name_len);
 
 /*
+ * Compute Y = act(conv(X, W) + B + Z) (FusedConv README, "Description",
+ * "Inputs" and "Outputs": B broadcast over each output channel, Z of Y's
+ * shape added before the activation; the manifest's "inputs" / "outputs"
+ * order x, w, bias, zResidual -> y).  Inputs and outputs are caller-owned
+ * device buffers: the library, unlike the README's JavaScript entry point,
+ * allocates nothing, so Y is passed in, sized by fusedconv_output_shape.
+ *
  * Enqueue the computation on `stream` (a hipStream_t; NULL = the default
  * stream) and return without waiting.  x, w, y: device pointers, contiguous,
  * 16-byte aligned.  bias / z: device pointers iff the descriptor declared
@@ -245,7 +290,26 @@ int fusedconv_run_ex(const fusedconv_handle* h, const void* x, const void* w, co
                      const void* z, void* y, void* workspace, size_t workspace_bytes,
                      unsigned flags, void* stream);
 
-/* Release a handle (NULL is allowed). */
+/*
+ * fusedconv_run_ex, with the convolution kernels timed by the device: the
+ * caller's events (hipEvent_t, made with hipEventCreate, timing not
+ * disabled) are recorded by the dispatches themselves, start_event at the
+ * begin of the route's first convolution kernel and stop_event at the end
+ * of its last one (the K-split combine, if any), so hipEventElapsedTime of
+ * the two is the kernels' own duration.  Weight preparation is outside the
+ * interval.  This is the measurement hook of the throughput figures (the
+ * algorithmic FLOP and bytes of one call divided by this duration); it does
+ * not change what is computed.  Both events or neither (then identical to
+ * fusedconv_run_ex); one alone gives FUSEDCONV_ERR_NULL_ARG.  Other
+ * arguments and errors as for fusedconv_run_ex.
+ */
+int fusedconv_run_timed(const fusedconv_handle* h, const void* x, const void* w,
+                        const void* bias, const void* z, void* y, void* workspace,
+                        size_t workspace_bytes, unsigned flags, void* stream, void* start_event,
+                        void* stop_event);
+
+/* Release a handle (NULL is allowed).  Host memory only; runs already
+ * enqueued with it are unaffected (the kernels received everything by value). */
 void fusedconv_destroy(fusedconv_handle* h);
 
 /* Static text for a status code. */

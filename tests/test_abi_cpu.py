@@ -310,3 +310,55 @@ def test_transposed_gemm_form_limits():
         h = B.Handle(dt, xs, ws, None, None, transposed=True, strides=[2, 2], **kw)
         assert h.kernel_name.startswith("transposed_gather"), (dt, xs, ws, kw, h.kernel_name)
         assert h.workspace_bytes == 0
+
+
+# 3-D problems whose depth axis has one input plane and a one-tap kernel, but
+# several output planes (an end pad or output_padding) or a leading depth pad:
+# the kernels written for 1-D and 2-D problems compute output plane 0 from
+# input plane 0 only, so the planner must send these to a route that handles
+# the depth axis (direct, igemm, the halo route, the transposed gather).
+DEPTH_ONE_CASES = [
+    # (dtype, x, w, attrs)
+    ("f16", [2, 16, 1, 16, 16], [32, 16, 1, 2, 2], dict(strides=[1, 2, 2], pads=[0, 0, 0, 1, 0, 0])),
+    ("f16", [2, 16, 1, 56, 56], [16, 1, 1, 7, 7], dict(group=16, pads=[0, 3, 3, 1, 3, 3])),
+    ("f16", [2, 16, 1, 56, 58], [16, 1, 1, 7, 7], dict(group=16, pads=[1, 3, 3, 0, 3, 3])),
+    ("f32", [2, 16, 1, 20, 20], [16, 1, 1, 3, 3], dict(group=16, pads=[0, 1, 1, 2, 1, 1])),
+    ("f16", [2, 3, 1, 64, 64], [32, 3, 1, 7, 7], dict(strides=[1, 4, 4], pads=[0, 3, 3, 1, 3, 3])),
+    ("f16", [2, 3, 1, 64, 64], [32, 3, 1, 7, 7], dict(strides=[2, 4, 4], pads=[1, 3, 3, 0, 3, 3])),
+    ("f16", [2, 64, 1, 8, 8], [64, 64, 1, 1, 1], dict(pads=[0, 0, 0, 1, 0, 0])),
+]
+SPECIALISED_2D = ("depthwise", "smallc", "pointwise")
+
+
+@pytest.mark.parametrize("ci", range(len(DEPTH_ONE_CASES)))
+def test_depth_one_3d_problems_avoid_2d_only_kernels(ci):
+    dt, xs, ws, kw = DEPTH_ONE_CASES[ci]
+    h = _h(xs, ws, dtype=dt, **kw)
+    ref = oracle.output_dims(xs[2:], ws[2:], kw.get("strides"), None, "NOTSET", kw.get("pads"))
+    assert h.y_shape[2:] == ref[0]
+    assert h.y_shape[2] > 1 or ref[1][0] > 0, "the case must exercise the depth axis"
+    assert h.route not in SPECIALISED_2D, (ci, h.route, h.kernel_name)
+    for route in SPECIALISED_2D:
+        with pytest.raises(B.FusedConvError) as e:
+            _h(xs, ws, dtype=dt, route=route, **kw)
+        assert e.value.status == "FUSEDCONV_ERR_ROUTE", (ci, route)
+    # the same shapes with a trivial depth axis do take a specialised kernel
+    # where one fits (the guard must not turn them away)
+    if ci in (0, 1, 4):
+        kw2 = dict(kw, pads=[0] + kw["pads"][1:3] + [0] + kw["pads"][4:6])
+        if "strides" in kw2:
+            kw2["strides"] = [1] + kw2["strides"][1:]
+        h2 = _h(xs, ws, dtype=dt, **kw2)
+        assert h2.route in SPECIALISED_2D, (ci, h2.route)
+
+
+def test_depth_one_transposed_output_padding_takes_the_gather_kernel():
+    # output_padding on the depth axis makes two output planes
+    h = B.Handle("f16", [1, 32, 1, 8, 8], [32, 16, 1, 2, 2], None, None, transposed=True,
+                 strides=[2, 2, 2], output_padding=[1, 0, 0])
+    assert h.y_shape == [1, 16, 2, 16, 16]
+    assert h.kernel_name.startswith("transposed_gather"), h.kernel_name
+    h = B.Handle("f16", [1, 32, 1, 8, 8], [32, 16, 1, 2, 2], None, None, transposed=True,
+                 strides=[2, 2, 2])
+    assert h.y_shape == [1, 16, 1, 16, 16]
+    assert h.kernel_name.startswith("transposed_2x2s2_pointwise"), h.kernel_name
