@@ -342,6 +342,8 @@ SMALLC_CASES = [
     ([1, 3, 30, 30], [16, 3, 3, 3], dict(dilations=[2, 1])),                   # dilated rows
     ([1, 3, 32, 32], [200, 3, 3, 3], dict(pads=[1, 1, 1, 1])),                 # 2 m blocks
     ([2, 3, 27, 27], [16, 3, 3, 3], dict(strides=[2, 2])),                     # OW % 4 != 0
+    ([2, 3, 64, 64], [32, 3, 7, 7], dict(strides=[4, 4], pads=[1, 1, 1, 1])),  # no tap shift fits
+    ([1, 3, 64, 72], [48, 3, 6, 6], dict(strides=[4, 4], pads=[2, 2, 2, 2])),  # tap shift 2
 ]
 
 
@@ -359,6 +361,31 @@ def test_smallc_route(ci):
         got = run_gpu(x, w, b, z, route="smallc", **a)
         ref = oracle.fusedconv(x, w, b, z, **a)
         check(got, ref, "f16", f"smallc case {ci}")
+
+
+@pytest.mark.parametrize("act", ["Gelu", "Erf"])
+def test_smallc_phi_table_activations(act):
+    """The few-channel route evaluates the erf-form Gelu and Erf from an LDS table
+    of the normal CDF with linear interpolation.  Pre-activations here spread
+    well past +-6 (the table's range) and cover its interior densely; Erf's
+    outputs lie in [-1, 1], so its bound is absolute: the table's error
+    (<= 1.5e-5 in erf, 4.4e-5 in Gelu), the fp32 sums' error carried through
+    the activation (~1e-5 here) and one fp16 rounding (<= 2^-11 * |y|)."""
+    xs, ws = [2, 3, 64, 64], [64, 3, 7, 7]
+    attrs = dict(strides=[2, 2], pads=[3, 3, 3, 3], activation=act)
+    h = B.Handle("f16", xs, ws, [64], None, route="smallc", **attrs)
+    x, w, b, _ = random_tensors([9350, len(act)], "f16", xs, ws, [64], None, dist="normal",
+                                w_std=0.5)
+    log(f"CASE smallc phi table {act} {h.kernel_name}")
+    got = run_gpu(x, w, b, None, route="smallc", **attrs).astype(np.float64)
+    ref = oracle.fusedconv(x, w, b, None, **attrs)
+    pre = oracle.fusedconv(x, w, b, None, **dict(attrs, activation=None))
+    assert np.abs(pre).max() > 8 and np.mean(np.abs(pre) < 6) > 0.3  # both regions covered
+    err = np.abs(got - ref)
+    if act == "Erf":
+        assert err.max() <= 1e-4 + 2.0 ** -11, err.max()
+    else:
+        assert np.all(err <= 1e-4 + 2.0 ** -11 * np.abs(ref)), err.max()
 
 
 # Grids of 1024 work units (4 blocks per CU), XCD-remapped block order, full
