@@ -34,7 +34,7 @@ EXPORTS = ["fusedconv_desc_init", "fusedconv_create", "fusedconv_create_transpos
            "fusedconv_output_shape",
            "fusedconv_workspace_size", "fusedconv_plan_info", "fusedconv_run",
            "fusedconv_prepare_weights", "fusedconv_run_ex", "fusedconv_run_timed",
-           "fusedconv_destroy",
+           "fusedconv_run_noalloc", "fusedconv_destroy",
            "fusedconv_status_string", "fusedconv_last_error"]
 RUN_WEIGHTS_PREPARED = 1
 
@@ -108,6 +108,8 @@ def load():
         lib.fusedconv_run_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                             ctypes.c_uint, vp, vp, vp]
         lib.fusedconv_run_timed.restype = ctypes.c_int
+        lib.fusedconv_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+        lib.fusedconv_run_noalloc.restype = ctypes.c_int
         lib.fusedconv_destroy.argtypes = [vp]
         lib.fusedconv_destroy.restype = None
         lib.fusedconv_status_string.argtypes = [ctypes.c_int]
@@ -210,6 +212,12 @@ class Handle:
         else:
             rc = self._lib.fusedconv_run_ex(self._h, x, w, bias, z, y, workspace,
                                             workspace_bytes, flags, stream)
+        if rc != 0:
+            raise FusedConvError(rc, self._lib.fusedconv_last_error().decode())
+
+    def run_noalloc(self, x, w, bias, z, y, stream):
+        """fusedconv_run_noalloc: the workspace is the library's own fixed array."""
+        rc = self._lib.fusedconv_run_noalloc(self._h, x, w, bias, z, y, stream)
         if rc != 0:
             raise FusedConvError(rc, self._lib.fusedconv_last_error().decode())
 

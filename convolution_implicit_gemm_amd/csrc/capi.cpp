@@ -62,6 +62,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 namespace fc {
 
+int set_last_error(int code, const std::string& msg) { return set_err(code, msg); }
+
 int set_max_dynamic_lds(const void* kfn, int bytes) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FUSEDCONV_ERR_LAUNCH;

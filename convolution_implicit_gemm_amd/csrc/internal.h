@@ -60,6 +60,9 @@ struct RunArgs {
   void* ev_stop;    // and at the last one's end (both NULL otherwise)
 };
 
+// Record `msg` as the calling thread's fusedconv_last_error() text; returns code.
+int set_last_error(int code, const std::string& msg);
+
 // Raise kernel kfn's dynamic-LDS limit to `bytes` on the current device,
 // once per (kernel, device, bytes); safe to call from several threads.
 int set_max_dynamic_lds(const void* kfn, int bytes);

@@ -308,6 +308,23 @@ int fusedconv_run_timed(const fusedconv_handle* h, const void* x, const void* w,
                         size_t workspace_bytes, unsigned flags, void* stream, void* start_event,
                         void* stop_event);
 
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same as
+ * fusedconv_run (weights prepared on every call), but the workspace is a
+ * fixed array inside the library, FUSEDCONV_NOALLOC_SCRATCH_BYTES on each
+ * GPU (held until the process ends), so the call allocates nothing and takes
+ * no workspace argument.  A plan whose fusedconv_workspace_size exceeds that
+ * size is refused with FUSEDCONV_ERR_WORKSPACE before anything is launched.
+ * The array is shared by every call on a GPU and keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other threads)
+ * race and must be serialized by the caller.  Other arguments and errors as
+ * for fusedconv_run.
+ */
+#define FUSEDCONV_NOALLOC_SCRATCH_BYTES (8u << 20)
+int fusedconv_run_noalloc(const fusedconv_handle* h, const void* x, const void* w,
+                          const void* bias, const void* z, void* y, void* stream);
+
 /* Release a handle (NULL is allowed).  Host memory only; runs already
  * enqueued with it are unaffected (the kernels received everything by value). */
 void fusedconv_destroy(fusedconv_handle* h);
