@@ -72,7 +72,8 @@ def bound_of(wl, flop, nbytes):
 KERNEL_SOURCES = {"halo_kernel": "kernels_halo.hip", "dw_fast_kernel": "kernels_depthwise.hip",
                   "depthwise_kernel": "kernels_depthwise.hip", "igemm_kernel": "kernels_igemm.hip",
                   "direct_kernel": "kernels_direct.hip", "smallc_kernel": "kernels_smallc.hip",
-                  "dwm_kernel": "kernels_dwmfma.hip", "pw_kernel": "kernels_pointwise.hip"}
+                  "dwm_kernel": "kernels_dwmfma.hip", "pw_kernel": "kernels_pointwise.hip",
+                  "im2col_kernel": "kernels_im2col.hip"}
 
 
 def sources_hash(kernel_pat):
@@ -96,7 +97,7 @@ def traffic_for(name):
 
 
 class Runner:
-    def __init__(self, name, seed_sets=None):
+    def __init__(self, name, seed_sets=None, route=None):
         import torch
         import convolution_implicit_gemm_amd as fc
         self.torch = torch
@@ -106,6 +107,8 @@ class Runner:
         attrs = dict(wl["attrs"])
         if attrs.get("activation_params") is not None:
             attrs["activation_params"] = [float(np.float32(v)) for v in attrs["activation_params"]]
+        if route:
+            attrs["route"] = route
         self.attrs = attrs
         self.op = fc.FusedConv(wl["x"], wl["w"], wl["dtype"], wl["b"] is not None,
                                wl["z"] is not None, **attrs)
@@ -286,6 +289,7 @@ def main():
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-config-steps", type=int, default=20)
+    ap.add_argument("--no-route-comparison", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run a plain device copy of this many MiB first (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("KERNEL_PATTERN", "FETCH_CSV", "WRITE_CSV"),
@@ -370,6 +374,25 @@ def main():
             torch.cuda.empty_cache()
             per.append(ss)
         out["per_config"] = per
+    if not args.no_route_comparison:
+        # the explicit im2col route against the implicit ones, same workload,
+        # same timing method (the planner's own choice is the per_config line)
+        comp = []
+        for name, wl_c in WORKLOADS.items():
+            for route in wl_c.get("compare_routes", []):
+                log(f"bench: route comparison {name} {route}")
+                rr = Runner(name, route=route)
+                ss = rr.summary(args.per_config_steps, 3)
+                ss["max_rel_err"] = rr.max_err(1500)
+                ss["workspace_bytes"] = rr.op.workspace_bytes
+                rr.free()
+                del rr
+                torch.cuda.empty_cache()
+                comp.append({k: ss[k] for k in ("workload", "route", "kernel", "kernel_ms_mean",
+                                                 "kernel_ms_median", "weight_prep_ms_mean",
+                                                 "tflops", "gbs", "max_rel_err",
+                                                 "workspace_bytes")})
+        out["route_comparison"] = comp
     print(json.dumps(out))
 
 

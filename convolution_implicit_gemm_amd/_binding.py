@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libfusedconv.so")
 MAX_RANK = 8
 F32, F16 = 0, 1
 ROUTES = {"auto": 0, "direct": 1, "igemm": 2, "depthwise": 3, "igemm_halo": 4, "smallc": 5,
-          "pointwise": 6, "transposed": 7}
+          "pointwise": 6, "transposed": 7, "im2col": 8}
 ROUTE_NAMES = {v: k for k, v in ROUTES.items()}
 
 STATUS = {

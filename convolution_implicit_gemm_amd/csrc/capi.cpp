@@ -166,7 +166,9 @@ int fusedconv_prepare_weights(const fusedconv_handle* h, const void* w, void* wo
                    "workspace smaller than fusedconv_workspace_size() reports");
   const bool pw = h->plan.route == FUSEDCONV_ROUTE_POINTWISE ||
                   (h->plan.route == FUSEDCONV_ROUTE_TRANSPOSED && h->plan.tile == 1);
-  if (h->plan.route != FUSEDCONV_ROUTE_IGEMM_HALO && h->plan.route != FUSEDCONV_ROUTE_SMALLC && !pw)
+  const bool ic = h->plan.route == FUSEDCONV_ROUTE_IM2COL;
+  if (h->plan.route != FUSEDCONV_ROUTE_IGEMM_HALO && h->plan.route != FUSEDCONV_ROUTE_SMALLC && !pw &&
+      !ic)
     return FUSEDCONV_OK;
   int rc = check_device(stream);
   if (rc != FUSEDCONV_OK) return rc;
@@ -174,7 +176,8 @@ int fusedconv_prepare_weights(const fusedconv_handle* h, const void* w, void* wo
   fc::RunArgs a{nullptr, w, nullptr, nullptr, nullptr, workspace, stream, 0u};
   rc = h->plan.route == FUSEDCONV_ROUTE_SMALLC ? fc::prepare_smallc(h->geo, h->plan, a)
        : pw ? fc::prepare_pointwise(h->geo, h->plan, a)
-                                                    : fc::prepare_igemm_halo(h->geo, h->plan, a);
+       : ic ? fc::prepare_im2col(h->geo, h->plan, a)
+            : fc::prepare_igemm_halo(h->geo, h->plan, a);
   if (rc != FUSEDCONV_OK) {
     hipError_t e = hipGetLastError();
     return set_err(rc, std::string("kernel launch failed: ") + hipGetErrorString(e));
@@ -222,6 +225,7 @@ int fusedconv_run_timed(const fusedconv_handle* h, const void* x, const void* w,
     case FUSEDCONV_ROUTE_SMALLC: rc = fc::launch_smallc(h->geo, h->plan, a); break;
     case FUSEDCONV_ROUTE_POINTWISE: rc = fc::launch_pointwise(h->geo, h->plan, a); break;
     case FUSEDCONV_ROUTE_TRANSPOSED: rc = fc::launch_transposed(h->geo, h->plan, a); break;
+    case FUSEDCONV_ROUTE_IM2COL: rc = fc::launch_im2col(h->geo, h->plan, a); break;
     default: return set_err(FUSEDCONV_ERR_ROUTE, "handle has no route");
   }
   if (rc != FUSEDCONV_OK) {

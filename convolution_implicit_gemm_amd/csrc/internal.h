@@ -77,6 +77,12 @@ int prepare_smallc(const Geometry& g, const Plan& p, const RunArgs& a);
 int launch_pointwise(const Geometry& g, const Plan& p, const RunArgs& a);
 int launch_transposed(const Geometry& g, const Plan& p, const RunArgs& a);
 int prepare_pointwise(const Geometry& g, const Plan& p, const RunArgs& a);
+// Explicit im2col route (kernels_im2col.hip), fp16: fits (with its workspace:
+// the GEMM's repacked weights, W padded to a multiple of 8 columns, the
+// column matrix), weight preparation and launch.
+bool im2col_fits(const ConvParams& cp, int32_t dtype, size_t* workspace);
+int prepare_im2col(const Geometry& g, const Plan& p, const RunArgs& a);
+int launch_im2col(const Geometry& g, const Plan& p, const RunArgs& a);
 
 // Kernels whose activation is a compile-time parameter: the build compiles
 // their source once per activation id (FC_ACT = 0 .. ACT_COUNT-1); unit k

@@ -331,6 +331,12 @@ void dwm_kernel(const half_t* __restrict__ x, const half_t* __restrict__ w,
           // keep only a few fragments in flight (registers for the prefetch)
           if (s % 3 == 2) __builtin_amdgcn_sched_barrier(0);
         }
+        // at least 32 wait states between the last MFMA and the first read of
+        // its result (the compiler's count was measured too low on gfx950 for
+        // v_mfma_f32_16x16x32_f16 results read soon after)
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
         // lane holds D[4q + i][j16] of tile p: output row 64v + 4 (4q + i) + p,
         // column 16t - S + j16 (stage column 16t - S + j16 + 8; rows past OH
         // and columns outside the image land in stage rows and margins that

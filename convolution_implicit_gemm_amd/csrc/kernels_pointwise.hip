@@ -223,7 +223,9 @@ __global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t*
       po[k] = (it & 7) + 8 * ((it >> 4) & 1);
       cq[k] = ((it >> 3) & 1) + 2 * (it >> 5);
       const int64_t pp = p0 + 8 * po[k];
-      pix_ok[k] = pp < P;  // P (and OW for a patch conv) % 8 == 0: an octet is all in or all out
+      // P (and OW for a patch conv) % 8 == 0, or the padded rows of an
+      // im2col column matrix: an octet is all in or all out of X
+      pix_ok[k] = pp < P;
       const half_t* img = x + (n * cp.C + (int64_t)g * cp.Cg) * cp.in_sz;
       if constexpr (PATCH != 2) {
         xs[k] = img + pp;
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t*
           if constexpr (PATCH != 2) {
             const int c = st * kBK + 4 * cq[k] + j;
             const bool ok = pix_ok[k] && c < cp.Cg;
-            v[k][j] = *(const half8*)(ok ? xs[k] + (int64_t)c * P : x);
+            v[k][j] = *(const half8*)(ok ? xs[k] + (int64_t)c * cp.in_sz : x);
           } else {
             const int c = st * (kBK / 4) + cq[k];
             const bool ok = pix_ok[k] && c < cp.Cg;
@@ -437,7 +439,12 @@ bool choose(const ConvParams& cp, int32_t dtype, PwTile& pt) {
   pt.kp = tr ? cp.Cg : cp.Cg * patch * patch;
   if (pt.kp % 8 != 0 || pt.kp < 16) return false;
   pt.P = tr ? cp.in_sz : cp.out_sz;
-  if (pt.P % 8 != 0) return false;
+  // X rows hold in_sz pixels: for a 1x1 conv in_sz == out_sz, so P % 8 == 0;
+  // a column matrix (the explicit im2col route) may pad its rows of P % 4 ==
+  // 0 pixels to a multiple of 8 -- the octets straddling P read the padding
+  // and the epilogue's 4-pixel groups are all in or all out
+  if (patch == 1 ? (cp.in_sz % 8 != 0 || cp.in_sz < pt.P || pt.P % 4 != 0) : pt.P % 8 != 0)
+    return false;
   // epilogue offsets: 64 channel planes of one image (16 planes of 4P
   // outputs for the transposed form) in 31-bit byte offsets
   if (pt.P * 64 * 2 * (tr ? 2 : 1) >= ((int64_t)1 << 31)) return false;

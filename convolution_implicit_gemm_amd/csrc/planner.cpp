@@ -13,6 +13,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "internal.h"
@@ -27,6 +28,15 @@ constexpr int64_t kSplitMaxBase = 128;      // only split grids this small
 constexpr size_t kSplitMaxBytes = (size_t)256 << 20;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Non-overlapping patches: stride = kernel on every axis, no padding, no
+// dilation, and a kernel above 1x1 (2x2 with stride 2 has the POINTWISE
+// route's patch form).
+bool patchify(const ConvParams& cp) {
+  if (cp.pd || cp.ph || cp.pw || cp.dd != 1 || cp.dh != 1 || cp.dw != 1) return false;
+  if (cp.sd != cp.KD || cp.sh != cp.KH || cp.sw != cp.KW) return false;
+  return cp.taps > 4;
+}
 
 // Grid limits of the IGEMM launch: x = column tiles, y = row tiles, z = group * split.
 bool igemm_grid_ok(const ConvParams& cp, int64_t split) {
@@ -81,7 +91,7 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
     err = "split_k must be >= 0";
     return FUSEDCONV_ERR_ROUTE;
   }
-  if (route < FUSEDCONV_ROUTE_AUTO || route > FUSEDCONV_ROUTE_TRANSPOSED) {
+  if (route < FUSEDCONV_ROUTE_AUTO || route > FUSEDCONV_ROUTE_IM2COL) {
     err = "unknown route";
     return FUSEDCONV_ERR_ROUTE;
   }
@@ -124,6 +134,10 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
     else if (pointwise_fits(cp, g.dtype)) route = FUSEDCONV_ROUTE_POINTWISE;
     else if (igemm_halo_fits(cp, g.dtype, th, tw, halo_ws)) route = FUSEDCONV_ROUTE_IGEMM_HALO;
     else if (smallc_fits(cp, g.dtype, th, tw, halo_ws)) route = FUSEDCONV_ROUTE_SMALLC;
+    // larger non-overlapping patches (stride = kernel): explicit im2col, whose
+    // column matrix is then a permutation of X (the manifest's
+    // implicitTiledWorthIt rule: the implicit routes pay off for stride < kernel)
+    else if (patchify(cp) && im2col_fits(cp, g.dtype, nullptr)) route = FUSEDCONV_ROUTE_IM2COL;
     else if (cp.K >= 8 && cp.Mg >= 8 && igemm_grid_ok(cp, 1)) route = FUSEDCONV_ROUTE_IGEMM;
     else route = FUSEDCONV_ROUTE_DIRECT;
   }
@@ -191,6 +205,16 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
       p.workspace = halo_ws;
       snprintf(p.name, sizeof(p.name), "pointwise_f16_%sm%d_n128", patch == 2 ? "patch2x2_" : "",
                (int)bm);
+      return FUSEDCONV_OK;
+    case FUSEDCONV_ROUTE_IM2COL:
+      if (!im2col_fits(cp, g.dtype, &halo_ws)) {
+        err = "IM2COL needs a forward fp16 problem with a number of output pixels per image that is a multiple of 4";
+        return FUSEDCONV_ERR_ROUTE;
+      }
+      p.route = route;
+      p.workspace = halo_ws;
+      // K rounded up to a multiple of 8 and at least 16: the GEMM's reduction
+      snprintf(p.name, sizeof(p.name), "im2col_f16_k%d", std::max(16, (int)((cp.K + 7) / 8 * 8)));
       return FUSEDCONV_OK;
     default:
       err = "unknown route";

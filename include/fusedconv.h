@@ -78,6 +78,16 @@ typedef enum fusedconv_dtype {
  *              C/group a multiple of 8 (>= 16) run instead as an MFMA GEMM
  *              (input pixels x (output channel, 2x2 phase)) with a workspace
  *              for the repacked weights.
+ *   IM2COL     explicit im2col, fp16 only (the FusedConv README's
+ *              im2col_gemm_tiled_reg_f16_columns variant): the column matrix
+ *              [n][group][K rounded up to 8][output pixels rounded up to 8]
+ *              is written into the workspace, then multiplied by W on MFMA
+ *              by the POINTWISE 1x1 kernel with the fused epilogue.  Any
+ *              fp16 forward problem whose output pixels per image are a
+ *              multiple of 4 (ViT's 14x14 patch grid is); the planner takes
+ *              it for non-overlapping patch convolutions (stride = kernel,
+ *              no padding, dilation 1, kernel above 2x2), where the column
+ *              matrix is a permutation of X.
  */
 typedef enum fusedconv_route {
   FUSEDCONV_ROUTE_AUTO = 0,
@@ -87,7 +97,8 @@ typedef enum fusedconv_route {
   FUSEDCONV_ROUTE_IGEMM_HALO = 4,
   FUSEDCONV_ROUTE_SMALLC = 5,
   FUSEDCONV_ROUTE_POINTWISE = 6,
-  FUSEDCONV_ROUTE_TRANSPOSED = 7
+  FUSEDCONV_ROUTE_TRANSPOSED = 7,
+  FUSEDCONV_ROUTE_IM2COL = 8
 } fusedconv_route;
 
 /* Shape of one tensor.  present = 0 means the (optional) input is absent. */
@@ -275,8 +286,8 @@ int fusedconv_run(const fusedconv_handle* h, const void* x, const void* w, const
  * preparation (for IGEMM_HALO a repack of W into the tap-major layout held in
  * the workspace, for SMALLC a repack into rows of 8 kernel columns, for
  * POINTWISE (and the GEMM form of TRANSPOSED) a repack into MFMA fragment
- * order; a no-op for the other
- * routes), and fusedconv_run_ex with
+ * order, for IM2COL the same after padding W's rows to a multiple of 8; a
+ * no-op for the other routes), and fusedconv_run_ex with
  * FUSEDCONV_RUN_WEIGHTS_PREPARED then skips that step and reads the prepared
  * weights from the workspace.  The caller guarantees that the workspace holds
  * the prepared form of the same W, made with the same handle; otherwise the

@@ -71,7 +71,10 @@ def test_workload_shapes_and_routes():
         h = B.Handle(wl["dtype"], wl["x"], wl["w"], wl["b"], wl["z"], **wl["attrs"])
         assert h.y_shape == wl["y"], name
         assert h.route in ("direct", "igemm", "depthwise", "igemm_halo", "smallc",
-                           "pointwise", "transposed"), name
+                           "pointwise", "transposed", "im2col"), name
+        for r in wl.get("compare_routes", []):   # every compared route plans
+            hr = B.Handle(wl["dtype"], wl["x"], wl["w"], wl["b"], wl["z"], route=r, **wl["attrs"])
+            assert hr.route == r and hr.y_shape == wl["y"], (name, r)
         if wl["attrs"].get("group", 1) == wl["x"][1]:
             assert h.route == "depthwise", name
     stem = WORKLOADS["vision_stem_7x7s4_f16"]
@@ -237,6 +240,46 @@ def test_pointwise_route_limits():
         with pytest.raises(B.FusedConvError) as e:
             _h(c.pop("x"), c.pop("w"), route="pointwise", **c)
         assert e.value.status == "FUSEDCONV_ERR_ROUTE"
+
+
+def test_im2col_route_limits():
+    # workspace = fragment-ordered weights + W padded to K rounded up to 8
+    # (when K % 8 != 0) + the column matrix [n][group][Kp][P rounded up to 8]
+    def al(v):
+        return (v + 255) // 256 * 256
+    h = _h([2, 3, 224, 224], [768, 3, 16, 16], dtype="f16", strides=[16, 16])
+    assert h.route == "im2col" and h.kernel_name == "im2col_f16_k768"
+    # 768 / 64 = 12 steps x 3 m blocks of 256 x 16384 halves; col: 2 x 768 x 200
+    assert h.workspace_bytes == al(3 * 12 * 16384 * 2) + 2 * 768 * 200 * 2
+    h = _h([4, 12, 32, 32], [64, 12, 3, 3], dtype="f16", pads=[1, 1, 1, 1], route="im2col")
+    assert h.kernel_name == "im2col_f16_k112"
+    assert h.workspace_bytes == al(2 * 8192 * 2) + al(64 * 112 * 2) + 4 * 112 * 1024 * 2
+    # groups: the GEMM view has G x Kp channels; 3-D and 1-D problems flatten
+    for xs, ws, kw in [([2, 32, 8, 8], [64, 8, 3, 3], dict(group=4, pads=[1, 1, 1, 1])),
+                       ([1, 8, 8, 16, 16], [32, 8, 2, 4, 4], dict(strides=[2, 4, 4])),
+                       ([3, 4, 96], [16, 4, 5], dict(strides=[2], pads=[2, 2])),
+                       ([1, 3, 20, 20], [16, 3, 5, 5], dict(dilations=[2, 2]))]:
+        h = _h(xs, ws, dtype="f16", route="im2col", **kw)
+        assert h.route == "im2col", (xs, ws, kw)
+    # AUTO takes it for patchify only, after the small-C kernel
+    assert _h([2, 64, 64, 64], [128, 64, 8, 8], dtype="f16", strides=[8, 8]).route == "im2col"
+    assert _h([2, 3, 768, 768], [128, 3, 4, 4], dtype="f16", strides=[4, 4]).route == "smallc"
+    assert _h([2, 64, 64, 64], [128, 64, 8, 8], dtype="f16", strides=[4, 4]).route != "im2col"
+    assert _h([2, 64, 64, 64], [128, 64, 8, 8], dtype="f16", strides=[8, 8],
+              pads=[4, 4, 4, 4]).route != "im2col"
+    refused = [
+        dict(x=[1, 3, 224, 224], w=[768, 3, 16, 16], strides=[16, 16], dtype="f32"),  # fp32
+        dict(x=[1, 3, 42, 42], w=[64, 3, 6, 6], strides=[6, 6], dtype="f16"),  # 49 pixels
+    ]
+    for c in refused:
+        c = dict(c)
+        with pytest.raises(B.FusedConvError) as e:
+            _h(c.pop("x"), c.pop("w"), route="im2col", **c)
+        assert e.value.status == "FUSEDCONV_ERR_ROUTE"
+    with pytest.raises(B.FusedConvError) as e:   # forward convolutions only
+        B.Handle("f16", [1, 16, 8, 8], [16, 16, 2, 2], None, None, transposed=True,
+                 strides=[2, 2], route="im2col")
+    assert e.value.status == "FUSEDCONV_ERR_ROUTE"
 
 
 def test_forced_routes_and_split_plan():

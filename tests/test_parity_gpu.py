@@ -541,12 +541,56 @@ def test_pointwise_route(ci):
         check(got, ref, "f16", f"pointwise case {ci}")
 
 
+IM2COL_CASES = [
+    # (x, w, attrs) for the explicit im2col route (fp16): patchify shapes,
+    # K not a multiple of 8 (W padded in the workspace), P not a multiple of
+    # 8 (padded column rows), groups, 1-D and 3-D, padding and dilation
+    ([2, 3, 64, 64], [96, 3, 4, 4], dict(strides=[4, 4])),             # K 48, P 256
+    ([2, 3, 224, 224], [64, 3, 16, 16], dict(strides=[16, 16])),       # K 768, P 196 (rows of 200)
+    ([1, 8, 28, 28], [32, 8, 14, 14], dict(strides=[14, 14])),         # P 4 (rows of 8), K 1568
+    ([4, 12, 32, 32], [64, 12, 3, 3], dict(pads=[1, 1, 1, 1])),        # K 108 -> 112
+    ([2, 3, 20, 20], [16, 3, 3, 3], dict(pads=[1, 1, 1, 1])),          # K 27 -> 32, M 16
+    ([2, 32, 8, 8], [64, 8, 3, 3], dict(group=4, pads=[1, 1, 1, 1])),  # groups, K 72
+    ([1, 8, 8, 16, 16], [32, 8, 2, 4, 4], dict(strides=[2, 4, 4])),    # 3-D patchify, P 64
+    ([3, 4, 96], [16, 4, 5], dict(strides=[2], pads=[2, 2])),          # 1-D, K 20 -> 24, P 48
+    ([1, 3, 20, 20], [16, 3, 5, 5], dict(dilations=[2, 2])),           # dilation, K 75 -> 80
+    ([2, 64, 32, 32], [300, 64, 4, 4], dict(strides=[4, 4])),          # 2 m blocks of 256, K 1024
+    ([2, 1, 16, 16], [5, 1, 2, 2], dict(strides=[2, 2])),              # K 4 -> 16, M 5
+    ([3, 16, 30, 30], [24, 16, 5, 5], dict(strides=[5, 5])),           # P 36 (rows of 40), n 3
+    # staging of X rows: W % 8 != 0 (2-byte row loads) with 11 pixel chunks,
+    # stride 2 with an end pad and 9 chunks, 3-D rows, and rows too wide to
+    # stage (the per-element gather kernel)
+    ([1, 1, 40, 1100], [8, 1, 3, 3], dict(pads=[1, 1, 1, 1])),
+    ([1, 1, 9, 5000], [8, 1, 2, 3], dict(strides=[1, 2], pads=[0, 1, 0, 1])),
+    ([1, 2, 4, 20, 30], [8, 2, 3, 3, 3], dict(strides=[1, 2, 2], pads=[1, 1, 1, 1, 1, 1])),
+    ([1, 2, 3, 8200], [8, 2, 2, 2], dict(strides=[1, 2])),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(IM2COL_CASES)))
+def test_im2col_route(ci):
+    xs, ws, attrs = IM2COL_CASES[ci]
+    h = B.Handle("f16", xs, ws, None, None, route="im2col", **attrs)
+    assert h.route == "im2col"
+    for k, (bias, resid) in enumerate([(True, True), (False, False), (True, False)]):
+        act, params = ACTS[(5 * ci + 3 * k) % len(ACTS)]
+        x, w, b, z = random_tensors([9500, ci, k], "f16", xs, ws, [ws[0]] if bias else None,
+                                    h.y_shape if resid else None, dist="normal",
+                                    w_std=1.0 / np.sqrt(np.prod(ws[1:])))
+        a = dict(attrs, activation=act, activation_params=f32params(params))
+        log(f"CASE im2col {ci} x={xs} w={ws} {a} bias={bias} z={resid}")
+        got = run_gpu(x, w, b, z, route="im2col", **a)
+        ref = oracle.fusedconv(x, w, b, z, **a)
+        check(got, ref, "f16", f"im2col case {ci}")
+
+
 @pytest.mark.parametrize("route", ["igemm_halo", "igemm", "depthwise", "smallc", "pointwise",
-                                   "pointwise_patch2x2"])
+                                   "pointwise_patch2x2", "im2col", "im2col_oddk"])
 def test_prepared_weights_match_plain_run(route):
     patch = route == "pointwise_patch2x2"
-    route = "pointwise" if patch else route
-    C = {"depthwise": 16, "smallc": 3}.get(route, 64)
+    oddk = route == "im2col_oddk"   # K 27: W padded to 32 columns in the workspace
+    route = "pointwise" if patch else ("im2col" if oddk else route)
+    C = {"depthwise": 16, "smallc": 3}.get(route, 3 if oddk else 64)
     M, grp = (C, C) if route == "depthwise" else (96, 1)
     k = 2 if patch else (1 if route == "pointwise" else 3)
     xs, ws = [2, C, 16, 16], [M, C // grp, k, k]
@@ -627,17 +671,14 @@ def chunks(n, per_image_outputs, limit=1 << 25):
     return [(i, min(n, i + step)) for i in range(0, n, step)]
 
 
-@pytest.mark.parametrize("name", list(WORKLOADS))
-def test_full_size_workloads(name):
-    """The whole output tensor of every workload, in the launch configuration
-    bench.py times, against the oracle (image ranges, so that the float64
-    reference of one range at a time stays in memory)."""
+def full_size_check(name, route=None):
     wl = WORKLOADS[name]
-    log(f"CASE workload {name} x={wl['x']} w={wl['w']}")
+    log(f"CASE workload {name} route={route or 'auto'} x={wl['x']} w={wl['w']}")
     inp = make_inputs(name)
     attrs = dict(wl["attrs"])
     attrs["activation_params"] = f32params(attrs.get("activation_params"))
-    got = run_gpu(inp["x"], inp["w"], inp["b"], inp["z"], **attrs)
+    rattrs = dict(attrs, route=route) if route else attrs
+    got = run_gpu(inp["x"], inp["w"], inp["b"], inp["z"], **rattrs)
     assert list(got.shape) == wl["y"]
     assert np.all(np.isfinite(got)), name
     n = wl["x"][0]
@@ -654,9 +695,31 @@ def test_full_size_workloads(name):
         max_ref = max(max_ref, float(np.max(np.abs(ref))))
         del ref
     rel = max_err / max(max_ref, 1e-30)
-    log(f"RESULT workload {name}: max |Y - Y_ref| / max |Y_ref| = {rel:.3e} over all "
-        f"{got.size} outputs (tau {TAU[wl['dtype']]})")
-    assert rel <= TAU[wl["dtype"]], f"{name}: rel err {rel:.3e}"
+    log(f"RESULT workload {name} route {route or 'auto'}: max |Y - Y_ref| / max |Y_ref| = "
+        f"{rel:.3e} over all {got.size} outputs (tau {TAU[wl['dtype']]})")
+    assert rel <= TAU[wl["dtype"]], f"{name} {route}: rel err {rel:.3e}"
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_full_size_workloads(name):
+    """The whole output tensor of every workload, in the launch configuration
+    bench.py times, against the oracle (image ranges, so that the float64
+    reference of one range at a time stays in memory)."""
+    full_size_check(name)
+
+
+COMPARED = [(name, r) for name, wl in WORKLOADS.items() for r in wl.get("compare_routes", [])]
+
+
+@pytest.mark.parametrize("name,route", COMPARED, ids=[f"{n}-{r}" for n, r in COMPARED])
+def test_full_size_compared_routes(name, route):
+    """Every route bench.py times a workload on (the implicit and explicit
+    im2col comparison), whole output tensor against the oracle."""
+    wl = WORKLOADS[name]
+    h = B.Handle(wl["dtype"], wl["x"], wl["w"], wl["b"], wl["z"], **wl["attrs"])
+    if h.route == route:
+        pytest.skip("the planner's own route: test_full_size_workloads covers it")
+    full_size_check(name, route)
 
 
 TRANSPOSED_CASES = [

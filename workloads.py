@@ -13,8 +13,14 @@ ConvGroup), a vision-encoder patch-embed stem and strided downsample
 (FusedConv manifest grouped_large_kernel variants), grouped 1-D and 3-D
 convs, the 1x1 reduce conv of a ResNet-50 stage-3 bottleneck (the FusedConv
 README's usage example is a 1x1 conv), and a 2x2 stride-2 transposed conv (the
-decoder-side inverse of the downsample).  No dataset, image or trained weight
-is used.
+decoder-side inverse of the downsample).  Three more compare the explicit
+im2col route with the implicit ones: a CIFAR-sized 3x3 pad-1 conv with few
+input channels (12: a reduction of 108, not a multiple of 16; the tinygrad
+page's MatmulConv2d runs the CIFAR net's 3x3 convs as an explicit patch
+matrix times the weights), a non-overlapping 4x4 stride-4
+patch embedding and a SigLIP-style 16x16 stride-16 patch embedding (a 14x14
+patch grid).  "compare_routes" lists the routes each is timed on.  No
+dataset, image or trained weight is used.
 
 Draw rule: numpy.random.default_rng([workload_index, sub]); tensors are
 drawn in the order X, W, B, Z in float64 (standard normal times a standard
@@ -52,11 +58,28 @@ WORKLOADS = {
         seed=[1, 0], dtype="f16", x=[512, 128, 16, 16], w=[256, 128, 3, 3], b=None,
         z=[512, 256, 16, 16], y=[512, 256, 16, 16], dist="normal",
         w_std=1.0 / math.sqrt(128 * 9),
-        attrs=dict(pads=[1, 1, 1, 1], activation="QuickGelu", activation_params=[1.702])),
+        attrs=dict(pads=[1, 1, 1, 1], activation="QuickGelu", activation_params=[1.702]),
+        compare_routes=["igemm_halo", "im2col"]),
+    "cifar_conv3x3_12to64_f16": dict(
+        seed=[1, 1], dtype="f16", x=[512, 12, 32, 32], w=[64, 12, 3, 3], b=None, z=None,
+        y=[512, 64, 32, 32], dist="normal", w_std=1.0 / math.sqrt(12 * 9),
+        attrs=dict(pads=[1, 1, 1, 1]),
+        compare_routes=["igemm", "im2col"]),
     "vision_stem_7x7s4_f16": dict(
         seed=[2, 0], dtype="f16", x=[32, 3, 768, 768], w=[128, 3, 7, 7], b=[128], z=None,
         y=[32, 128, 192, 192], dist="normal", w_std=1.0 / math.sqrt(147),
-        attrs=dict(strides=[4, 4], pads=[3, 3, 3, 3], activation="Gelu")),
+        attrs=dict(strides=[4, 4], pads=[3, 3, 3, 3], activation="Gelu"),
+        compare_routes=["smallc", "im2col"]),
+    "patch_embed_4x4s4_f16": dict(
+        seed=[2, 2], dtype="f16", x=[32, 3, 768, 768], w=[128, 3, 4, 4], b=[128], z=None,
+        y=[32, 128, 192, 192], dist="normal", w_std=1.0 / math.sqrt(48),
+        attrs=dict(strides=[4, 4]),
+        compare_routes=["smallc", "im2col", "igemm"]),
+    "siglip_patch_embed_16x16s16_f16": dict(
+        seed=[7, 0], dtype="f16", x=[256, 3, 224, 224], w=[768, 3, 16, 16], b=[768], z=None,
+        y=[256, 768, 14, 14], dist="normal", w_std=1.0 / math.sqrt(768),
+        attrs=dict(strides=[16, 16]),
+        compare_routes=["im2col", "igemm"]),
     "downsample_2x2s2_f16": dict(
         seed=[2, 1], dtype="f16", x=[32, 128, 192, 192], w=[256, 128, 2, 2], b=None, z=None,
         y=[32, 256, 96, 96], dist="normal", w_std=1.0 / math.sqrt(512),
