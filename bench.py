@@ -213,6 +213,57 @@ class Runner:
         self.ws = None
 
 
+def backward_timing(name, steps, warmup):
+    """The backward of a workload's convolution, each entry point timed over
+    `steps` calls between two events on the stream (so the weight flip and
+    the column matrix are inside): the input gradient with the QuickGelu
+    derivative of the layer below and a residual gradient, and the weight
+    gradient with the bias gradient.  FLOPs as the forward (2 n M P K)."""
+    import torch
+    import convolution_implicit_gemm_amd as fc
+    wl = WORKLOADS[name]
+    xs, ws, dt = wl["x"], wl["w"], wl["dtype"]
+    attrs = {k: v for k, v in wl["attrs"].items() if k not in ("activation", "activation_params")}
+    tdt = torch.float16 if dt == "f16" else torch.float32
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    rnd = lambda shape, s=1.0: (torch.randn(shape, generator=gen, device="cuda") * s).to(tdt)
+    x, w = rnd(xs), rnd(ws, 1.0 / math.sqrt(float(np.prod(ws[1:]))))
+    g, pre, r = rnd(wl["y"], 0.1), rnd(xs, 2.0), rnd(xs, 0.1)
+    opd = fc.ConvBackwardData(xs, ws, dt, True, "QuickGelu", [1.702], **attrs)
+    opw = fc.ConvBackwardWeight(xs, ws, dt, True, **attrs)
+    dx = torch.empty(xs, dtype=tdt, device="cuda")
+    dw = torch.empty(ws, dtype=torch.float32, device="cuda")
+    db = torch.empty([ws[0]], dtype=torch.float32, device="cuda")
+    wsd = torch.empty(max(opd.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    wsw = torch.empty(max(opw.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    flop = work(wl, wl["y"])[0]
+    esz = 2 if dt == "f16" else 4
+    ny, nx, nw = float(np.prod(wl["y"])), float(np.prod(xs)), float(np.prod(ws))
+    out = []
+    for label, call, nbytes, op in [
+            ("backward_data", lambda: opd(g, w, pre, r, out=dx, workspace=wsd),
+             (ny + nw + 3 * nx) * esz, opd),
+            ("backward_weight", lambda: opw(x, g, dw, db, workspace=wsw),
+             (nx + ny) * esz + (nw + ws[0]) * 4, opw)]:
+        for _ in range(warmup):
+            call()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(steps):
+            call()
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / steps
+        tf = flop / (ms * 1e-3) / 1e12
+        out.append(dict(workload=name, op=label, route=op.handle.route,
+                        kernel=op.handle.kernel_name, ms_per_call=ms, tflops=tf,
+                        mfma_frac=tf / PEAK_TFLOPS[dt], gbs=nbytes / (ms * 1e-3) / 1e9,
+                        workspace_bytes=op.workspace_bytes,
+                        time_source="events around the calls on the stream"))
+    return out
+
+
 def cpu_baseline(name, target_s=20.0):
     """The oracle, as it stands, on a bounded sample of the workload's images."""
     from oracle import oracle
@@ -290,6 +341,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-config-steps", type=int, default=20)
     ap.add_argument("--no-route-comparison", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run a plain device copy of this many MiB first (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("KERNEL_PATTERN", "FETCH_CSV", "WRITE_CSV"),
@@ -393,6 +445,10 @@ def main():
                                                  "tflops", "gbs", "max_rel_err",
                                                  "workspace_bytes")})
         out["route_comparison"] = comp
+    if not args.no_backward:
+        log("bench: backward of the headline convolution")
+        out["backward"] = backward_timing(HEADLINE, args.per_config_steps, 3)
+        torch.cuda.empty_cache()
     print(json.dumps(out))
 
 

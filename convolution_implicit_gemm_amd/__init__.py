@@ -9,7 +9,8 @@ from __future__ import annotations
 
 from ._binding import EXPORTS, FusedConvError, Handle, LIB_PATH, load
 
-__all__ = ["fused_conv", "FusedConv", "Handle", "FusedConvError", "load", "LIB_PATH", "EXPORTS"]
+__all__ = ["fused_conv", "FusedConv", "Handle", "FusedConvError", "load", "LIB_PATH", "EXPORTS",
+           "ConvBackwardData", "ConvBackwardWeight", "conv_backward_data", "conv_backward_weight"]
 
 _cache: dict = {}
 
@@ -137,3 +138,125 @@ def fused_conv(x, w, bias=None, z=None, *, auto_pad=None, group=1, kernel_shape=
                        z is not None, **attrs)
         _cache[key] = op
     return op(x, w, bias, z)
+
+
+def _device_checks(named, want, device):
+    """Each (name, tensor, shape) must be a contiguous device tensor of dtype
+    `want` (None: any) and the given shape on `device`."""
+    for name, t, shape in named:
+        if not t.is_cuda:
+            raise FusedConvError(-1, f"{name} must be a device tensor (no CPU path)")
+        if not t.is_contiguous():
+            raise FusedConvError(-1, f"{name} must be contiguous")
+        if want is not None and t.dtype != want:
+            raise ValueError(f"{name} is {t.dtype}, the plan is {want}")
+        if list(t.shape) != list(shape):
+            raise ValueError(f"{name} has shape {list(t.shape)}, the plan expects {list(shape)}")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+class ConvBackwardData:
+    """The input gradient of a planned convolution (fusedconv_create_backward_data):
+    dP = (conv^T(G, W) + R) * act_in'(P), G the gradient of the convolution's
+    pre-activation output, act_in the activation that produced X from P."""
+
+    def __init__(self, x_shape, w_shape, dtype, has_residual=False, input_activation=None,
+                 input_activation_params=None, **attrs):
+        self.x_shape = [int(v) for v in x_shape]
+        self.w_shape = [int(v) for v in w_shape]
+        self.dtype = dtype
+        self.has_residual = bool(has_residual)
+        self.has_pre = input_activation is not None
+        fwd = {k: v for k, v in attrs.items() if k not in ("route", "split_k")}
+        self.y_shape = Handle(dtype, x_shape, w_shape, None, None, **fwd).y_shape
+        self.handle = Handle(dtype, x_shape, w_shape, None,
+                             self.x_shape if has_residual else None, activation=input_activation,
+                             activation_params=input_activation_params, kind="backward_data",
+                             **attrs)
+        self.workspace_bytes = self.handle.workspace_bytes
+
+    def __call__(self, dy, w, pre=None, residual=None, out=None, workspace=None, stream=None):
+        import torch
+        want = torch.float16 if self.dtype == "f16" else torch.float32
+        named = [("dy", dy, self.y_shape), ("w", w, self.w_shape)]
+        if self.has_pre:
+            if pre is None:
+                raise ValueError("pre (the input pre-activation) was planned but not given")
+            named.append(("pre", pre, self.x_shape))
+        elif pre is not None:
+            raise ValueError("pre given but no input activation was planned")
+        if self.has_residual != (residual is not None):
+            raise ValueError("residual given / planned mismatch")
+        if residual is not None:
+            named.append(("residual", residual, self.x_shape))
+        if out is not None:
+            named.append(("out", out, self.x_shape))
+        _device_checks(named, want, dy.device)
+        dx = out if out is not None else torch.empty(self.x_shape, dtype=dy.dtype, device=dy.device)
+        ws = workspace
+        if self.workspace_bytes and ws is None:
+            ws = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=dy.device)
+        if ws is not None and ws.numel() * ws.element_size() < self.workspace_bytes:
+            raise FusedConvError(-14, f"workspace holds fewer than {self.workspace_bytes} bytes")
+        st = stream if stream is not None else torch.cuda.current_stream(dy.device).cuda_stream
+        self.handle.backward_data(dy.data_ptr(), w.data_ptr(),
+                                  pre.data_ptr() if pre is not None else None,
+                                  residual.data_ptr() if residual is not None else None,
+                                  dx.data_ptr(), ws.data_ptr() if ws is not None else None,
+                                  self.workspace_bytes if ws is not None else 0, st)
+        return dx
+
+
+class ConvBackwardWeight:
+    """The weight (and optionally bias) gradient of a planned convolution
+    (fusedconv_create_backward_weight), in float32."""
+
+    def __init__(self, x_shape, w_shape, dtype, bias_grad=False, **attrs):
+        self.x_shape = [int(v) for v in x_shape]
+        self.w_shape = [int(v) for v in w_shape]
+        self.dtype = dtype
+        self.bias_grad = bool(bias_grad)
+        fwd = {k: v for k, v in attrs.items() if k not in ("route", "split_k")}
+        self.y_shape = Handle(dtype, x_shape, w_shape, None, None, **fwd).y_shape
+        self.handle = Handle(dtype, x_shape, w_shape, [w_shape[0]] if bias_grad else None,
+                             None, kind="backward_weight", **attrs)
+        self.workspace_bytes = self.handle.workspace_bytes
+
+    def __call__(self, x, dy, dw=None, db=None, workspace=None, stream=None):
+        import torch
+        want = torch.float16 if self.dtype == "f16" else torch.float32
+        _device_checks([("x", x, self.x_shape), ("dy", dy, self.y_shape)], want, x.device)
+        if dw is None:
+            dw = torch.empty(self.w_shape, dtype=torch.float32, device=x.device)
+        if self.bias_grad and db is None:
+            db = torch.empty([self.w_shape[0]], dtype=torch.float32, device=x.device)
+        if not self.bias_grad and db is not None:
+            raise ValueError("db given but the bias gradient was not planned")
+        named = [("dw", dw, self.w_shape)] + ([("db", db, [self.w_shape[0]])] if db is not None else [])
+        _device_checks(named, torch.float32, x.device)
+        ws = workspace
+        if self.workspace_bytes and ws is None:
+            ws = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=x.device)
+        if ws is not None and ws.numel() * ws.element_size() < self.workspace_bytes:
+            raise FusedConvError(-14, f"workspace holds fewer than {self.workspace_bytes} bytes")
+        st = stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream
+        self.handle.backward_weight(x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
+                                    db.data_ptr() if db is not None else None,
+                                    ws.data_ptr() if ws is not None else None,
+                                    self.workspace_bytes if ws is not None else 0, st)
+        return (dw, db) if self.bias_grad else dw
+
+
+def conv_backward_data(dy, w, x_shape, pre=None, residual=None, *, input_activation=None,
+                       input_activation_params=None, **attrs):
+    """dP = (conv^T(dy, w) + residual) * act_in'(pre) on the current stream."""
+    op = ConvBackwardData(x_shape, list(w.shape), _dtype_name(dy), residual is not None,
+                          input_activation, input_activation_params, **attrs)
+    return op(dy, w, pre, residual)
+
+
+def conv_backward_weight(x, dy, w_shape, *, bias_grad=False, **attrs):
+    """dW (and dB with bias_grad=True), float32, on the current stream."""
+    op = ConvBackwardWeight(list(x.shape), w_shape, _dtype_name(x), bias_grad, **attrs)
+    return op(x, dy)

@@ -34,7 +34,9 @@ EXPORTS = ["fusedconv_desc_init", "fusedconv_create", "fusedconv_create_transpos
            "fusedconv_output_shape",
            "fusedconv_workspace_size", "fusedconv_plan_info", "fusedconv_run",
            "fusedconv_prepare_weights", "fusedconv_run_ex", "fusedconv_run_timed",
-           "fusedconv_run_noalloc", "fusedconv_destroy",
+           "fusedconv_run_noalloc", "fusedconv_create_backward_data",
+           "fusedconv_backward_data", "fusedconv_create_backward_weight",
+           "fusedconv_backward_weight", "fusedconv_destroy",
            "fusedconv_status_string", "fusedconv_last_error"]
 RUN_WEIGHTS_PREPARED = 1
 
@@ -110,6 +112,13 @@ def load():
         lib.fusedconv_run_timed.restype = ctypes.c_int
         lib.fusedconv_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp]
         lib.fusedconv_run_noalloc.restype = ctypes.c_int
+        for fn in ("fusedconv_create_backward_data", "fusedconv_create_backward_weight"):
+            getattr(lib, fn).argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(vp)]
+            getattr(lib, fn).restype = ctypes.c_int
+        lib.fusedconv_backward_data.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.fusedconv_backward_data.restype = ctypes.c_int
+        lib.fusedconv_backward_weight.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.fusedconv_backward_weight.restype = ctypes.c_int
         lib.fusedconv_destroy.argtypes = [vp]
         lib.fusedconv_destroy.restype = None
         lib.fusedconv_status_string.argtypes = [ctypes.c_int]
@@ -143,12 +152,19 @@ def _i64list(vals, keep):
 
 
 class Handle:
-    """An immutable FusedConv problem: resolved shapes, attributes and plan."""
+    """An immutable FusedConv problem: resolved shapes, attributes and plan.
+
+    kind: "forward" (fusedconv_create, or fusedconv_create_transposed with
+    transposed=True), "backward_data" (fusedconv_create_backward_data: the
+    activation names the one that produced X, z_shape declares a residual
+    gradient of X's shape) or "backward_weight"
+    (fusedconv_create_backward_weight: bias_shape requests the bias gradient).
+    """
 
     def __init__(self, dtype, x_shape, w_shape, bias_shape=None, z_shape=None, *,
                  auto_pad=None, group=1, kernel_shape=None, strides=None, dilations=None,
                  pads=None, activation=None, activation_params=None, route="auto", split_k=0,
-                 transposed=False, output_padding=None):
+                 transposed=False, output_padding=None, kind="forward"):
         lib = load()
         d = Desc()
         lib.fusedconv_desc_init(ctypes.byref(d))
@@ -178,7 +194,13 @@ class Handle:
         d.route = ROUTES[route] if isinstance(route, str) else int(route)
         d.split_k = int(split_k)
         h = ctypes.c_void_p()
-        if transposed:
+        if kind == "backward_data":
+            rc = lib.fusedconv_create_backward_data(ctypes.byref(d), ctypes.byref(h))
+        elif kind == "backward_weight":
+            rc = lib.fusedconv_create_backward_weight(ctypes.byref(d), ctypes.byref(h))
+        elif kind != "forward":
+            raise ValueError(f"unknown handle kind {kind!r}")
+        elif transposed:
             op, nop = _i64list(output_padding, keep)
             rc = lib.fusedconv_create_transposed(ctypes.byref(d), op, nop, ctypes.byref(h))
         else:
@@ -187,6 +209,7 @@ class Handle:
             raise FusedConvError(rc, lib.fusedconv_last_error().decode())
         self._lib = lib
         self._h = h
+        self.kind = kind
         dims = (ctypes.c_int64 * MAX_RANK)()
         rank = ctypes.c_int32()
         lib.fusedconv_output_shape(h, dims, ctypes.byref(rank))
@@ -218,6 +241,20 @@ class Handle:
     def run_noalloc(self, x, w, bias, z, y, stream):
         """fusedconv_run_noalloc: the workspace is the library's own fixed array."""
         rc = self._lib.fusedconv_run_noalloc(self._h, x, w, bias, z, y, stream)
+        if rc != 0:
+            raise FusedConvError(rc, self._lib.fusedconv_last_error().decode())
+
+    def backward_data(self, dy, w, pre, dres, dx, workspace, workspace_bytes, stream):
+        """fusedconv_backward_data on raw device pointers (ints or None)."""
+        rc = self._lib.fusedconv_backward_data(self._h, dy, w, pre, dres, dx, workspace,
+                                               workspace_bytes, stream)
+        if rc != 0:
+            raise FusedConvError(rc, self._lib.fusedconv_last_error().decode())
+
+    def backward_weight(self, x, dy, dw, db, workspace, workspace_bytes, stream):
+        """fusedconv_backward_weight on raw device pointers (ints or None)."""
+        rc = self._lib.fusedconv_backward_weight(self._h, x, dy, dw, db, workspace,
+                                                 workspace_bytes, stream)
         if rc != 0:
             raise FusedConvError(rc, self._lib.fusedconv_last_error().decode())
 

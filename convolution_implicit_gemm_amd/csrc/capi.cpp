@@ -10,12 +10,8 @@
 #include <string>
 #include <tuple>
 
+#include "handle.h"
 #include "internal.h"
-
-struct fusedconv_handle {
-  fc::Geometry geo;
-  fc::Plan plan;
-};
 
 namespace {
 
@@ -56,13 +52,18 @@ int check_device(void* stream) {
   return FUSEDCONV_OK;
 }
 
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+using fc::aligned16;
 
 }  // namespace
 
 namespace fc {
 
 int set_last_error(int code, const std::string& msg) { return set_err(code, msg); }
+
+int check_device(void* stream) { return ::check_device(stream); }
+
+// the calling thread's last-error text is cleared by a successful create
+void clear_last_error() { t_last_error.clear(); }
 
 int set_max_dynamic_lds(const void* kfn, int bytes) {
   int dev = 0;
@@ -92,7 +93,7 @@ void fusedconv_desc_init(fusedconv_desc* d) {
 int fusedconv_create(const fusedconv_desc* d, fusedconv_handle** out) {
   if (out) *out = nullptr;
   if (!d || !out) return set_err(FUSEDCONV_ERR_NULL_ARG, "desc and out must not be NULL");
-  fusedconv_handle* h = new (std::nothrow) fusedconv_handle;
+  fusedconv_handle* h = new (std::nothrow) fusedconv_handle();
   if (!h) return set_err(FUSEDCONV_ERR_ALLOC, "out of host memory");
   std::string err;
   int rc = fc::resolve(*d, h->geo, err);
@@ -110,7 +111,7 @@ int fusedconv_create_transposed(const fusedconv_desc* d, const int64_t* output_p
                                 int32_t n_output_padding, fusedconv_handle** out) {
   if (out) *out = nullptr;
   if (!d || !out) return set_err(FUSEDCONV_ERR_NULL_ARG, "desc and out must not be NULL");
-  fusedconv_handle* h = new (std::nothrow) fusedconv_handle;
+  fusedconv_handle* h = new (std::nothrow) fusedconv_handle();
   if (!h) return set_err(FUSEDCONV_ERR_ALLOC, "out of host memory");
   std::string err;
   int rc = fc::resolve_transposed(*d, output_padding, n_output_padding, h->geo, err);
@@ -159,6 +160,8 @@ int fusedconv_run(const fusedconv_handle* h, const void* x, const void* w, const
 int fusedconv_prepare_weights(const fusedconv_handle* h, const void* w, void* workspace,
                               size_t workspace_bytes, void* stream) {
   if (!h || !w) return set_err(FUSEDCONV_ERR_NULL_ARG, "h and w are required");
+  if (h->kind != fc::kForward)
+    return set_err(FUSEDCONV_ERR_ROUTE, "a backward handle: use fusedconv_backward_data / _weight");
   if (!aligned16(w) || (workspace && !aligned16(workspace)))
     return set_err(FUSEDCONV_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
   if (h->plan.workspace > 0 && (!workspace || workspace_bytes < h->plan.workspace))
@@ -173,7 +176,7 @@ int fusedconv_prepare_weights(const fusedconv_handle* h, const void* w, void* wo
   int rc = check_device(stream);
   if (rc != FUSEDCONV_OK) return rc;
   (void)hipGetLastError();
-  fc::RunArgs a{nullptr, w, nullptr, nullptr, nullptr, workspace, stream, 0u};
+  fc::RunArgs a{nullptr, w, nullptr, nullptr, nullptr, nullptr, workspace, stream, 0u};
   rc = h->plan.route == FUSEDCONV_ROUTE_SMALLC ? fc::prepare_smallc(h->geo, h->plan, a)
        : pw ? fc::prepare_pointwise(h->geo, h->plan, a)
        : ic ? fc::prepare_im2col(h->geo, h->plan, a)
@@ -197,6 +200,8 @@ int fusedconv_run_timed(const fusedconv_handle* h, const void* x, const void* w,
                         size_t workspace_bytes, unsigned flags, void* stream, void* start_event,
                         void* stop_event) {
   if (!h || !x || !w || !y) return set_err(FUSEDCONV_ERR_NULL_ARG, "h, x, w and y are required");
+  if (h->kind != fc::kForward)
+    return set_err(FUSEDCONV_ERR_ROUTE, "a backward handle: use fusedconv_backward_data / _weight");
   if (!start_event != !stop_event)
     return set_err(FUSEDCONV_ERR_NULL_ARG, "give both timing events or neither");
   const fc::ConvParams& cp = h->geo.cp;
@@ -216,7 +221,7 @@ int fusedconv_run_timed(const fusedconv_handle* h, const void* x, const void* w,
   (void)hipGetLastError();  // drop a stale error so a launch failure is reported as ours
   if (flags & ~FUSEDCONV_RUN_WEIGHTS_PREPARED)
     return set_err(FUSEDCONV_ERR_ATTR_VALUE, "unknown run flags");
-  fc::RunArgs a{x, w, bias, z, y, workspace, stream, flags, start_event, stop_event};
+  fc::RunArgs a{x, w, bias, z, nullptr, y, workspace, stream, flags, start_event, stop_event};
   switch (h->plan.route) {
     case FUSEDCONV_ROUTE_DIRECT: rc = fc::launch_direct(h->geo, h->plan, a); break;
     case FUSEDCONV_ROUTE_IGEMM: rc = fc::launch_igemm(h->geo, h->plan, a); break;

@@ -40,6 +40,12 @@ struct ConvParams {
   // count X's channels, M and Mg Y's, W is [C][M/G][k...], (D, H, W) is X's
   // extent and (OD, OH, OW) Y's, and the pads are Y's begin offsets.
   int32_t transposed;
+  // 1: the input gradient of a convolution (fusedconv_create_backward_data).
+  // X is then the gradient G of that convolution's output, Y the gradient of
+  // the pre-activation P of its input, and the epilogue computes
+  // Y = (acc + Z) * act'(P): Z the optional residual gradient, act the
+  // activation that produced the convolution's input (no bias).
+  int32_t bwd;
 };
 
 // True when the depth axis is trivial, i.e. the problem is really 1-D or 2-D:

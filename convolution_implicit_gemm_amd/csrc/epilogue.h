@@ -124,12 +124,81 @@ __device__ __forceinline__ float act_apply(int act, float v, float a, float b) {
   return r;
 }
 
-// acc: the convolution sum for output (n, m, o) at flat Y index yi.
+// Derivative of activation A at v, the backward of act_t: the textbook
+// derivatives of the forms above; where a piecewise activation has no
+// derivative, the branch its comparison selects (Relu 0 at 0, LeakyRelu
+// alpha at 0, Clip 1 on [min, max], HardSigmoid alpha strictly inside
+// (0, 1), HardSwish v/3 + 1/2 strictly inside (-3, 3), ThresholdedRelu 0 at
+// alpha).
+template <int A>
+__device__ __forceinline__ float dact_t(float v, float a, float b) {
+  if constexpr (A == ACT_NONE) return 1.0f;
+  if constexpr (A == ACT_RELU) return v > 0.0f ? 1.0f : 0.0f;
+  if constexpr (A == ACT_LEAKYRELU) return v > 0.0f ? 1.0f : a;
+  if constexpr (A == ACT_SIGMOID) {
+    const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+    return s * (1.0f - s);
+  }
+  if constexpr (A == ACT_TANH) {
+    const float t = tanh_fast(v);
+    return 1.0f - t * t;
+  }
+  if constexpr (A == ACT_HARDSIGMOID) {
+    const float u = a * v + b;
+    return (u > 0.0f && u < 1.0f) ? a : 0.0f;
+  }
+  if constexpr (A == ACT_HARDSWISH) return v <= -3.0f ? 0.0f : (v >= 3.0f ? 1.0f : v * (1.0f / 3.0f) + 0.5f);
+  if constexpr (A == ACT_CLIP) return (v >= a && v <= b) ? 1.0f : 0.0f;
+  if constexpr (A == ACT_QUICKGELU) {
+    const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-a * v));
+    return s + a * v * s * (1.0f - s);
+  }
+  if constexpr (A == ACT_ELU) return v > 0.0f ? 1.0f : a * __expf(v);
+  if constexpr (A == ACT_GELU) {
+    // Phi(v) + v phi(v): Phi the normal CDF (erfc form as in act_t), phi its density
+    const float c = erfc_as(fabsf(v) * 0.70710678118654752f);
+    const float phi_cdf = v < 0.0f ? 0.5f * c : 1.0f - 0.5f * c;
+    return phi_cdf + v * 0.39894228040143268f * __expf(-0.5f * v * v);
+  }
+  if constexpr (A == ACT_FASTGELU) {
+    const float k = 0.79788456080286536f;
+    const float t = tanh_fast(k * (v + 0.044715f * v * v * v));
+    return 0.5f * (1.0f + t) + 0.5f * v * (1.0f - t * t) * k * (1.0f + 0.134145f * v * v);
+  }
+  if constexpr (A == ACT_SOFTPLUS) return __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+  if constexpr (A == ACT_THRESHOLDEDRELU) return v > a ? 1.0f : 0.0f;
+  if constexpr (A == ACT_ERF) return 1.12837916709551257f * __expf(-v * v);
+  return 1.0f;
+}
+
+// Runtime-dispatched derivative.
+__device__ __forceinline__ float dact_apply(int act, float v, float a, float b) {
+  float r = 1.0f;
+  with_act(act, [&](auto tag) { r = dact_t<decltype(tag)::value>(v, a, b); });
+  return r;
+}
+
+// Four derivatives at once: one dispatch per 4 outputs.
+__device__ __forceinline__ act4_t dact_apply4(int act, act4_t v, float a, float b) {
+  act4_t r = v;
+  with_act(act, [&](auto tag) {
+    constexpr int A = decltype(tag)::value;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = dact_t<A>(v[k], a, b);
+  });
+  return r;
+}
+
+// acc: the convolution sum for output (n, m, o) at flat Y index yi.  The
+// backward-data form (cp.bwd) returns (acc + Z) * act'(P[yi]) instead.
 template <typename T>
 __device__ __forceinline__ T epilogue(float acc, int m, int64_t yi, const ConvParams& cp,
-                                      const T* bias, const T* z) {
+                                      const T* bias, const T* z, const T* pre) {
   if (cp.has_bias) acc += to_f32(bias[m]);
   if (cp.has_z) acc += to_f32(z[yi]);
+  if (cp.bwd)
+    return from_f32<T>(cp.act == ACT_NONE ? acc
+                                          : acc * dact_apply(cp.act, to_f32(pre[yi]), cp.alpha, cp.beta));
   return from_f32<T>(act_apply(cp.act, acc, cp.alpha, cp.beta));
 }
 

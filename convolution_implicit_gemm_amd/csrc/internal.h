@@ -52,6 +52,7 @@ struct RunArgs {
   const void* w;
   const void* bias;
   const void* z;
+  const void* pre;  // backward data: the pre-activation P of the convolution's input
   void* y;
   void* ws;
   void* stream;
@@ -62,6 +63,7 @@ struct RunArgs {
 
 // Record `msg` as the calling thread's fusedconv_last_error() text; returns code.
 int set_last_error(int code, const std::string& msg);
+void clear_last_error();
 
 // Raise kernel kfn's dynamic-LDS limit to `bytes` on the current device,
 // once per (kernel, device, bytes); safe to call from several threads.
@@ -81,8 +83,27 @@ int prepare_pointwise(const Geometry& g, const Plan& p, const RunArgs& a);
 // the GEMM's repacked weights, W padded to a multiple of 8 columns, the
 // column matrix), weight preparation and launch.
 bool im2col_fits(const ConvParams& cp, int32_t dtype, size_t* workspace);
+// The column matrix of cp (a forward problem) in dtype: col[n][g][Kq][Pp],
+// rows k < K the im2col of X (zero outside X and at pixels p >= P), row K
+// ones at p < P when `ones`, the other rows zero; Kq >= K, Pp >= P, Pp % 8
+// == 0.  One kernel, launched with launch_conv's timing edges.
+int launch_columns(const ConvParams& cp, int32_t dtype, const void* x, void* col, int Kq,
+                   int64_t Pp, int ones, const RunArgs& a, unsigned edges);
 int prepare_im2col(const Geometry& g, const Plan& p, const RunArgs& a);
 int launch_im2col(const Geometry& g, const Plan& p, const RunArgs& a);
+
+// Backward (kernels_backward.hip).  W of forward problem f, [M][C/G][taps],
+// to W' = [C][M/G][taps] flipped in every spatial axis (the weights of the
+// stride-1 input gradient as a forward convolution).
+int launch_flip_weights(const ConvParams& f, int32_t dtype, const void* w, void* wf, void* stream);
+// Weight gradient of forward problem cp as a GEMM over its column matrix:
+// fits, with the workspace (column matrix + fp32 partials) and the image
+// ranges; launch (plan route IM2COL: the GEMM; DIRECT: the plain reduction).
+// dw: float [M][C/G][taps]; db: float [M] or NULL.
+bool wgrad_gemm_fits(const ConvParams& cp, int32_t dtype, int has_db, size_t* workspace,
+                     int32_t* splits);
+int launch_wgrad(const Geometry& g, const Plan& p, const void* x, const void* dy, float* dw,
+                 float* db, void* ws, void* stream);
 
 // Kernels whose activation is a compile-time parameter: the build compiles
 // their source once per activation id (FC_ACT = 0 .. ACT_COUNT-1); unit k

@@ -18,7 +18,8 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void direct_kernel(const T* __restrict__ x,
                                                           const T* __restrict__ w,
                                                           const T* __restrict__ bias,
-                                                          const T* z, T* y, ConvParams cp) {
+                                                          const T* z, const T* pre, T* y,
+                                                          ConvParams cp) {
   const int64_t total = cp.n * cp.M * cp.out_sz;
   const int64_t step = (int64_t)gridDim.x * kThreads;
   for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < total; idx += step) {
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void direct_kernel(const T* __restrict__ 
         }
       }
     }
-    y[idx] = epilogue<T>(acc, m, idx, cp, bias, z);
+    y[idx] = epilogue<T>(acc, m, idx, cp, bias, z, pre);
   }
 }
 
@@ -65,7 +66,8 @@ int launch(const Geometry& g, const RunArgs& a) {
   int64_t blocks = (total + kThreads - 1) / kThreads;
   if (blocks > (1 << 22)) blocks = 1 << 22;
   return launch_conv(direct_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), 0, a, kEdgeBoth,
-                     (const T*)a.x, (const T*)a.w, (const T*)a.bias, (const T*)a.z, (T*)a.y, cp);
+                     (const T*)a.x, (const T*)a.w, (const T*)a.bias, (const T*)a.z,
+                     (const T*)a.pre, (T*)a.y, cp);
 }
 
 }  // namespace

@@ -140,8 +140,8 @@ template <int BM, int BN, int PF, bool VEC, int NWM, int ACT>
 __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
                                           const half_t* __restrict__ wp,
                                           const half_t* __restrict__ bias, const half_t* z,
-                                          half_t* y, const ConvParams& cp, const HaloTile& ht,
-                                          const Unit& u) {
+                                          const half_t* pre, half_t* y, const ConvParams& cp,
+                                          const HaloTile& ht, const Unit& u) {
   constexpr int NT = 128 * NWM;  // threads
   constexpr int TP = BN / 32;
   constexpr int TM = BM / (16 * NWM);
@@ -430,6 +430,10 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
         __builtin_amdgcn_make_buffer_rsrc((void*)(y + wbase), (short)0, 0x7fffffff, kBufferWord3);
     const __amdgpu_buffer_rsrc_t zb = __builtin_amdgcn_make_buffer_rsrc(
         cp.has_z ? (void*)(z + wbase) : (void*)y, (short)0, cp.has_z ? 0x7fffffff : 0, kBufferWord3);
+    // backward data: the input pre-activation P, read like Z
+    const bool dpre = ACT == ACT_NONE && cp.bwd && cp.act != ACT_NONE;
+    const __amdgpu_buffer_rsrc_t pb = __builtin_amdgcn_make_buffer_rsrc(
+        dpre ? (void*)(pre + wbase) : (void*)y, (short)0, dpre ? 0x7fffffff : 0, kBufferWord3);
     auto voff = [&](int j, int it) __attribute__((always_inline)) {
       const int r = j * 16 + it * RPI + rsub;  // channel relative to mw0
       return (pok && mw0 + r < cp.Mg) ? (unsigned)((r * (int)cp.out_sz + pix) * 2) : kOff;
@@ -442,6 +446,14 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
         zr[j][it] = __builtin_bit_cast(uint2v, __builtin_amdgcn_raw_buffer_load_b64(zb, voff(j, it), 0, 0));
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
+      uint2v pr[ITER];
+      if constexpr (ACT == ACT_NONE) {
+        if (dpre) {
+#pragma unroll
+          for (int it = 0; it < ITER; ++it)
+            pr[it] = __builtin_bit_cast(uint2v, __builtin_amdgcn_raw_buffer_load_b64(pb, voff(j, it), 0, 0));
+        }
+      }
 #pragma unroll
       for (int i = 0; i < TP; ++i) *(float4v*)(stage + r16 * RP + i * 16 + q * 4) = acc[i][j];
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -454,6 +466,15 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
         act4_t v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = sv[e] + (float)zh[e];
+        if constexpr (ACT == ACT_NONE) {
+          if (dpre) {  // (acc + Z) * act'(P)
+            const half4 ph = __builtin_bit_cast(half4, pr[it]);
+            act4_t pv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pv[e] = (float)ph[e];
+            v *= dact_apply4(cp.act, pv, cp.alpha, cp.beta);
+          }
+        }
         v = act4<ACT>(v, cp.alpha, cp.beta);
         half4 out;
 #pragma unroll
@@ -527,6 +548,13 @@ __device__ __forceinline__ void halo_tile(const half_t* __restrict__ x,
         for (int r = 0; r < 4; ++r)
           if (r < nv) v4[r] += to_f32(z[yi + r]);
       }
+      if constexpr (ACT == ACT_NONE) {
+        if (cp.bwd && cp.act != ACT_NONE) {  // backward data: (acc + Z) * act'(P)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (r < nv) v4[r] *= dact_apply(cp.act, to_f32(pre[yi + r]), cp.alpha, cp.beta);
+        }
+      }
       v4 = act4<ACT>(v4, cp.alpha, cp.beta);
       half4 out;
 #pragma unroll
@@ -552,7 +580,8 @@ template <int BM, int BN, int PF, bool VEC, int NWM, int ACT>
 __global__ __launch_bounds__(128 * NWM, NWM == 2 ? 2 : 1) void halo_kernel(const half_t* __restrict__ x,
                                                            const half_t* __restrict__ wp,
                                                            const half_t* __restrict__ bias,
-                                                           const half_t* z, half_t* y,
+                                                           const half_t* z, const half_t* pre,
+                                                           half_t* y,
                                                            ConvParams cp, HaloTile ht) {
   const int per_g = ht.ntile * ht.nmb;
   Unit u;
@@ -576,7 +605,7 @@ __global__ __launch_bounds__(128 * NWM, NWM == 2 ? 2 : 1) void halo_kernel(const
   u.od0 = td_i * ht.TD;
   u.oh0 = th_i * ht.TH;
   u.ow0 = tw_i * ht.TW;
-  halo_tile<BM, BN, PF, VEC, NWM, ACT>(x, wp, bias, z, y, cp, ht, u);
+  halo_tile<BM, BN, PF, VEC, NWM, ACT>(x, wp, bias, z, pre, y, cp, ht, u);
 }
 
 struct Choice {
@@ -705,7 +734,7 @@ int launch_t(const Geometry& g, const Choice& ch, const RunArgs& a) {
   const unsigned blocks = (unsigned)((int64_t)ch.ht.ntile * ch.ht.nmb * cp.G);
   return launch_conv(halo_kernel<BM, BN, PF, VEC, NWM, FC_ACT>, dim3(blocks), dim3(128 * NWM), lds, a,
                      kEdgeBoth, (const half_t*)a.x, (const half_t*)a.ws, (const half_t*)a.bias,
-                     (const half_t*)a.z, (half_t*)a.y, cp, ch.ht);
+                     (const half_t*)a.z, (const half_t*)a.pre, (half_t*)a.y, cp, ch.ht);
 }
 
 }  // namespace
@@ -751,7 +780,8 @@ int prepare_igemm_halo(const Geometry& g, const Plan&, const RunArgs& a) {
 
 int launch_igemm_halo(const Geometry& g, const Plan&, const RunArgs& a) {
   static const ActLaunchFn table[ACT_COUNT] = FC_ACT_TABLE(launch_halo_act_);
-  return table[g.cp.act](g, a);
+  // the backward-data epilogue lives in the activation-free instance
+  return table[g.cp.bwd ? ACT_NONE : g.cp.act](g, a);
 }
 #endif
 

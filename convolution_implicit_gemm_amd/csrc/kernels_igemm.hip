@@ -122,7 +122,7 @@ template <typename T, int BM, int WGM, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void igemm_kernel(const T* __restrict__ x,
                                                          const T* __restrict__ w,
                                                          const T* __restrict__ bias,
-                                                         const T* z, T* y,
+                                                         const T* z, const T* pre, T* y,
                                                          float* __restrict__ part,
                                                          ConvParams cp, int k_tiles,
                                                          int kt_per_split, int avec) {
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(const T* __restrict__ x
           part[((int64_t)sidx * cp.M + gm) * cp.P + p] = acc[i][j][rr];
         } else {
           const int64_t yi = (nimg * cp.M + gm) * cp.out_sz + o;
-          y[yi] = epilogue<T>(acc[i][j][rr], gm, yi, cp, bias, z);
+          y[yi] = epilogue<T>(acc[i][j][rr], gm, yi, cp, bias, z, pre);
         }
       }
     }
@@ -297,8 +297,8 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(const T* __restrict__ x
 template <typename T>
 __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const float* __restrict__ part,
                                                                  const T* __restrict__ bias,
-                                                                 const T* z, T* y, ConvParams cp,
-                                                                 int split) {
+                                                                 const T* z, const T* pre, T* y,
+                                                                 ConvParams cp, int split) {
   const int64_t total = (int64_t)cp.M * cp.P;
   const int64_t step = (int64_t)gridDim.x * kThreads;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += step) {
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const float* __
     const int64_t p = i % cp.P;
     const int64_t nimg = p / cp.out_sz, o = p % cp.out_sz;
     const int64_t yi = (nimg * cp.M + gm) * cp.out_sz + o;
-    y[yi] = epilogue<T>(acc, gm, yi, cp, bias, z);
+    y[yi] = epilogue<T>(acc, gm, yi, cp, bias, z, pre);
   }
 }
 
@@ -321,18 +321,20 @@ int launch_t(const Geometry& g, const Plan& p, const RunArgs& a) {
   const int avec = (cp.K % (16 / (int)sizeof(T))) == 0;
   if (split) {
     if (launch_conv(igemm_kernel<T, BM, WGM, true>, grid, dim3(kThreads), 0, a, kEdgeFirst,
-                    (const T*)a.x, (const T*)a.w, (const T*)a.bias, (const T*)a.z, (T*)a.y,
-                    (float*)a.ws, cp, p.k_tiles, p.k_tiles_per_split, avec) != FUSEDCONV_OK)
+                    (const T*)a.x, (const T*)a.w, (const T*)a.bias, (const T*)a.z,
+                    (const T*)a.pre, (T*)a.y, (float*)a.ws, cp, p.k_tiles, p.k_tiles_per_split,
+                    avec) != FUSEDCONV_OK)
       return FUSEDCONV_ERR_LAUNCH;
     int64_t blocks = ((int64_t)cp.M * cp.P + kThreads - 1) / kThreads;
     if (blocks > (1 << 20)) blocks = 1 << 20;
     return launch_conv(splitk_reduce_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), 0, a,
-                       kEdgeLast, (const float*)a.ws, (const T*)a.bias, (const T*)a.z, (T*)a.y, cp,
-                       p.split_k);
+                       kEdgeLast, (const float*)a.ws, (const T*)a.bias, (const T*)a.z,
+                       (const T*)a.pre, (T*)a.y, cp, p.split_k);
   }
   return launch_conv(igemm_kernel<T, BM, WGM, false>, grid, dim3(kThreads), 0, a, kEdgeBoth,
-                     (const T*)a.x, (const T*)a.w, (const T*)a.bias, (const T*)a.z, (T*)a.y,
-                     (float*)nullptr, cp, p.k_tiles, p.k_tiles_per_split, avec);
+                     (const T*)a.x, (const T*)a.w, (const T*)a.bias, (const T*)a.z,
+                     (const T*)a.pre, (T*)a.y, (float*)nullptr, cp, p.k_tiles,
+                     p.k_tiles_per_split, avec);
 }
 
 }  // namespace

@@ -110,17 +110,19 @@ __global__ __launch_bounds__(kThreads) void pad_w_kernel(const half_t* __restric
 // reads the same input row (id, ih) = (od*sd - pd + kd*dd, oh*sh - ph +
 // kh*dh), and col row k = ((c*KD + kd)*KH + kh)*KW + kw holds the chunk's
 // pixels contiguously.  So the block loads the chunk's input rows once
-// (16-byte loads when W % 8 == 0; zero rows outside X) into LDS and then
-// writes, for each kw, the chunk's segment of col row k as whole 16-byte
-// pieces of 8 pixels.  LDS element j of a row sits at j + 2*(j >> 6) (4
-// bytes of skew per 128): the 8 pixels of a lane are sw apart, and the skew
-// spreads the lanes of a wave over the banks for any stride.  Extra blocks
-// (when Kp > K) write the zero rows k >= K of their chunk.
+// (16-byte loads when a row is a whole number of them; zero rows outside X)
+// into LDS and then writes, for each kw, the chunk's segment of col row k
+// as whole pieces of 8 pixels.  LDS element j of a row sits at j + 2*(j >> 6)
+// (skew of 2 elements per 64): the 8 pixels of a lane are sw apart, and the
+// skew spreads the lanes of a wave over the banks for any stride.  Extra
+// blocks (when Kq > K) write the rows k >= K of their chunk: zeros, except
+// row K when `ones` (1 for the P valid pixels: the bias-gradient row of the
+// weight-gradient GEMM).
 struct StagedGeo {
   int L;        // pixels per chunk (multiple of 8)
   int nchunk;   // chunks per col row: ceil(Pp / L)
   int rows;     // LDS rows per block (>= input rows a chunk can span)
-  int pitch;    // LDS row pitch in halves
+  int pitch;    // LDS row pitch in elements
   int64_t main_blocks;
   int64_t blocks;
 };
@@ -129,25 +131,50 @@ constexpr int kStagedLdsBytes = 32 * 1024;
 
 __device__ __forceinline__ int skew(int j) { return j + 2 * (j >> 6); }
 
-__global__ __launch_bounds__(kThreads) void im2col_staged_kernel(const half_t* __restrict__ x,
-                                                                 half_t* __restrict__ col,
-                                                                 ConvParams cp, int Kp,
-                                                                 int64_t Pp, StagedGeo sg) {
-  extern __shared__ half_t rows[];
+// 8 consecutive elements of T as one store (two 16-byte stores for float)
+template <typename T> struct Vec8;
+template <> struct Vec8<half_t> {
+  half8 v;
+  __device__ void set(int e, half_t x) { v[e] = x; }
+  __device__ void store(half_t* p) const { *(half8*)p = v; }
+};
+template <> struct Vec8<float> {
+  typedef float float4v_ __attribute__((ext_vector_type(4)));
+  float4v_ a, b;
+  __device__ void set(int e, float x) {
+    if (e < 4) a[e] = x; else b[e - 4] = x;
+  }
+  __device__ void store(float* p) const {
+    *(float4v_*)p = a;
+    *(float4v_*)(p + 4) = b;
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void im2col_staged_kernel(const T* __restrict__ x,
+                                                                 T* __restrict__ col,
+                                                                 ConvParams cp, int Kq,
+                                                                 int64_t Pp, int ones,
+                                                                 StagedGeo sg) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+  T* rows = (T*)lds_raw;
   const int tid = threadIdx.x;
   const int P = (int)cp.out_sz;
   int64_t t = blockIdx.x;
   if (t >= sg.main_blocks) {
-    // zero rows k = K .. Kp-1 of one (image, group) and chunk
+    // rows k = K .. Kq-1 of one (image, group) and chunk
     t -= sg.main_blocks;
     const int chunk = (int)(t % sg.nchunk);
     const int64_t ng = t / sg.nchunk;
     const int P0 = chunk * sg.L;
     const int noct = (int)(min((int64_t)sg.L, Pp - P0) / 8);
-    const int nz = Kp - cp.K;
+    const int nz = Kq - cp.K;
     for (int i = tid; i < nz * noct; i += kThreads) {
       const int k = cp.K + i / noct, o = i % noct;
-      *(half8*)(col + (ng * Kp + k) * Pp + P0 + 8 * o) = half8{};
+      Vec8<T> v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v.set(e, (ones && k == cp.K && P0 + 8 * o + e < P) ? (T)1 : (T)0);
+      v.store(col + (ng * Kq + k) * Pp + P0 + 8 * o);
     }
     return;
   }
@@ -166,34 +193,33 @@ __global__ __launch_bounds__(kThreads) void im2col_staged_kernel(const half_t* _
   const int Pv = min(Pend, P);                          // ... and in valid pixels (P0 < P)
   const int R0 = P0 / cp.OW;
   const int nrows = (Pv - 1) / cp.OW - R0 + 1;  // <= sg.rows (host)
-  const half_t* xc = x + (n * cp.C + (int64_t)g * cp.Cg + c) * cp.in_sz;
+  const T* xc = x + (n * cp.C + (int64_t)g * cp.Cg + c) * cp.in_sz;
 
   // stage the input rows of output rows R0 .. R0 + nrows - 1
-  auto row_src = [&](int r) -> const half_t* {
+  auto row_src = [&](int r) -> const T* {
     const int R = R0 + r;
     const int od = R / cp.OH, oh = R - od * cp.OH;
     const int id = od * cp.sd - cp.pd + kd * cp.dd, ih = oh * cp.sh - cp.ph + kh * cp.dh;
     if ((unsigned)id >= (unsigned)cp.D || (unsigned)ih >= (unsigned)cp.H) return nullptr;
     return xc + ((int64_t)id * cp.H + ih) * cp.W;
   };
-  if (cp.W % 8 == 0) {
-    const int wv = cp.W / 8;
+  constexpr int VE = 16 / sizeof(T);  // elements per 16-byte load
+  if (cp.W % VE == 0) {
+    typedef T tvec __attribute__((ext_vector_type(VE)));
+    const int wv = cp.W / VE;
     for (int i = tid; i < nrows * wv; i += kThreads) {
-      const int r = i / wv, j = (i - r * wv) * 8;
-      const half_t* src = row_src(r);
-      const half8 v = src ? *(const half8*)(src + j) : half8{};
-      half_t* dst = rows + r * sg.pitch + skew(j);  // 8 halves stay in one 64-block
+      const int r = i / wv, j = (i - r * wv) * VE;
+      const T* src = row_src(r);
+      const tvec v = src ? *(const tvec*)(src + j) : tvec{};
+      T* dst = rows + r * sg.pitch + skew(j);  // VE elements stay in one 64-block
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-        *(half2v*)(dst + e) = half2v{v[e], v[e + 1]};
-      }
+      for (int e = 0; e < VE; ++e) dst[e] = v[e];
     }
   } else {
     for (int i = tid; i < nrows * cp.W; i += kThreads) {
       const int r = i / cp.W, j = i - r * cp.W;
-      const half_t* src = row_src(r);
-      rows[r * sg.pitch + skew(j)] = src ? src[j] : (half_t)0;
+      const T* src = row_src(r);
+      rows[r * sg.pitch + skew(j)] = src ? src[j] : (T)0;
     }
   }
   __syncthreads();
@@ -201,31 +227,33 @@ __global__ __launch_bounds__(kThreads) void im2col_staged_kernel(const half_t* _
   // col rows k of this (c, kd, kh): one 8-pixel piece per thread and step
   const int noct = (Pend - P0) / 8;
   const int kbase = ((c * cp.KD + kd) * cp.KH + kh) * cp.KW;
-  half_t* colb = col + (ng * Kp + kbase) * Pp + P0;
+  T* colb = col + (ng * Kq + kbase) * Pp + P0;
   for (int i = tid; i < cp.KW * noct; i += kThreads) {
     const int kw = i / noct, o = i - kw * noct;
     const int p0 = P0 + 8 * o;
     int R = p0 / cp.OW, ow = p0 - R * cp.OW;
     const int iw0 = kw * cp.dw - cp.pw;
-    half8 v = {};
+    Vec8<T> v;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
+      T val = (T)0;
       if (p0 + e < Pv) {
         const int iw = ow * cp.sw + iw0;
-        if ((unsigned)iw < (unsigned)cp.W) v[e] = rows[(R - R0) * sg.pitch + skew(iw)];
+        if ((unsigned)iw < (unsigned)cp.W) val = rows[(R - R0) * sg.pitch + skew(iw)];
       }
+      v.set(e, val);
       if (++ow == cp.OW) {
         ow = 0;
         ++R;
       }
     }
-    *(half8*)(colb + (int64_t)kw * Pp + 8 * o) = v;
+    v.store(colb + (int64_t)kw * Pp + 8 * o);
   }
 }
 
-bool staged_plan(const ConvParams& cp, int Kp, int64_t Pp, StagedGeo& sg) {
+bool staged_plan(const ConvParams& cp, int Kq, int64_t Pp, int esize, StagedGeo& sg) {
   sg.pitch = cp.W + 2 * (cp.W >> 6) + 2;
-  sg.rows = kStagedLdsBytes / (sg.pitch * 2);
+  sg.rows = kStagedLdsBytes / (sg.pitch * esize);
   if (sg.rows < 2) return false;
   // a chunk of L pixels starting anywhere spans at most (L - 1) / OW + 2 rows
   const int64_t lmax = (int64_t)(sg.rows - 2) * cp.OW + 1;
@@ -238,46 +266,49 @@ bool staged_plan(const ConvParams& cp, int Kp, int64_t Pp, StagedGeo& sg) {
   sg.rows = (int)std::min<int64_t>(sg.rows, (L - 1) / cp.OW + 2);
   sg.nchunk = (int)((Pp + L - 1) / L);
   sg.main_blocks = cp.n * cp.G * cp.Cg * cp.KD * cp.KH * sg.nchunk;
-  sg.blocks = sg.main_blocks + (Kp > cp.K ? cp.n * cp.G * sg.nchunk : 0);
+  sg.blocks = sg.main_blocks + (Kq > cp.K ? cp.n * cp.G * sg.nchunk : 0);
   return sg.blocks < ((int64_t)1 << 31);
 }
 
-// ---- gather form (rows too wide to stage): col[((n*G + g)*Kp + k)*Pp + p]
-// for 8 consecutive pixels p per thread (one 16-byte store; Pp % 8 == 0 so
-// the 8 never leave the row of col); zeros at k >= K and p >= P
-__global__ __launch_bounds__(kThreads) void im2col_gather_kernel(const half_t* __restrict__ x,
-                                                                 half_t* __restrict__ col,
-                                                                 ConvParams cp, int Kp,
-                                                                 int64_t Pp) {
+// ---- gather form (rows too wide to stage): col[((n*G + g)*Kq + k)*Pp + p]
+// for 8 consecutive pixels p per thread (one piece of 8; Pp % 8 == 0 so the
+// 8 never leave the row of col); rows k >= K as in the staged form
+template <typename T>
+__global__ __launch_bounds__(kThreads) void im2col_gather_kernel(const T* __restrict__ x,
+                                                                 T* __restrict__ col,
+                                                                 ConvParams cp, int Kq,
+                                                                 int64_t Pp, int ones) {
   const int P = (int)cp.out_sz;
   const int64_t p8 = Pp / 8;
-  const int64_t total = cp.n * cp.G * Kp * p8;
+  const int64_t total = cp.n * cp.G * Kq * p8;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * kThreads) {
     const int pc = (int)(i % p8);
     int64_t r = i / p8;
-    const int k = (int)(r % Kp);
-    r /= Kp;  // n * G + g
+    const int k = (int)(r % Kq);
+    r /= Kq;  // n * G + g
     const int g = (int)(r % cp.G);
     const int64_t n = r / cp.G;
-    half8 v = {};
+    Vec8<T> v;
+    const int p0 = pc * 8;
     if (k < cp.K) {
       // k -> (c, kd, kh, kw) in W's order
       const int kw = k % cp.KW, kh = (k / cp.KW) % cp.KH, kd = (k / (cp.KW * cp.KH)) % cp.KD;
       const int c = k / cp.taps;
-      const half_t* xc = x + (n * cp.C + (int64_t)g * cp.Cg + c) * cp.in_sz;
-      const int p0 = pc * 8;
+      const T* xc = x + (n * cp.C + (int64_t)g * cp.Cg + c) * cp.in_sz;
       int ow = p0 % cp.OW, R = p0 / cp.OW;
       int oh = R % cp.OH, od = R / cp.OH;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
+        T val = (T)0;
         if (p0 + e < P) {
           const int id = od * cp.sd - cp.pd + kd * cp.dd, ih = oh * cp.sh - cp.ph + kh * cp.dh,
                     iw = ow * cp.sw - cp.pw + kw * cp.dw;
           if ((unsigned)id < (unsigned)cp.D && (unsigned)ih < (unsigned)cp.H &&
               (unsigned)iw < (unsigned)cp.W)
-            v[e] = xc[((int64_t)id * cp.H + ih) * cp.W + iw];
+            val = xc[((int64_t)id * cp.H + ih) * cp.W + iw];
         }
+        v.set(e, val);
         if (++ow == cp.OW) {
           ow = 0;
           if (++oh == cp.OH) {
@@ -286,8 +317,11 @@ __global__ __launch_bounds__(kThreads) void im2col_gather_kernel(const half_t* _
           }
         }
       }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v.set(e, (ones && k == cp.K && p0 + e < P) ? (T)1 : (T)0);
     }
-    *(half8*)(col + i * 8) = v;
+    v.store(col + i * 8);
   }
 }
 
@@ -319,6 +353,26 @@ int prepare_weights_impl(const Geometry& g, const Im2colGeo& ig, const RunArgs& 
 
 }  // namespace
 
+namespace {
+template <typename T>
+int launch_columns_t(const ConvParams& cp, const void* x, void* col, int Kq, int64_t Pp, int ones,
+                     const RunArgs& a, unsigned edges) {
+  StagedGeo sg;
+  if (staged_plan(cp, Kq, Pp, (int)sizeof(T), sg))
+    return launch_conv(im2col_staged_kernel<T>, dim3((unsigned)sg.blocks), dim3(kThreads),
+                       (size_t)sg.rows * sg.pitch * sizeof(T), a, edges, (const T*)x, (T*)col, cp,
+                       Kq, Pp, ones, sg);
+  return launch_conv(im2col_gather_kernel<T>, dim3(grid_for(cp.n * cp.G * Kq * (Pp / 8))),
+                     dim3(kThreads), 0, a, edges, (const T*)x, (T*)col, cp, Kq, Pp, ones);
+}
+}  // namespace
+
+int launch_columns(const ConvParams& cp, int32_t dtype, const void* x, void* col, int Kq,
+                   int64_t Pp, int ones, const RunArgs& a, unsigned edges) {
+  return dtype == FUSEDCONV_F16 ? launch_columns_t<half_t>(cp, x, col, Kq, Pp, ones, a, edges)
+                                : launch_columns_t<float>(cp, x, col, Kq, Pp, ones, a, edges);
+}
+
 bool im2col_fits(const ConvParams& cp, int32_t dtype, size_t* workspace) {
   Im2colGeo ig;
   if (!plan_geo(cp, dtype, ig)) return false;
@@ -345,15 +399,7 @@ int launch_im2col(const Geometry& g, const Plan&, const RunArgs& a) {
   // timed run spans both
   RunArgs ai = a;
   ai.ev_stop = nullptr;
-  StagedGeo sg;
-  const int rc =
-      staged_plan(cp, ig.Kp, ig.Pp, sg)
-          ? launch_conv(im2col_staged_kernel, dim3((unsigned)sg.blocks), dim3(kThreads),
-                        (size_t)sg.rows * sg.pitch * sizeof(half_t), ai, kEdgeFirst,
-                        (const half_t*)a.x, col, cp, ig.Kp, ig.Pp, sg)
-          : launch_conv(im2col_gather_kernel, dim3(grid_for(cp.n * cp.G * ig.Kp * (ig.Pp / 8))),
-                        dim3(kThreads), 0, ai, kEdgeFirst, (const half_t*)a.x, col, cp, ig.Kp,
-                        ig.Pp);
+  const int rc = launch_columns(cp, FUSEDCONV_F16, a.x, col, ig.Kp, ig.Pp, 0, ai, kEdgeFirst);
   if (rc != FUSEDCONV_OK) return rc;
   RunArgs b = a;
   b.x = col;

@@ -336,6 +336,74 @@ int fusedconv_run_timed(const fusedconv_handle* h, const void* x, const void* w,
 int fusedconv_run_noalloc(const fusedconv_handle* h, const void* x, const void* w,
                           const void* bias, const void* z, void* y, void* stream);
 
+/*
+ * Backward of the convolution, for training (the tinygrad compare page,
+ * tinygrad/codegen/opt/reduce.py: direct_conv_bwd_activation_program runs a
+ * 3x3 convolution's input gradient as per-tap GEMMs with the QuickGelu
+ * derivative fused into the epilogue, col2im_program assembles the same
+ * gradient from per-tap columns with an optional fused activation
+ * derivative).  G denotes the gradient of the loss with respect to the
+ * convolution's pre-activation output conv(X, W) + B + Z (the caller
+ * multiplies a gradient of Y by act'(pre-activation) first, or obtains G
+ * from the backward-data call of the layer above, which fuses it).
+ *
+ * fusedconv_create_backward_data: d describes the FORWARD convolution (x, w,
+ * group, strides, dilations, pads / auto_pad, kernel_shape, dtype) with
+ * these differences: d->activation and d->activation_params name the
+ * activation act_in that produced X from its pre-activation P (NULL:
+ * none); d->z present declares a residual gradient R with X's shape; d->bias
+ * must be absent.  The handle computes
+ *     dP = (conv^T(G, W) + R) * act_in'(P)
+ * (conv^T the adjoint of the cross-correlation in X; fp32 accumulation, one
+ * rounding; the derivative at the kinks of the piecewise activations is the
+ * one-sided value: Relu 0 at 0, LeakyRelu alpha at 0, Clip 1 on [min, max],
+ * HardSigmoid alpha strictly inside (0, 1), HardSwish x/3 + 1/2 strictly
+ * inside (-3, 3), ThresholdedRelu 0 at alpha).  Planning: with every stride
+ * 1 (and pads no larger than dilation*(k - 1)) the gradient is the forward
+ * convolution of G with W transposed per group and flipped, run on the
+ * IGEMM_HALO (fp16), IGEMM or DIRECT kernel with this epilogue; otherwise
+ * the gather kernel of the TRANSPOSED route.  d->route: AUTO, IGEMM_HALO,
+ * IGEMM, DIRECT (stride 1 only) or TRANSPOSED; d->split_k as for IGEMM.
+ * fusedconv_output_shape reports X's shape, fusedconv_workspace_size the
+ * workspace (the flipped W first, then the route's own).  Errors as for
+ * fusedconv_create; bias present: FUSEDCONV_ERR_BIAS_SHAPE; z not of X's
+ * shape: FUSEDCONV_ERR_Z_SHAPE.
+ *
+ * fusedconv_backward_data: dy = G (the forward Y's shape), w = W, pre = P
+ * (X's shape; required when act_in is set, else ignored), dres = R (X's
+ * shape; required iff declared), dx = dP (X's shape, dtype T, may not alias
+ * an input).  Device pointers, 16-byte aligned; enqueued on `stream`.
+ * A handle from any other create call: FUSEDCONV_ERR_ROUTE.
+ */
+int fusedconv_create_backward_data(const fusedconv_desc* d, fusedconv_handle** out);
+int fusedconv_backward_data(const fusedconv_handle* h, const void* dy, const void* w,
+                            const void* pre, const void* dres, void* dx, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * fusedconv_create_backward_weight: d describes the forward convolution as
+ * for fusedconv_create; d->bias present requests the bias gradient too;
+ * d->z, d->activation and its parameters are ignored.  The handle computes
+ *     dW[m, c, k] = sum over n, o of G[n, m, o] * X[n, g*(C/group) + c,
+ *                                                   o*stride - pad_begin + k*dilation]
+ *     dB[m]       = sum over n, o of G[n, m, o]
+ * in fp32 (fp32 accumulation; the fp16 products are exact).  Planning
+ * (d->route): AUTO or IM2COL, the column matrix of X (with a row of ones for
+ * dB) in the workspace times G on MFMA, image ranges summed by a second
+ * kernel; needs the output pixels per image to be a multiple of 4; DIRECT,
+ * one reduction per dW element (any problem).  fusedconv_output_shape
+ * reports W's shape.
+ *
+ * fusedconv_backward_weight: x = X, dy = G, dw = float [M][C/group][k...],
+ * db = float [M] (required iff the bias gradient was requested, else NULL).
+ * Device pointers, 16-byte aligned; enqueued on `stream`.  A handle from any
+ * other create call: FUSEDCONV_ERR_ROUTE.
+ */
+int fusedconv_create_backward_weight(const fusedconv_desc* d, fusedconv_handle** out);
+int fusedconv_backward_weight(const fusedconv_handle* h, const void* x, const void* dy,
+                              float* dw, float* db, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* Release a handle (NULL is allowed).  Host memory only; runs already
  * enqueued with it are unaffected (the kernels received everything by value). */
 void fusedconv_destroy(fusedconv_handle* h);

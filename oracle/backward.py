@@ -141,7 +141,8 @@ def conv_backward_data(dy, w, x_shape, *, group=1, strides=None, dilations=None,
         dyg = dy[:, g * Mg:(g + 1) * Mg]
         wg = w[g * Mg:(g + 1) * Mg]
         for tap in np.ndindex(*ksp):
-            contrib = np.einsum("nm...,mc->nc...", dyg, wg[(slice(None), slice(None)) + tap])
+            contrib = np.einsum("nm...,mc->nc...", dyg, wg[(slice(None), slice(None)) + tap],
+                                optimize=True)
             sl = tuple(slice(tap[i] * d[i], tap[i] * d[i] + s[i] * (out[i] - 1) + 1, s[i])
                        for i in range(nsp))
             buf[(slice(None), slice(g * Cg, (g + 1) * Cg)) + sl] += contrib
@@ -177,7 +178,7 @@ def conv_backward_weight(x, dy, w_shape, *, group=1, strides=None, dilations=Non
                        for i in range(nsp))
             xs = xg[(slice(None), slice(None)) + sl]
             dw[(slice(g * Mg, (g + 1) * Mg), slice(None)) + tap] = np.einsum(
-                "nmp,ncp->mc", dyg.reshape(n, Mg, -1), xs.reshape(n, Cg, -1))
+                "nmp,ncp->mc", dyg.reshape(n, Mg, -1), xs.reshape(n, Cg, -1), optimize=True)
     return dw
 
 

@@ -405,3 +405,105 @@ def test_depth_one_transposed_output_padding_takes_the_gather_kernel():
                  strides=[2, 2, 2])
     assert h.y_shape == [1, 16, 1, 16, 16]
     assert h.kernel_name.startswith("transposed_2x2s2_pointwise"), h.kernel_name
+
+
+# ---------------------------------------------------------------------------
+# Backward handles (fusedconv_create_backward_data / _weight): planning only.
+# ---------------------------------------------------------------------------
+
+def _bd(x, w, dtype="f16", z=None, **kw):
+    return B.Handle(dtype, x, w, None, z, kind="backward_data", **kw)
+
+
+def _bw(x, w, dtype="f16", bias=False, **kw):
+    return B.Handle(dtype, x, w, [w[0]] if bias else None, None, kind="backward_weight", **kw)
+
+
+def test_backward_data_planning():
+    # stride 1: the flipped-kernel forward problem, on the halo kernel (fp16,
+    # 16+ channels per group) or IGEMM / DIRECT; the workspace holds W' first
+    h = _bd([8, 64, 16, 16], [128, 64, 3, 3], pads=[1, 1, 1, 1], activation="QuickGelu")
+    assert h.route == "igemm_halo" and h.kernel_name.startswith("bwd_data_flip_igemm_halo")
+    assert h.y_shape == [8, 64, 16, 16]
+    flip = (128 * 64 * 9 * 2 + 255) // 256 * 256
+    fwd_ws = _h([8, 128, 16, 16], [64, 128, 3, 3], dtype="f16", pads=[1, 1, 1, 1],
+                route="igemm_halo").workspace_bytes
+    assert h.workspace_bytes == flip + fwd_ws
+    assert _bd([2, 12, 9, 9], [20, 12, 3, 3], dtype="f32").route == "igemm"       # full conv
+    assert _bd([2, 3, 9, 9], [5, 3, 3, 3], dtype="f32").route == "direct"         # 5 channels
+    assert _bd([2, 8, 9, 9], [8, 8, 3, 3], route="direct").route == "direct"
+    h = _bd([2, 16, 9, 9], [16, 16, 3, 3], dtype="f32", route="igemm", split_k=2)
+    assert h.route == "igemm" and h.split_k == 2
+    # strides, or pads beyond dilation*(k-1): the transposed gather kernel
+    for kw in [dict(strides=[2, 2], pads=[1, 1, 1, 1]), dict(pads=[3, 3, 3, 3]),
+               dict(strides=[1, 2])]:
+        h = _bd([2, 16, 12, 12], [32, 16, 3, 3], **kw)
+        assert h.route == "transposed" and h.kernel_name == "bwd_data_gather_f16", kw
+        assert h.workspace_bytes == 0 and h.y_shape == [2, 16, 12, 12]
+    assert _bd([2, 16, 12, 12], [32, 16, 3, 3], pads=[1, 1, 1, 1],
+               route="transposed").route == "transposed"
+    refused = [
+        (dict(x=[2, 16, 12, 12], w=[32, 16, 3, 3], strides=[2, 2], route="igemm"), "FUSEDCONV_ERR_ROUTE"),
+        (dict(x=[2, 16, 12, 12], w=[32, 16, 3, 3], route="pointwise"), "FUSEDCONV_ERR_ROUTE"),
+        (dict(x=[2, 16, 12, 12], w=[32, 16, 3, 3], z=[2, 32, 10, 10]), "FUSEDCONV_ERR_Z_SHAPE"),
+        (dict(x=[2, 16, 12, 12], w=[32, 16, 3, 3], activation="Nope"), "FUSEDCONV_ERR_ACTIVATION"),
+    ]
+    for c, status in refused:
+        c = dict(c)
+        with pytest.raises(B.FusedConvError) as e:
+            _bd(c.pop("x"), c.pop("w"), **c)
+        assert e.value.status == status, c
+    with pytest.raises(B.FusedConvError) as e:   # the input gradient takes no bias
+        B.Handle("f16", [2, 16, 12, 12], [32, 16, 3, 3], [32], None, kind="backward_data")
+    assert e.value.status == "FUSEDCONV_ERR_BIAS_SHAPE"
+    # the residual gradient has X's shape
+    assert _bd([2, 16, 12, 12], [32, 16, 3, 3], z=[2, 16, 12, 12]).route == "igemm_halo"
+
+
+def test_backward_weight_planning():
+    def al(v):
+        return (v + 255) // 256 * 256
+    # col [n][G][Kq][Pp] + fp32 partials [splits][M][Kq]; Kq = K (+1 bias row) rounded to 8
+    h = _bw([8, 64, 16, 16], [128, 64, 3, 3], bias=True, pads=[1, 1, 1, 1])
+    assert h.route == "im2col" and h.kernel_name == "bwd_weight_gemm_f16"
+    kq = (576 + 1 + 7) // 8 * 8
+    assert h.y_shape == [128, 64, 3, 3]
+    assert h.workspace_bytes == al(8 * kq * 256 * 2) + h.split_k * 128 * kq * 4
+    assert h.split_k == 8   # 1 x 5 tiles: up to 1024 blocks, at most one range per image
+    h = _bw([512, 128, 16, 16], [256, 128, 3, 3], pads=[1, 1, 1, 1])
+    assert h.split_k == 103 and h.workspace_bytes == al(512 * 1152 * 256 * 2) + 103 * 256 * 1152 * 4
+    h = _bw([2, 8, 10, 10], [6, 4, 3, 3], dtype="f32", group=2, strides=[2, 2])  # 4x4 outputs
+    assert h.route == "im2col" and h.kernel_name == "bwd_weight_gemm_f32"
+    # 15x15 outputs (not a multiple of 4): the plain reduction
+    assert _bw([2, 8, 15, 15], [6, 8, 1, 1], dtype="f32").route == "direct"
+    with pytest.raises(B.FusedConvError) as e:
+        _bw([2, 8, 15, 15], [6, 8, 1, 1], route="im2col")
+    assert e.value.status == "FUSEDCONV_ERR_ROUTE"
+    with pytest.raises(B.FusedConvError) as e:
+        _bw([2, 8, 16, 16], [6, 8, 1, 1], route="igemm")
+    assert e.value.status == "FUSEDCONV_ERR_ROUTE"
+    assert _bw([2, 8, 16, 16], [6, 8, 1, 1], route="direct").route == "direct"
+    with pytest.raises(B.FusedConvError) as e:   # the bias shape is still checked
+        B.Handle("f16", [2, 8, 16, 16], [6, 8, 1, 1], [5], None, kind="backward_weight")
+    assert e.value.status == "FUSEDCONV_ERR_BIAS_SHAPE"
+
+
+def test_handle_kinds_are_not_interchangeable():
+    """Each entry point refuses another kind of handle before touching the
+    device (the pointers below are never dereferenced)."""
+    lib = fc.load()
+    fake = 1 << 20   # 16-byte aligned, never dereferenced
+    fwd = _h([1, 8, 8, 8], [8, 8, 3, 3], dtype="f16", pads=[1, 1, 1, 1])
+    bd = _bd([1, 8, 8, 8], [8, 8, 3, 3], pads=[1, 1, 1, 1])
+    bw = _bw([1, 8, 8, 8], [8, 8, 3, 3], pads=[1, 1, 1, 1])
+    st = {v: k for k, v in B.STATUS.items()}["FUSEDCONV_ERR_ROUTE"]
+    for h in (bd, bw):
+        assert lib.fusedconv_run_ex(h._h, fake, fake, None, None, fake, fake, 1 << 30, 0,
+                                    None) == st
+        assert lib.fusedconv_prepare_weights(h._h, fake, fake, 1 << 30, None) == st
+    for h in (fwd, bw):
+        assert lib.fusedconv_backward_data(h._h, fake, fake, None, None, fake, fake, 1 << 30,
+                                           None) == st
+    for h in (fwd, bd):
+        assert lib.fusedconv_backward_weight(h._h, fake, fake, fake, None, fake, 1 << 30,
+                                             None) == st
