@@ -235,12 +235,21 @@ int fusedconv_create_backward_weight(const fusedconv_desc* d, fusedconv_handle**
   Plan& p = h->plan;
   memset(&p, 0, sizeof(p));
   p.split_k = 1;
-  int32_t route = d->route == FUSEDCONV_ROUTE_AUTO ? FUSEDCONV_ROUTE_IM2COL : d->route;
+  int32_t route = d->route;
   size_t ws = 0;
   int32_t splits = 1;
+  if (route == FUSEDCONV_ROUTE_AUTO)
+    route = wgrad_tap_fits(cp, g.dtype, h->has_db, nullptr, nullptr) ? FUSEDCONV_ROUTE_IGEMM_HALO
+                                                                     : FUSEDCONV_ROUTE_IM2COL;
   if (cp.transposed) {
     rc = FUSEDCONV_ERR_ROUTE;
     err = "weight gradients of forward convolutions only";
+  } else if (route == FUSEDCONV_ROUTE_IGEMM_HALO) {
+    if (!wgrad_tap_fits(cp, g.dtype, h->has_db, &ws, &splits)) {
+      rc = FUSEDCONV_ERR_ROUTE;
+      err = "the shifted-tap weight gradient needs fp16, stride 1, a 1-D or 2-D kernel of at "
+            "most 9 taps, W and output W multiples of 8 and C/group a multiple of 16";
+    }
   } else if (route == FUSEDCONV_ROUTE_IM2COL) {
     if (!wgrad_gemm_fits(cp, g.dtype, h->has_db, &ws, &splits)) {
       if (d->route == FUSEDCONV_ROUTE_AUTO) {
@@ -253,7 +262,7 @@ int fusedconv_create_backward_weight(const fusedconv_desc* d, fusedconv_handle**
     }
   } else if (route != FUSEDCONV_ROUTE_DIRECT) {
     rc = FUSEDCONV_ERR_ROUTE;
-    err = "the weight gradient runs on AUTO, IM2COL or DIRECT";
+    err = "the weight gradient runs on AUTO, IGEMM_HALO, IM2COL or DIRECT";
   }
   if (rc == FUSEDCONV_OK && route == FUSEDCONV_ROUTE_DIRECT &&
       (int64_t)cp.M * (cp.K + h->has_db) >= ((int64_t)1 << 31)) {
@@ -265,7 +274,11 @@ int fusedconv_create_backward_weight(const fusedconv_desc* d, fusedconv_handle**
     return set_last_error(rc, err);
   }
   p.route = route;
-  if (route == FUSEDCONV_ROUTE_IM2COL) {
+  if (route == FUSEDCONV_ROUTE_IGEMM_HALO) {
+    p.workspace = ws;
+    p.split_k = splits;
+    snprintf(p.name, sizeof(p.name), "bwd_weight_taps_f16");
+  } else if (route == FUSEDCONV_ROUTE_IM2COL) {
     p.workspace = ws;
     p.split_k = splits;
     snprintf(p.name, sizeof(p.name), "bwd_weight_gemm_%s", g.dtype == FUSEDCONV_F16 ? "f16" : "f32");

@@ -102,6 +102,10 @@ int launch_flip_weights(const ConvParams& f, int32_t dtype, const void* w, void*
 // dw: float [M][C/G][taps]; db: float [M] or NULL.
 bool wgrad_gemm_fits(const ConvParams& cp, int32_t dtype, int has_db, size_t* workspace,
                      int32_t* splits);
+// The shifted-tap form (plan route IGEMM_HALO): no column matrix, fp32
+// partials only.
+bool wgrad_tap_fits(const ConvParams& cp, int32_t dtype, int has_db, size_t* workspace,
+                    int32_t* splits);
 int launch_wgrad(const Geometry& g, const Plan& p, const void* x, const void* dy, float* dw,
                  float* db, void* ws, void* stream);
 

@@ -280,6 +280,235 @@ bool wg_plan(const ConvParams& cp, int32_t dtype, int has_db, WgGeo& wg, size_t*
   return true;
 }
 
+// ---- shifted-tap weight gradient (fp16, stride 1, 2-D or 1-D, up to 9
+// taps, W and OW multiples of 8, C/group a multiple of 16): no column
+// matrix.  The tinygrad page runs a 3x3 input gradient as nine per-tap
+// GEMMs; here the weight gradient is nine per-tap GEMMs over one staged box
+// of X.  Block = 4 waves along 256 output channels x 16 input channels x
+// every tap, over a range of images.  Per image and band of output rows:
+//   1. KW copies of the band's input rows of the 16 channels go to LDS,
+//      copy kw shifted by kw*dw - pw columns (zeros outside X), so that for
+//      every tap (kh, kw) the 8 pixels of an MFMA operand are one aligned
+//      16-byte LDS read: copy kw, row r + kh*dh, columns ow .. ow+7.  A copy
+//      piece is cut in registers out of the three 16-byte pieces of the
+//      input row around it (the shift is uniform: one switch case);
+//   2. steps of 32 pixels: the G operand (8 pixels of one output channel)
+//      is a 16-byte global load, prefetched a step ahead; per tap one LDS
+//      read and 4 MFMAs (v_mfma_f32_16x16x32_f16, reduction = pixels).
+// The blocks of channel tile 0 also sum G against an operand of ones (the
+// bias gradient).  Partials per image range go to [range][M][K (+1)], summed
+// by wgrad_reduce_kernel.  Blocks that share an image range and output
+// channels (they differ only in channel tile) are 8 block ids apart: the
+// same XCD, so G is read once per XCD's L2.
+constexpr int kTapCT = 16;            // input channels per block
+constexpr int kTapMaxTaps = 9;
+constexpr size_t kTapLds = 64 * 1024;
+
+struct TapGeo {
+  int BR;        // output rows per band
+  int R;         // box rows per band: BR + (KH-1)*dh
+  int nband;     // bands per image
+  int nct, nmt;  // channel tiles, 256-channel output tiles
+  int splits, ipb;
+  int Kq;        // partial row: K (+1 bias column)
+  int has_db;
+  int64_t outer;   // splits * G * nmt
+  int64_t blocks;  // outer rounded up to 8, times nct
+  size_t lds;      // bytes
+};
+
+// Elements 8+S .. 15+S of the 24 halves pc[0] | pc[1] | pc[2] (S compile-time).
+template <int S>
+__device__ __forceinline__ half8 window_t(const half8 (&pc)[3]) {
+  half8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = 8 + S + e;
+    r[e] = k < 8 ? pc[0][k & 7] : (k < 16 ? pc[1][k & 7] : pc[2][k & 7]);
+  }
+  return r;
+}
+
+// The same for a shift s in [-8, 8] that is uniform across the block.
+__device__ __forceinline__ half8 window(int s, const half8 (&pc)[3]) {
+  switch (s) {
+#define FC_WIN(S) \
+  case S: return window_t<S>(pc);
+    FC_WIN(-8) FC_WIN(-7) FC_WIN(-6) FC_WIN(-5) FC_WIN(-4) FC_WIN(-3) FC_WIN(-2) FC_WIN(-1)
+    FC_WIN(0) FC_WIN(1) FC_WIN(2) FC_WIN(3) FC_WIN(4) FC_WIN(5) FC_WIN(6) FC_WIN(7) FC_WIN(8)
+#undef FC_WIN
+    default: return half8{};
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void wgrad_tap_kernel(const half_t* __restrict__ x,
+                                                                const half_t* __restrict__ dy,
+                                                                float* __restrict__ part,
+                                                                ConvParams cp, TapGeo tg) {
+  extern __shared__ __attribute__((aligned(16))) half_t lds[];
+  const int64_t b = blockIdx.x;
+  const int ct = (int)((b >> 3) % tg.nct);
+  const int64_t outer = ((b >> 3) / tg.nct) * 8 + (b & 7);
+  if (outer >= tg.outer) return;
+  const int mt = (int)(outer % tg.nmt);
+  const int64_t t2 = outer / tg.nmt;
+  const int g = (int)(t2 % cp.G);
+  const int s = (int)(t2 / cp.G);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, q = lane >> 4;
+  const int m0 = mt * 256 + wave * 64;
+  const int c0 = ct * kTapCT;
+  const int taps = cp.KH * cp.KW;
+  const int R = tg.R, W = cp.W, OW = cp.OW;
+  const int64_t P = cp.out_sz;
+  half_t* cpy = lds;  // [KW][16][R][OW]
+  // LDS offset of tap t's operand relative to copy 0, row 0
+  int toff[kTapMaxTaps];
+#pragma unroll
+  for (int t = 0; t < kTapMaxTaps; ++t) {
+    const int kh = t / cp.KW, kw = t - kh * cp.KW;
+    toff[t] = (kw * kTapCT * R + kh * cp.dh) * OW;
+  }
+  const bool do_db = tg.has_db && ct == 0;
+  const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+  bool am[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) am[i] = m0 + i * 16 + r16 < cp.Mg;
+
+  float4v acc[4][kTapMaxTaps], dacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    dacc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < kTapMaxTaps; ++t) acc[i][t] = float4v{0.f, 0.f, 0.f, 0.f};
+  }
+  const int64_t n0 = (int64_t)s * tg.ipb;
+  const int nimg = (int)std::min<int64_t>(tg.ipb, cp.n - n0);
+  const int W8 = W / 8, OW8 = OW / 8;
+  for (int ii = 0; ii < nimg; ++ii) {
+    const int64_t n = n0 + ii;
+    const half_t* xg = x + (n * cp.C + (int64_t)g * cp.Cg + c0) * cp.in_sz;
+    const half_t* gg = dy + (n * cp.M + (int64_t)g * cp.Mg + m0 + r16) * P;
+    for (int band = 0; band < tg.nband; ++band) {
+      const int oh0 = band * tg.BR;
+      // 1. the KW shifted copies of the band's input rows, straight from X:
+      // a copy piece (8 output columns) is a window of the three 16-byte
+      // pieces of the input row around it (zeros outside X)
+      if (band > 0 || ii > 0) __syncthreads();  // the previous products are done
+      for (int i = tid; i < kTapCT * R * OW8; i += kThreads) {
+        const int c = i / (R * OW8), r2 = i - c * (R * OW8);
+        const int rr = r2 / OW8, u = r2 - rr * OW8;
+        const int ih = oh0 - cp.ph + rr;
+        const bool rok = (unsigned)ih < (unsigned)cp.H;
+        const half_t* row = xg + (int64_t)c * cp.in_sz + (int64_t)(rok ? ih : 0) * W;
+        half8 pc[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          const int pu = u - 1 + k;
+          pc[k] = (rok && (unsigned)pu < (unsigned)W8) ? *(const half8*)(row + 8 * pu) : half8{};
+        }
+        half_t* dst = cpy + (c * R + rr) * OW + 8 * u;
+        for (int kw = 0; kw < cp.KW; ++kw)
+          *(half8*)(dst + kw * kTapCT * R * OW) = window(kw * cp.dw - cp.pw, pc);
+      }
+      __syncthreads();
+      // 2. products over the band's pixels
+      const int bandpix = std::min(tg.BR, cp.OH - oh0) * OW;
+      const int nst = (bandpix + 31) / 32;
+      half8 a[4], na[4];
+      auto load_a = [&](int st, half8 (&v)[4]) __attribute__((always_inline)) {
+        const int p = st * 32 + 8 * q;
+        const bool ok = p < bandpix;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[i] = (ok && am[i]) ? *(const half8*)(gg + (int64_t)i * 16 * P + (int64_t)oh0 * OW + p)
+                               : half8{};
+      };
+      load_a(0, a);
+      int r = (8 * q) / OW, ow = 8 * q - r * OW;  // this lane's pixels in the band
+      for (int st = 0; st < nst; ++st) {
+        if (st + 1 < nst) load_a(st + 1, na);
+        const bool ok = st * 32 + 8 * q < bandpix;
+        const half_t* cb = cpy + (r16 * R + (ok ? r : 0)) * OW + (ok ? ow : 0);
+#pragma unroll
+        for (int t = 0; t < kTapMaxTaps; ++t) {
+          if (t < taps) {
+            const half8 bv = ok ? *(const half8*)(cb + toff[t]) : half8{};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bv, acc[i][t], 0, 0, 0);
+          }
+        }
+        if (do_db) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            dacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], ones, dacc[i], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = na[i];
+        ow += 32;
+        while (ow >= OW) {
+          ow -= OW;
+          ++r;
+        }
+      }
+    }
+  }
+  // wait states between the last products and the VALU reads of their
+  // accumulators
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  // lane: rows (channels) 4q + r, column r16 (input channel c0 + r16) of
+  // every tap's tile; the ones column gives the same sum in every column
+  float* pb = part + ((int64_t)s * cp.M + (int64_t)g * cp.Mg) * tg.Kq;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + i * 16 + q * 4 + r;
+      if (m >= cp.Mg) continue;
+#pragma unroll
+      for (int t = 0; t < kTapMaxTaps; ++t)
+        if (t < taps) pb[(int64_t)m * tg.Kq + (c0 + r16) * taps + t] = acc[i][t][r];
+      if (do_db && r16 == 0) pb[(int64_t)m * tg.Kq + cp.K] = dacc[i][r];
+    }
+}
+
+bool tap_plan(const ConvParams& cp, int32_t dtype, int has_db, TapGeo& tg, size_t* part_bytes) {
+  if (dtype != FUSEDCONV_F16 || cp.transposed || cp.D != 1 || cp.KD != 1 || cp.OD != 1 ||
+      cp.pd != 0 || cp.sh != 1 || cp.sw != 1)
+    return false;
+  if (cp.KH * cp.KW > kTapMaxTaps || cp.W % 8 || cp.OW % 8 || cp.Cg % kTapCT) return false;
+  // a copy's column shift kw*dw - pw stays within one 16-byte piece either side
+  if (cp.pw > 8 || (int64_t)(cp.KW - 1) * cp.dw - cp.pw > 8) return false;
+  if ((int64_t)cp.H * cp.W >= ((int64_t)1 << 31) || cp.out_sz >= ((int64_t)1 << 31)) return false;
+  const int span = (cp.KH - 1) * cp.dh;
+  // the largest band of output rows whose rows and copies fit the LDS budget
+  const size_t per_row = (size_t)kTapCT * cp.KW * cp.OW * sizeof(half_t);
+  const int64_t rmax = (int64_t)(kTapLds / per_row);
+  if (rmax < span + 1) return false;
+  tg.BR = (int)std::min<int64_t>(cp.OH, rmax - span);
+  tg.R = tg.BR + span;
+  tg.nband = (int)cdiv(cp.OH, tg.BR);
+  tg.lds = (size_t)tg.R * per_row;
+  tg.nct = cp.Cg / kTapCT;
+  tg.nmt = (int)cdiv(cp.Mg, 256);
+  tg.has_db = has_db;
+  tg.Kq = cp.K + has_db;
+  const int64_t tiles = (int64_t)cp.G * tg.nmt * tg.nct;
+  // about two blocks per CU, at least one image per range
+  const int64_t splits = std::max<int64_t>(1, std::min<int64_t>(cp.n, cdiv(512, tiles)));
+  tg.ipb = (int)cdiv(cp.n, splits);
+  tg.splits = (int)cdiv(cp.n, tg.ipb);
+  tg.outer = (int64_t)tg.splits * cp.G * tg.nmt;
+  tg.blocks = cdiv(tg.outer, 8) * 8 * tg.nct;
+  if (tg.blocks >= ((int64_t)1 << 31)) return false;
+  *part_bytes = (size_t)tg.splits * cp.M * tg.Kq * sizeof(float);
+  return true;
+}
+
 unsigned grid_for(int64_t work, int64_t cap) {
   int64_t b = (work + kThreads - 1) / kThreads;
   return (unsigned)std::max<int64_t>(1, std::min(b, cap));
@@ -296,6 +525,27 @@ int launch_wgrad_t(const Geometry& g, const Plan& p, const void* x, const void* 
     return launch_conv(wgrad_direct_kernel<T>, dim3((unsigned)((int64_t)cp.M * (cp.K + has_db))),
                        dim3(kThreads), 0, a, kEdgeNone, (const T*)x, (const T*)dy, dw, db, cp,
                        has_db);
+  }
+  if (p.route == FUSEDCONV_ROUTE_IGEMM_HALO) {
+    if constexpr (sizeof(T) != 2) {
+      return FUSEDCONV_ERR_ROUTE;
+    } else {
+      TapGeo tg;
+      size_t part_bytes = 0;
+      if (!tap_plan(cp, g.dtype, db != nullptr, tg, &part_bytes)) return FUSEDCONV_ERR_ROUTE;
+      if (set_max_dynamic_lds((const void*)wgrad_tap_kernel, (int)kTapLds) != FUSEDCONV_OK)
+        return FUSEDCONV_ERR_LAUNCH;
+      float* part = (float*)ws;
+      int rc = launch_conv(wgrad_tap_kernel, dim3((unsigned)tg.blocks), dim3(kThreads), tg.lds, a,
+                           kEdgeNone, (const half_t*)x, (const half_t*)dy, part, cp, tg);
+      if (rc != FUSEDCONV_OK) return rc;
+      WgGeo wg{};
+      wg.Kq = tg.Kq;
+      wg.splits = tg.splits;
+      wg.has_db = tg.has_db;
+      return launch_conv(wgrad_reduce_kernel, dim3(grid_for((int64_t)cp.M * wg.Kq, 8192)),
+                         dim3(kThreads), 0, a, kEdgeNone, (const float*)part, dw, db, cp, wg);
+    }
   }
   WgGeo wg;
   size_t col_bytes = 0, part_bytes = 0;
@@ -333,6 +583,16 @@ bool wgrad_gemm_fits(const ConvParams& cp, int32_t dtype, int has_db, size_t* wo
   if (!wg_plan(cp, dtype, has_db, wg, &col_bytes, &part_bytes)) return false;
   if (workspace) *workspace = col_bytes + part_bytes;
   if (splits) *splits = wg.splits;
+  return true;
+}
+
+bool wgrad_tap_fits(const ConvParams& cp, int32_t dtype, int has_db, size_t* workspace,
+                    int32_t* splits) {
+  TapGeo tg;
+  size_t part_bytes = 0;
+  if (!tap_plan(cp, dtype, has_db, tg, &part_bytes)) return false;
+  if (workspace) *workspace = part_bytes;
+  if (splits) *splits = tg.splits;
   return true;
 }
 

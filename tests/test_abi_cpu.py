@@ -463,14 +463,31 @@ def test_backward_data_planning():
 def test_backward_weight_planning():
     def al(v):
         return (v + 255) // 256 * 256
-    # col [n][G][Kq][Pp] + fp32 partials [splits][M][Kq]; Kq = K (+1 bias row) rounded to 8
+    # fp16, stride 1, up to 9 taps, W and OW multiples of 8, C/group a multiple
+    # of 16: the shifted-tap kernel, fp32 partials [splits][M][K + 1] only
     h = _bw([8, 64, 16, 16], [128, 64, 3, 3], bias=True, pads=[1, 1, 1, 1])
+    assert h.route == "igemm_halo" and h.kernel_name == "bwd_weight_taps_f16"
+    # 1 x 4 tiles: up to 512 blocks, at most one range per image
+    assert h.split_k == 8 and h.workspace_bytes == 8 * 128 * (576 + 1) * 4
+    h = _bw([512, 128, 16, 16], [256, 128, 3, 3], pads=[1, 1, 1, 1])
+    assert h.route == "igemm_halo" and h.split_k == 64
+    assert h.workspace_bytes == 64 * 256 * 1152 * 4
+    for xs, ws, kw in [([2, 64, 16, 12], [32, 64, 3, 3], dict(pads=[1, 1, 1, 1])),   # W 12
+                       ([2, 24, 16, 16], [32, 24, 3, 3], dict(pads=[1, 1, 1, 1])),   # C 24
+                       ([2, 32, 16, 16], [32, 32, 5, 5], dict(pads=[2, 2, 2, 2])),   # 25 taps
+                       ([2, 32, 16, 16], [32, 32, 3, 3], dict(strides=[2, 2], pads=[1, 1, 1, 1]))]:
+        assert _bw(xs, ws, **kw).route == "im2col", (xs, ws, kw)
+        with pytest.raises(B.FusedConvError):
+            _bw(xs, ws, route="igemm_halo", **kw)
+    assert _bw([2, 32, 16, 16], [32, 32, 3, 3], dtype="f32", pads=[1, 1, 1, 1]).route == "im2col"
+    # col [n][G][Kq][Pp] + fp32 partials [splits][M][Kq]; Kq = K (+1 bias row) rounded to 8
+    h = _bw([8, 64, 16, 16], [128, 64, 3, 3], bias=True, pads=[1, 1, 1, 1], route="im2col")
     assert h.route == "im2col" and h.kernel_name == "bwd_weight_gemm_f16"
     kq = (576 + 1 + 7) // 8 * 8
     assert h.y_shape == [128, 64, 3, 3]
     assert h.workspace_bytes == al(8 * kq * 256 * 2) + h.split_k * 128 * kq * 4
     assert h.split_k == 8   # 1 x 5 tiles: up to 1024 blocks, at most one range per image
-    h = _bw([512, 128, 16, 16], [256, 128, 3, 3], pads=[1, 1, 1, 1])
+    h = _bw([512, 128, 16, 16], [256, 128, 3, 3], pads=[1, 1, 1, 1], route="im2col")
     assert h.split_k == 103 and h.workspace_bytes == al(512 * 1152 * 256 * 2) + 103 * 256 * 1152 * 4
     h = _bw([2, 8, 10, 10], [6, 4, 3, 3], dtype="f32", group=2, strides=[2, 2])  # 4x4 outputs
     assert h.route == "im2col" and h.kernel_name == "bwd_weight_gemm_f32"

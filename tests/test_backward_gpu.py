@@ -165,9 +165,33 @@ WEIGHT_CASES = [
 
 @pytest.mark.parametrize("ci", range(len(WEIGHT_CASES)))
 def test_backward_weight(ci):
+    # the column-matrix GEMM (the planner's choice for all of these but case 0)
     dtype, xs, ws, attrs = WEIGHT_CASES[ci]
-    assert run_weight(dtype, xs, ws, attrs, [9900, ci], bias=True) == "im2col"
-    assert run_weight(dtype, xs, ws, attrs, [9901, ci], bias=False) == "im2col"
+    assert run_weight(dtype, xs, ws, attrs, [9900, ci], bias=True, route="im2col") == "im2col"
+    assert run_weight(dtype, xs, ws, attrs, [9901, ci], bias=False, route="im2col") == "im2col"
+
+
+TAP_CASES = [
+    # the shifted-tap kernel: fp16, stride 1, <= 9 taps, W and OW multiples of
+    # 8, C/group a multiple of 16
+    ([4, 64, 16, 16], [96, 64, 3, 3], dict(pads=[1, 1, 1, 1])),
+    ([2, 32, 16, 16], [64, 16, 3, 3], dict(pads=[1, 1, 1, 1], group=2)),
+    ([2, 16, 24, 32], [300, 16, 3, 3], dict(pads=[1, 1, 1, 1])),         # 2 output tiles, M 300
+    ([1, 32, 8, 64], [32, 32, 1, 3], dict(pads=[0, 1, 0, 1])),           # 1x3
+    ([3, 16, 16, 16], [16, 16, 3, 3], dict(pads=[2, 2, 2, 2], dilations=[2, 2])),
+    ([2, 32, 64], [48, 32, 5], dict(pads=[2, 2])),                       # 1-D, 5 taps
+    ([1, 16, 100, 48], [32, 16, 3, 3], dict(pads=[1, 1, 1, 1])),         # 13 bands of 8 rows
+    ([2, 16, 18, 16], [24, 16, 3, 3], dict(pads=[0, 1, 0, 1])),          # valid rows, OH 16
+]
+
+
+@pytest.mark.parametrize("ci", range(len(TAP_CASES)))
+def test_backward_weight_shifted_taps(ci):
+    xs, ws, attrs = TAP_CASES[ci]
+    assert run_weight("f16", xs, ws, attrs, [9920, ci], bias=True) == "igemm_halo"
+    assert run_weight("f16", xs, ws, attrs, [9921, ci], bias=False) == "igemm_halo"
+    # the same problem on the column-matrix GEMM
+    assert run_weight("f16", xs, ws, attrs, [9920, ci], bias=True, route="im2col") == "im2col"
 
 
 def test_backward_weight_plain_reduction():
@@ -220,7 +244,7 @@ def test_full_size_headline_backward():
     log(f"RESULT full-size bwd-data {name}: {rel:.3e} over {dx.size} outputs")
     assert rel <= TAU_X["f16"]
     opw = fc.ConvBackwardWeight(xs, ws, "f16", True, **attrs)
-    log(f"CASE full-size bwd-weight {name} splits={opw.handle.split_k}")
+    log(f"CASE full-size bwd-weight {name} route={opw.handle.route} splits={opw.handle.split_k}")
     dw, db = opw(dev(inp["x"]), dev(g))
     dw, db = dw.cpu().numpy(), db.cpu().numpy()
     ref_w = bwd.conv_backward_weight(inp["x"], g, ws, **attrs)
