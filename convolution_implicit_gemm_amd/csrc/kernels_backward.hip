@@ -293,8 +293,11 @@ bool wg_plan(const ConvParams& cp, int32_t dtype, int has_db, WgGeo& wg, size_t*
 //      piece is cut in registers out of the three 16-byte pieces of the
 //      input row around it (the shift is uniform: one switch case);
 //   2. steps of 32 pixels: the G operand (8 pixels of one output channel)
-//      is a 16-byte global load, prefetched a step ahead; per tap one LDS
-//      read and 4 MFMAs (v_mfma_f32_16x16x32_f16, reduction = pixels).
+//      arrives through a per-wave LDS ring filled by buffer_load ... lds two
+//      steps ahead (across band and image boundaries, so the next image's
+//      first steps load during its copies), no registers held; each lane
+//      reads back its own 16 bytes after an explicit vmcnt wait.  Per tap one
+//      LDS read and 4 MFMAs (v_mfma_f32_16x16x32_f16, reduction = pixels).
 // The blocks of channel tile 0 also sum G against an operand of ones (the
 // bias gradient).  Partials per image range go to [range][M][K (+1)], summed
 // by wgrad_reduce_kernel.  Blocks that share an image range and output
@@ -302,7 +305,9 @@ bool wg_plan(const ConvParams& cp, int32_t dtype, int has_db, WgGeo& wg, size_t*
 // same XCD, so G is read once per XCD's L2.
 constexpr int kTapCT = 16;            // input channels per block
 constexpr int kTapMaxTaps = 9;
-constexpr size_t kTapLds = 64 * 1024;
+constexpr int kTapRing = 3;           // G steps in the per-wave LDS ring: the current one + 2 ahead
+constexpr size_t kTapRingBytes = (size_t)4 * kTapRing * 4 * 64 * 16;  // 4 waves x ring x 4 tiles x 1 KB
+constexpr size_t kTapLds = 80 * 1024;  // two blocks per CU
 
 struct TapGeo {
   int BR;        // output rows per band
@@ -341,6 +346,7 @@ __device__ __forceinline__ half8 window(int s, const half8 (&pc)[3]) {
   }
 }
 
+template <int TAPS>
 __global__ __launch_bounds__(kThreads, 2) void wgrad_tap_kernel(const half_t* __restrict__ x,
                                                                 const half_t* __restrict__ dy,
                                                                 float* __restrict__ part,
@@ -359,37 +365,76 @@ __global__ __launch_bounds__(kThreads, 2) void wgrad_tap_kernel(const half_t* __
   const int r16 = lane & 15, q = lane >> 4;
   const int m0 = mt * 256 + wave * 64;
   const int c0 = ct * kTapCT;
-  const int taps = cp.KH * cp.KW;
   const int R = tg.R, W = cp.W, OW = cp.OW;
   const int64_t P = cp.out_sz;
-  half_t* cpy = lds;  // [KW][16][R][OW]
+  // [KW][16][CP]: channel planes of R rows x OW, CP = R*OW + 8 halves apart
+  // (16 bytes of skew: the 16 channels of an operand read then fall on 16
+  // different 4-bank groups)
+  const int CP = R * OW + 8;
+  half_t* cpy = lds;
   // LDS offset of tap t's operand relative to copy 0, row 0
-  int toff[kTapMaxTaps];
+  int toff[TAPS];
 #pragma unroll
-  for (int t = 0; t < kTapMaxTaps; ++t) {
+  for (int t = 0; t < TAPS; ++t) {
     const int kh = t / cp.KW, kw = t - kh * cp.KW;
-    toff[t] = (kw * kTapCT * R + kh * cp.dh) * OW;
+    toff[t] = kw * kTapCT * CP + kh * cp.dh * OW;
   }
   const bool do_db = tg.has_db && ct == 0;
   const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
-  bool am[4];
+  // the wave's G ring: slot k, tile i at ring + (k*4 + i)*512 halves, lane l's
+  // 16 bytes at + 8l (buffer_load ... lds writes a wave's 64 pieces in lane order)
+  half_t* ring = lds + (tg.lds - kTapRingBytes) / sizeof(half_t) + wave * (kTapRing * 4 * 512);
+  const int64_t n0 = (int64_t)s * tg.ipb;
+  const int nimg = (int)std::min<int64_t>(tg.ipb, cp.n - n0);
+  const int rows_ok = std::max(0, std::min(64, cp.Mg - m0));  // valid G rows of this wave
+  // issue pointer: the next (image, band, step) whose G operands are loaded
+  int iss_img = 0, iss_band = 0, iss_st = 0, issued = 0;
+  auto band_steps = [&](int band) __attribute__((always_inline)) {
+    return (std::min(tg.BR, cp.OH - band * tg.BR) * OW + 31) / 32;
+  };
+  auto issue = [&]() __attribute__((always_inline)) {
+    if (iss_img >= nimg) return;
+    const int64_t n = n0 + iss_img;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(dy + (n * cp.M + (int64_t)g * cp.Mg + m0) * P), (short)0,
+        (int)((int64_t)rows_ok * P * (int64_t)sizeof(half_t)), 0x00020000);
+    const int oh0 = iss_band * tg.BR;
+    const int bandpix = std::min(tg.BR, cp.OH - oh0) * OW;
+    const int p = iss_st * 32 + 8 * q;
+    half_t* slot = ring + (issued % kTapRing) * 4 * 512;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) am[i] = m0 + i * 16 + r16 < cp.Mg;
+    for (int i = 0; i < 4; ++i) {
+      const int row = i * 16 + r16;
+      const unsigned off = (p < bandpix && row < rows_ok)
+                               ? (unsigned)(((int64_t)row * P + (int64_t)oh0 * OW + p) * 2)
+                               : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(slot + i * 512), 16, off, 0, 0, 0);
+    }
+    ++issued;
+    if (++iss_st == band_steps(iss_band)) {
+      iss_st = 0;
+      if (++iss_band == tg.nband) {
+        iss_band = 0;
+        ++iss_img;
+      }
+    }
+  };
+  // before the first copies: their loads hide the first steps' latency
+  for (int k = 0; k < kTapRing - 1; ++k) issue();
 
-  float4v acc[4][kTapMaxTaps], dacc[4];
+  float4v acc[4][TAPS], dacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     dacc[i] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < kTapMaxTaps; ++t) acc[i][t] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < TAPS; ++t) acc[i][t] = float4v{0.f, 0.f, 0.f, 0.f};
   }
-  const int64_t n0 = (int64_t)s * tg.ipb;
-  const int nimg = (int)std::min<int64_t>(tg.ipb, cp.n - n0);
   const int W8 = W / 8, OW8 = OW / 8;
+  int cur = 0;  // steps consumed
   for (int ii = 0; ii < nimg; ++ii) {
     const int64_t n = n0 + ii;
     const half_t* xg = x + (n * cp.C + (int64_t)g * cp.Cg + c0) * cp.in_sz;
-    const half_t* gg = dy + (n * cp.M + (int64_t)g * cp.Mg + m0 + r16) * P;
     for (int band = 0; band < tg.nband; ++band) {
       const int oh0 = band * tg.BR;
       // 1. the KW shifted copies of the band's input rows, straight from X:
@@ -408,45 +453,52 @@ __global__ __launch_bounds__(kThreads, 2) void wgrad_tap_kernel(const half_t* __
           const int pu = u - 1 + k;
           pc[k] = (rok && (unsigned)pu < (unsigned)W8) ? *(const half8*)(row + 8 * pu) : half8{};
         }
-        half_t* dst = cpy + (c * R + rr) * OW + 8 * u;
+        half_t* dst = cpy + c * CP + rr * OW + 8 * u;
         for (int kw = 0; kw < cp.KW; ++kw)
-          *(half8*)(dst + kw * kTapCT * R * OW) = window(kw * cp.dw - cp.pw, pc);
+          *(half8*)(dst + kw * kTapCT * CP) = window(kw * cp.dw - cp.pw, pc);
       }
       __syncthreads();
       // 2. products over the band's pixels
       const int bandpix = std::min(tg.BR, cp.OH - oh0) * OW;
       const int nst = (bandpix + 31) / 32;
-      half8 a[4], na[4];
-      auto load_a = [&](int st, half8 (&v)[4]) __attribute__((always_inline)) {
-        const int p = st * 32 + 8 * q;
-        const bool ok = p < bandpix;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          v[i] = (ok && am[i]) ? *(const half8*)(gg + (int64_t)i * 16 * P + (int64_t)oh0 * OW + p)
-                               : half8{};
-      };
-      load_a(0, a);
       int r = (8 * q) / OW, ow = 8 * q - r * OW;  // this lane's pixels in the band
       for (int st = 0; st < nst; ++st) {
-        if (st + 1 < nst) load_a(st + 1, na);
-        const bool ok = st * 32 + 8 * q < bandpix;
-        const half_t* cb = cpy + (r16 * R + (ok ? r : 0)) * OW + (ok ? ow : 0);
-#pragma unroll
-        for (int t = 0; t < kTapMaxTaps; ++t) {
-          if (t < taps) {
-            const half8 bv = ok ? *(const half8*)(cb + toff[t]) : half8{};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bv, acc[i][t], 0, 0, 0);
-          }
+        // keep two steps ahead in the ring; then wait for this step's four
+        // loads (a wave's loads complete in issue order, and nothing but
+        // these ring loads is in flight here)
+        while (issued < cur + kTapRing && iss_img < nimg) issue();
+        __builtin_amdgcn_sched_barrier(0);
+        switch (issued - cur - 1) {
+          case 0: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); break;
+          case 1: __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8)); break;
+          default: __builtin_amdgcn_s_waitcnt(8 | (7 << 4) | (15 << 8)); break;
         }
+        __builtin_amdgcn_sched_barrier(0);
+        half8 a[4];
+        const half_t* slot = ring + (cur % kTapRing) * 4 * 512 + lane * 8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = *(const half8*)(slot + i * 512);
+        const bool ok = st * 32 + 8 * q < bandpix;
+        const half_t* cb = cpy + r16 * CP + (ok ? r : 0) * OW + (ok ? ow : 0);
+        half8 bv[TAPS];
+        if ((st + 1) * 32 <= bandpix) {  // a full step: every lane's pixels are in the band
+#pragma unroll
+          for (int t = 0; t < TAPS; ++t) bv[t] = *(const half8*)(cb + toff[t]);
+        } else {  // the band's last, partial step: zero operands past its end
+#pragma unroll
+          for (int t = 0; t < TAPS; ++t) bv[t] = ok ? *(const half8*)(cb + toff[t]) : half8{};
+        }
+#pragma unroll
+        for (int t = 0; t < TAPS; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bv[t], acc[i][t], 0, 0, 0);
         if (do_db) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             dacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], ones, dacc[i], 0, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = na[i];
+        ++cur;
         ow += 32;
         while (ow >= OW) {
           ow -= OW;
@@ -470,8 +522,7 @@ __global__ __launch_bounds__(kThreads, 2) void wgrad_tap_kernel(const half_t* __
       const int m = m0 + i * 16 + q * 4 + r;
       if (m >= cp.Mg) continue;
 #pragma unroll
-      for (int t = 0; t < kTapMaxTaps; ++t)
-        if (t < taps) pb[(int64_t)m * tg.Kq + (c0 + r16) * taps + t] = acc[i][t][r];
+      for (int t = 0; t < TAPS; ++t) pb[(int64_t)m * tg.Kq + (c0 + r16) * TAPS + t] = acc[i][t][r];
       if (do_db && r16 == 0) pb[(int64_t)m * tg.Kq + cp.K] = dacc[i][r];
     }
 }
@@ -486,13 +537,16 @@ bool tap_plan(const ConvParams& cp, int32_t dtype, int has_db, TapGeo& tg, size_
   if ((int64_t)cp.H * cp.W >= ((int64_t)1 << 31) || cp.out_sz >= ((int64_t)1 << 31)) return false;
   const int span = (cp.KH - 1) * cp.dh;
   // the largest band of output rows whose rows and copies fit the LDS budget
+  // copies: KW x 16 channel planes of R*OW + 8 halves
   const size_t per_row = (size_t)kTapCT * cp.KW * cp.OW * sizeof(half_t);
-  const int64_t rmax = (int64_t)(kTapLds / per_row);
+  const size_t skew = (size_t)kTapCT * cp.KW * 8 * sizeof(half_t);
+  if (kTapLds < kTapRingBytes + skew) return false;
+  const int64_t rmax = (int64_t)((kTapLds - kTapRingBytes - skew) / per_row);
   if (rmax < span + 1) return false;
   tg.BR = (int)std::min<int64_t>(cp.OH, rmax - span);
   tg.R = tg.BR + span;
   tg.nband = (int)cdiv(cp.OH, tg.BR);
-  tg.lds = (size_t)tg.R * per_row;
+  tg.lds = (size_t)tg.R * per_row + skew + kTapRingBytes;
   tg.nct = cp.Cg / kTapCT;
   tg.nmt = (int)cdiv(cp.Mg, 256);
   tg.has_db = has_db;
@@ -533,11 +587,26 @@ int launch_wgrad_t(const Geometry& g, const Plan& p, const void* x, const void* 
       TapGeo tg;
       size_t part_bytes = 0;
       if (!tap_plan(cp, g.dtype, db != nullptr, tg, &part_bytes)) return FUSEDCONV_ERR_ROUTE;
-      if (set_max_dynamic_lds((const void*)wgrad_tap_kernel, (int)kTapLds) != FUSEDCONV_OK)
-        return FUSEDCONV_ERR_LAUNCH;
       float* part = (float*)ws;
-      int rc = launch_conv(wgrad_tap_kernel, dim3((unsigned)tg.blocks), dim3(kThreads), tg.lds, a,
-                           kEdgeNone, (const half_t*)x, (const half_t*)dy, part, cp, tg);
+      int rc = FUSEDCONV_ERR_ROUTE;
+      auto go = [&](auto kfn) -> int {
+        if (set_max_dynamic_lds((const void*)kfn, (int)kTapLds) != FUSEDCONV_OK)
+          return FUSEDCONV_ERR_LAUNCH;
+        return launch_conv(kfn, dim3((unsigned)tg.blocks), dim3(kThreads), tg.lds, a, kEdgeNone,
+                           (const half_t*)x, (const half_t*)dy, part, cp, tg);
+      };
+      switch (cp.KH * cp.KW) {
+        case 1: rc = go(wgrad_tap_kernel<1>); break;
+        case 2: rc = go(wgrad_tap_kernel<2>); break;
+        case 3: rc = go(wgrad_tap_kernel<3>); break;
+        case 4: rc = go(wgrad_tap_kernel<4>); break;
+        case 5: rc = go(wgrad_tap_kernel<5>); break;
+        case 6: rc = go(wgrad_tap_kernel<6>); break;
+        case 7: rc = go(wgrad_tap_kernel<7>); break;
+        case 8: rc = go(wgrad_tap_kernel<8>); break;
+        case 9: rc = go(wgrad_tap_kernel<9>); break;
+        default: break;
+      }
       if (rc != FUSEDCONV_OK) return rc;
       WgGeo wg{};
       wg.Kq = tg.Kq;
