@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 
 SOURCES = ["resolver.cpp", "planner.cpp", "capi.cpp", "kernels_direct.hip", "kernels_igemm.hip",
            "kernels_transposed.hip", "kernels_im2col.hip", "noalloc.hip", "backward.cpp",
-           "kernels_backward.hip"]
+           "kernels_backward.hip", "kernels_halo32.hip"]
 # Kernels specialised per activation: compiled once per activation id
 # (-DFC_ACT=k, k = 0 .. ACT_COUNT-1); unit 0 also holds the route entry points.
 ACT_SOURCES = ["kernels_depthwise.hip", "kernels_dwmfma.hip", "kernels_halo.hip",

@@ -116,6 +116,7 @@ int fusedconv_create_backward_data(const fusedconv_desc* d, fusedconv_handle** o
       size_t ws = 0;
       if (d->split_k > 1) r = FUSEDCONV_ROUTE_IGEMM;
       else if (igemm_halo_fits(cp, g.dtype, th, tw, ws)) r = FUSEDCONV_ROUTE_IGEMM_HALO;
+      else if (halo32_fits(cp, g.dtype, nullptr, nullptr, nullptr)) r = FUSEDCONV_ROUTE_IGEMM_HALO;
       else if (cp.K >= 8 && cp.Mg >= 8) r = FUSEDCONV_ROUTE_IGEMM;
       else r = FUSEDCONV_ROUTE_DIRECT;
     }

@@ -772,13 +772,15 @@ bool igemm_halo_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32
   return true;
 }
 
-int prepare_igemm_halo(const Geometry& g, const Plan&, const RunArgs& a) {
+int prepare_igemm_halo(const Geometry& g, const Plan& p, const RunArgs& a) {
+  if (g.dtype == FUSEDCONV_F32) return prepare_halo32(g, p, a);
   Choice ch;
   if (!choose(g.cp, ch)) return FUSEDCONV_ERR_ROUTE;
   return launch_repack(g.cp, ch, a);
 }
 
-int launch_igemm_halo(const Geometry& g, const Plan&, const RunArgs& a) {
+int launch_igemm_halo(const Geometry& g, const Plan& p, const RunArgs& a) {
+  if (g.dtype == FUSEDCONV_F32) return launch_halo32(g, p, a);  // kernels_halo32.hip
   static const ActLaunchFn table[ACT_COUNT] = FC_ACT_TABLE(launch_halo_act_);
   // the backward-data epilogue lives in the activation-free instance
   return table[g.cp.bwd ? ACT_NONE : g.cp.act](g, a);

@@ -1,0 +1,464 @@
+// Implicit GEMM on the fp32 matrix cores with channel-last halo boxes (fp32
+// in, fp32 accumulate, true fp32 products: v_mfma_f32_16x16x4_f32).
+//
+// The fp16 halo kernel's structure (kernels_halo.hip), re-cut for fp32:
+//   * per block of 16 input channels, the input box that a tile's windows
+//     cover (zero outside the image) is copied once into LDS, channel-last
+//     [position][16 channels + 4 pad], positions split by stride phase, so
+//     for tap t every output pixel's 16-channel row is the LDS row at
+//     pixel(p) + offset(t);
+//   * a lane's operand is 4 consecutive channels of one pixel (one
+//     ds_read_b128), fed to four MFMAs: MFMA e contracts channel 4q + e of
+//     lane group q, for A (the pixels) and B (the weights) alike, so every
+//     channel is summed once;
+//   * the weights, repacked tap-major as Wp[g][tap][channel block][m][16]
+//     (fusedconv_prepare_weights or at the start of every run), go straight
+//     into registers one (channel block, tap) step ahead;
+//   * bias seeds the accumulators; Z, the activation and the store follow
+//     per lane: 4 consecutive pixels of one output channel, one 16-byte
+//     store where the row allows.
+// The per-element im2col gather of the IGEMM route, whose loads wait at the
+// joins of their bounds tests, is gone: X is read once per channel block as
+// whole 16-byte rows of the box.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "epilogue.h"
+#include "internal.h"
+#include "launch.h"
+#include "sync.h"
+
+namespace fc {
+namespace {
+
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kCB = 16;         // input channels per box
+constexpr int kLdc = 20;        // floats per LDS box row (80 bytes: 16 channels + 4 pad)
+constexpr size_t kMaxLds = 64 * 1024;  // two boxes; two blocks per CU
+constexpr int kMaxTaps = 64;
+
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int log2i(int v) { return 31 - __builtin_clz((unsigned)v); }
+
+struct Geo32 {
+  int TD, TH, TW, ltw, lth;  // output tile (TW a power of two >= 16)
+  int BD, BH, BW;            // input box extents
+  int ND, NH, NW;            // positions per stride phase
+  int LH, LW;                // LDS pitches in positions
+  int box_pos;               // positions per box
+  int tiles_d, tiles_h, tiles_w;
+  int ntile;
+  int nmb, ncb, mgp;         // m blocks, channel blocks, Wp rows per (tap, block)
+  int vec;                   // W % 4 == 0: 16-byte row loads
+  int tap_off[kMaxTaps];     // LDS row offset (positions) of each tap
+};
+
+__device__ __forceinline__ int phase_index(int a, int s, int n) {
+  if (s == 1) return a;
+  return (a % s) * n + a / s;
+}
+
+// Wp[((g*taps + t)*ncb + cb)*mgp + m][c'] = W[g*Mg + m][cb*16 + c'][t]; zero
+// past C/group and for rows m >= M/group.
+__global__ __launch_bounds__(kThreads) void repack32_kernel(const float* __restrict__ w,
+                                                            float* __restrict__ wp, ConvParams cp,
+                                                            int ncb, int mgp) {
+  const int cpad = ncb * kCB;
+  const int total = cp.G * mgp * cpad;
+  for (int i = blockIdx.x * kThreads + threadIdx.x; i < total; i += gridDim.x * kThreads) {
+    const int c = i % cpad;
+    const int r = i / cpad;
+    const int m = r % mgp;
+    const int g = r / mgp;
+    const bool ok = c < cp.Cg && m < cp.Mg;
+    const float* src = w + ((int64_t)(g * cp.Mg + (ok ? m : 0)) * cp.Cg + (ok ? c : 0)) * cp.taps;
+    float* dst = wp + (((int64_t)g * cp.taps * ncb + c / kCB) * mgp + m) * kCB + c % kCB;
+    for (int t = 0; t < cp.taps; ++t) dst[(int64_t)t * ncb * mgp * kCB] = ok ? src[t] : 0.0f;
+  }
+}
+
+// Block tile: WGP x WGM waves, each 64 pixels x 64 output channels (4 x 4
+// MFMA tiles of 16 x 16); BN = 64*WGP pixels, BM = 64*WGM channels.
+template <int WGP>
+__global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __restrict__ x,
+                                                             const float* __restrict__ wp,
+                                                             const float* __restrict__ bias,
+                                                             const float* z, const float* pre,
+                                                             float* y, ConvParams cp, Geo32 hg) {
+  constexpr int WGM = 4 / WGP;
+  constexpr int BN = 64 * WGP, BM = 64 * WGM;
+  extern __shared__ __attribute__((aligned(16))) float lds32[];
+  const int box = hg.box_pos * kLdc;  // floats per box
+
+  // ---- block -> (group, m block, tile)
+  const int per_g = hg.ntile * hg.nmb;
+  const int g = blockIdx.x / per_g;
+  int rb = blockIdx.x - g * per_g;
+  const int mb = rb % hg.nmb;
+  int tile = rb / hg.nmb;
+  const int tw_i = tile % hg.tiles_w;
+  tile /= hg.tiles_w;
+  const int th_i = tile % hg.tiles_h;
+  tile /= hg.tiles_h;
+  const int td_i = tile % hg.tiles_d;
+  const int64_t n = tile / hg.tiles_d;
+  const int od0 = td_i * hg.TD, oh0 = th_i * hg.TH, ow0 = tw_i * hg.TW;
+  const int bd0 = od0 * cp.sd - cp.pd, bh0 = oh0 * cp.sh - cp.ph, bw0 = ow0 * cp.sw - cp.pw;
+  const int m0 = mb * BM;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wpi = wave % WGP, wmi = wave / WGP;
+  const int r16 = lane & 15, q = lane >> 4;
+
+  // ---- zero both boxes: positions outside the image stay zero
+  for (int i = tid; i < 2 * box / 4; i += kThreads) ((float4v*)lds32)[i] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  // ---- box loader: item = (channel quad cq, in-image box row, 4-column
+  // group): four 16-byte loads (4 channels, same 4 columns), written as up
+  // to 4 LDS rows of 4 channels
+  const int d_lo = max(bd0, 0), d_hi = min(bd0 + hg.BD, cp.D);
+  const int h_lo = max(bh0, 0), h_hi = min(bh0 + hg.BH, cp.H);
+  const int w_lo = max(bw0, 0), w_hi = min(bw0 + hg.BW, cp.W);
+  const int g_lo = w_lo >> 2, g_hi = (w_hi + 3) >> 2;
+  const int nd = max(d_hi - d_lo, 0), nh = max(h_hi - h_lo, 0), ngr = max(g_hi - g_lo, 0);
+  const int nitems = 4 * nd * nh * ngr;
+  const float* ximg = x + (n * cp.C + (int64_t)g * cp.Cg) * cp.in_sz;
+  constexpr int PF = 2;  // items per thread held across a channel block
+  struct Item { int goff, ldst, cq, mask, aw0; };
+  auto decode = [&](int i) __attribute__((always_inline)) {
+    Item it;
+    it.cq = i & 3;
+    int r = i >> 2;
+    const int gi = r % ngr;
+    r /= ngr;
+    const int hh = r % nh;
+    const int dd = r / nh;
+    const int id = d_lo + dd, ih = h_lo + hh, iw = (g_lo + gi) * 4;
+    int mask = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (iw + e >= w_lo && iw + e < w_hi) mask |= 1 << e;
+    it.mask = mask;
+    it.goff = (id * cp.H + ih) * cp.W + iw;
+    it.ldst = (phase_index(id - bd0, cp.sd, hg.ND) * hg.LH + phase_index(ih - bh0, cp.sh, hg.NH)) * hg.LW;
+    it.aw0 = iw - bw0;
+    return it;
+  };
+  Item items[PF];
+  float4v xr[PF][4];
+  auto load_item = [&](const Item& it, int cb, float4v* v) __attribute__((always_inline)) {
+    const int c0 = cb * kCB + it.cq * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = it.mask != 0 && c0 + j < cp.Cg;
+      const float* s = ok ? ximg + (int64_t)(c0 + j) * cp.in_sz + it.goff : x;
+      if (hg.vec) {
+        v[j] = *(const float4v*)s;
+      } else {
+        float4v t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (ok && ((it.mask >> e) & 1)) t[e] = s[e];
+        v[j] = t;
+      }
+    }
+  };
+  auto store_item = [&](const Item& it, int cb, float* xs, const float4v* v) __attribute__((always_inline)) {
+    if (it.mask == 0) return;
+    const int cvalid = cp.Cg - cb * kCB - it.cq * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (!((it.mask >> e) & 1)) continue;
+      const int col = phase_index(it.aw0 + e, cp.sw, hg.NW);
+      float4v u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) u[j] = j < cvalid ? v[j][e] : 0.0f;
+      *(float4v*)(xs + (it.ldst + col) * kLdc + it.cq * 4) = u;
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < PF; ++k) {
+    const int i = tid + k * kThreads;
+    items[k].mask = 0;
+    items[k].goff = items[k].ldst = items[k].cq = items[k].aw0 = 0;
+    if (i < nitems) items[k] = decode(i);
+  }
+  auto prefetch_box = [&](int cb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < PF; ++k) load_item(items[k], cb, xr[k]);
+  };
+  auto store_box = [&](int buf, int cb) __attribute__((always_inline)) {
+    float* xs = lds32 + buf * box;
+#pragma unroll
+    for (int k = 0; k < PF; ++k) store_item(items[k], cb, xs, xr[k]);
+    for (int i0 = PF * kThreads; i0 < nitems; i0 += kThreads) {  // items beyond the held ones
+      const int i = i0 + tid;
+      Item it;
+      it.mask = 0;
+      it.goff = it.ldst = it.cq = it.aw0 = 0;
+      if (i < nitems) it = decode(i);
+      float4v v[4];
+      load_item(it, cb, v);
+      store_item(it, cb, xs, v);
+    }
+  };
+
+  // ---- weights: fragment j of step (cb, t) = 16 rows (channels m) x 16
+  // floats; lane (r16, q) reads the 4 floats of channels 4q .. 4q+3
+  const float* wg = wp + (int64_t)g * cp.taps * hg.ncb * hg.mgp * kCB;
+  const int wl = (m0 + wmi * 64 + r16) * kCB + q * 4;
+  const int64_t wstep = (int64_t)hg.mgp * kCB;
+
+  // ---- LDS row (positions) of this lane's pixel in pixel tile i
+  int apos[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pu = wpi * 64 + i * 16;  // 16 consecutive pixels of one tile row
+    const int tw = pu & (hg.TW - 1), th = (pu >> hg.ltw) & (hg.TH - 1), td = pu >> (hg.ltw + hg.lth);
+    apos[i] = (td * hg.LH + th) * hg.LW + tw + r16;
+  }
+
+  // ---- accumulators start at the bias (lane column r16 = channel m0 + wmi*64 + 16j + r16)
+  float4v acc[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wmi * 64 + j * 16 + r16;
+    const float bv = (cp.has_bias && m < cp.Mg) ? bias[g * cp.Mg + m] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i][j] = float4v{bv, bv, bv, bv};
+  }
+
+  lds_barrier();  // zero fill done
+  prefetch_box(0);
+  store_box(0, 0);
+  if (hg.ncb > 1) prefetch_box(1);
+  float4v wa[4], wb[4];
+  auto load_w = [&](int64_t off, float4v* v) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = *(const float4v*)(wg + off + wl + j * 16 * kCB);
+  };
+  load_w(0, wa);
+  lds_barrier();
+
+  const int taps = cp.taps, ncb = hg.ncb, nsteps = ncb * taps;
+  // step s = (cb, t) reads Wp tile t*ncb + cb
+  auto woff = [&](int s) __attribute__((always_inline)) {
+    const int cb = s / taps, t = s - cb * taps;
+    return ((int64_t)t * ncb + cb) * wstep;
+  };
+  auto step = [&](int s, const float4v* wc, float4v* wn) __attribute__((always_inline)) {
+    const int cb = s / taps, t = s - cb * taps;
+    // the next step's weights (past the last step: the first tile again)
+    load_w(s + 1 < nsteps ? woff(s + 1) : 0, wn);
+    __builtin_amdgcn_sched_barrier(0);
+    const float* xb = lds32 + (cb & 1) * box + hg.tap_off[t] * kLdc + q * 4;
+    float4v a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *(const float4v*)(xb + apos[i] * kLdc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][e], wc[j][e], acc[i][j], 0, 0, 0);
+    if (t + 1 == taps && cb + 1 < ncb) {
+      // the next channel block's box (held in registers) into the other
+      // buffer: its previous readers (channel block cb - 1) all passed the
+      // last barrier
+      store_box((cb + 1) & 1, cb + 1);
+      lds_barrier();
+      if (cb + 2 < ncb) prefetch_box(cb + 2);
+    }
+  };
+  int s = 0;
+  for (; s + 2 <= nsteps; s += 2) {
+    step(s, wa, wb);
+    step(s + 1, wb, wa);
+  }
+  if (s < nsteps) step(s, wa, wb);
+
+  // wait states between the last products and the VALU reads of their
+  // accumulators
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- epilogue: lane holds pixels 4q .. 4q+3 of pixel tile i (consecutive
+  // columns of one tile row) for channel m0 + wmi*64 + 16j + r16
+  const bool vec_y = (cp.OW & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pu = wpi * 64 + i * 16 + q * 4;
+    const int tw = pu & (hg.TW - 1), th = (pu >> hg.ltw) & (hg.TH - 1), td = pu >> (hg.ltw + hg.lth);
+    const int od = od0 + td, oh = oh0 + th, ow = ow0 + tw;
+    if (od >= cp.OD || oh >= cp.OH || ow >= cp.OW) continue;
+    const int nv = min(4, cp.OW - ow);
+    const int64_t pix = ((int64_t)od * cp.OH + oh) * cp.OW + ow;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wmi * 64 + j * 16 + r16;
+      if (m >= cp.Mg) continue;
+      const int64_t yi = (n * cp.M + (int64_t)g * cp.Mg + m) * cp.out_sz + pix;
+      float4v v = acc[i][j];
+      if (vec_y && nv == 4) {
+        if (cp.has_z) v += *(const float4v*)(z + yi);
+        if (cp.bwd) {
+          if (cp.act != ACT_NONE) {
+            const float4v pv = *(const float4v*)(pre + yi);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] *= dact_apply(cp.act, pv[e], cp.alpha, cp.beta);
+          }
+        } else {
+          v = act_apply4(cp.act, v, cp.alpha, cp.beta);
+        }
+        *(float4v*)(y + yi) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (e >= nv) continue;
+          float u = v[e];
+          if (cp.has_z) u += z[yi + e];
+          if (cp.bwd) {
+            if (cp.act != ACT_NONE) u *= dact_apply(cp.act, pre[yi + e], cp.alpha, cp.beta);
+          } else {
+            u = act_apply(cp.act, u, cp.alpha, cp.beta);
+          }
+          y[yi + e] = u;
+        }
+      }
+    }
+  }
+}
+
+// Tile choice: WGP = 4 (256 pixels x 64 channels) when M/group <= 64, else
+// WGP = 2 (128 x 128); tile widths 16 .. 256 in order of padded output
+// area; the first whose two boxes fit is taken.
+bool choose32_wgp(const ConvParams& cp, int wgp, Geo32& hg);
+
+bool choose32(const ConvParams& cp, int& wgp, Geo32& hg) {
+  if (cp.taps > kMaxTaps || cp.transposed) return false;
+  wgp = cp.Mg <= 64 ? 4 : 2;
+  if (choose32_wgp(cp, wgp, hg)) return true;
+  if (wgp == 4 && choose32_wgp(cp, 2, hg)) {  // smaller pixel tiles for small images
+    wgp = 2;
+    return true;
+  }
+  return false;
+}
+
+bool choose32_wgp(const ConvParams& cp, int wgp, Geo32& hg) {
+  const int bn = 64 * wgp, bm = 64 * (4 / wgp);
+  int order[5], no = 0;
+  double waste[5];
+  for (int w : {16, 32, 64, 128, 256}) {
+    if (w > bn) break;
+    const int th = bn / w;
+    if (th > 1 && cp.OH == 1 && cp.OD == 1) continue;  // 1-D: one row per tile
+    waste[no] = (double)cdiv(cp.OH, th) * th * cdiv(cp.OW, w) * w / ((double)cp.OH * cp.OW);
+    order[no++] = w;
+  }
+  for (int a = 0; a < no; ++a)
+    for (int b = a + 1; b < no; ++b)
+      if (waste[b] < waste[a] - 1e-9 || (waste[b] < waste[a] + 1e-9 && order[b] > order[a])) {
+        std::swap(waste[a], waste[b]);
+        std::swap(order[a], order[b]);
+      }
+  for (int oi = 0; oi < no; ++oi) {
+    const int tw = order[oi], th = bn / tw, td = 1;
+    Geo32 h{};
+    h.TD = td; h.TH = th; h.TW = tw;
+    h.ltw = log2i(tw);
+    h.lth = log2i(th);
+    h.BD = (td - 1) * cp.sd + (cp.KD - 1) * cp.dd + 1;
+    h.BH = (th - 1) * cp.sh + (cp.KH - 1) * cp.dh + 1;
+    h.BW = (tw - 1) * cp.sw + (cp.KW - 1) * cp.dw + 1;
+    h.ND = (int)cdiv(h.BD, cp.sd);
+    h.NH = (int)cdiv(h.BH, cp.sh);
+    h.NW = (int)cdiv(h.BW, cp.sw);
+    h.LH = cp.sh * h.NH;
+    h.LW = cp.sw * h.NW;
+    const int64_t bpos = (int64_t)cp.sd * h.ND * h.LH * h.LW;
+    if ((size_t)2 * bpos * kLdc * sizeof(float) > kMaxLds) continue;
+    if ((double)cdiv(cp.OD, td) * td * cdiv(cp.OH, th) * th * cdiv(cp.OW, tw) * tw > 2.0 * cp.out_sz)
+      continue;
+    h.box_pos = (int)bpos;
+    h.tiles_d = (int)cdiv(cp.OD, td);
+    h.tiles_h = (int)cdiv(cp.OH, th);
+    h.tiles_w = (int)cdiv(cp.OW, tw);
+    const int64_t ntile = cp.n * h.tiles_d * h.tiles_h * h.tiles_w;
+    h.nmb = (int)cdiv(cp.Mg, bm);
+    h.ncb = (int)cdiv(cp.Cg, kCB);
+    h.mgp = h.nmb * bm;
+    if (ntile * h.nmb * cp.G >= ((int64_t)1 << 31)) continue;
+    if ((int64_t)cp.G * cp.taps * h.ncb * h.mgp * kCB >= ((int64_t)1 << 31)) continue;
+    if (cp.in_sz >= ((int64_t)1 << 31)) continue;
+    h.ntile = (int)ntile;
+    h.vec = cp.W % 4 == 0;
+    for (int t = 0; t < cp.taps; ++t) {
+      const int kw = t % cp.KW, kh = (t / cp.KW) % cp.KH, kd = t / (cp.KW * cp.KH);
+      const int ad = kd * cp.dd, ah = kh * cp.dh, aw = kw * cp.dw;
+      h.tap_off[t] = (((ad % cp.sd) * h.ND + ad / cp.sd) * h.LH + (ah % cp.sh) * h.NH + ah / cp.sh) * h.LW +
+                     (aw % cp.sw) * h.NW + aw / cp.sw;
+    }
+    hg = h;
+    return true;
+  }
+  return false;
+}
+
+int launch_repack32(const ConvParams& cp, const Geo32& hg, const RunArgs& a) {
+  const int64_t total = (int64_t)cp.G * hg.mgp * hg.ncb * kCB;
+  int64_t blocks = (total + kThreads - 1) / kThreads;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(repack32_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                     (hipStream_t)a.stream, (const float*)a.w, (float*)a.ws, cp, hg.ncb, hg.mgp);
+  return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+bool halo32_fits(const ConvParams& cp, int32_t dtype, size_t* workspace, int32_t* tile_h,
+                 int32_t* tile_w) {
+  if (dtype != FUSEDCONV_F32) return false;
+  int wgp = 0;
+  Geo32 hg;
+  if (!choose32(cp, wgp, hg)) return false;
+  if (workspace) *workspace = (size_t)cp.G * cp.taps * hg.ncb * hg.mgp * kCB * sizeof(float);
+  if (tile_h) *tile_h = hg.TH;
+  if (tile_w) *tile_w = hg.TW;
+  return true;
+}
+
+int prepare_halo32(const Geometry& g, const Plan&, const RunArgs& a) {
+  int wgp = 0;
+  Geo32 hg;
+  if (!choose32(g.cp, wgp, hg)) return FUSEDCONV_ERR_ROUTE;
+  return launch_repack32(g.cp, hg, a);
+}
+
+int launch_halo32(const Geometry& g, const Plan&, const RunArgs& a) {
+  const ConvParams& cp = g.cp;
+  int wgp = 0;
+  Geo32 hg;
+  if (!choose32(cp, wgp, hg)) return FUSEDCONV_ERR_ROUTE;
+  if (!(a.flags & FUSEDCONV_RUN_WEIGHTS_PREPARED)) {
+    const int rc = launch_repack32(cp, hg, a);
+    if (rc != FUSEDCONV_OK) return rc;
+  }
+  const unsigned blocks = (unsigned)((int64_t)hg.ntile * hg.nmb * cp.G);
+  const size_t lds = (size_t)2 * hg.box_pos * kLdc * sizeof(float);
+  auto go = [&](auto kfn) -> int {
+    if (set_max_dynamic_lds((const void*)kfn, (int)kMaxLds) != FUSEDCONV_OK) return FUSEDCONV_ERR_LAUNCH;
+    return launch_conv(kfn, dim3(blocks), dim3(kThreads), lds, a, kEdgeBoth, (const float*)a.x,
+                       (const float*)a.ws, (const float*)a.bias, (const float*)a.z,
+                       (const float*)a.pre, (float*)a.y, cp, hg);
+  };
+  return wgp == 4 ? go(halo32_kernel<4>) : go(halo32_kernel<2>);
+}
+
+}  // namespace fc

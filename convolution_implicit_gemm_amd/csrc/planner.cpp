@@ -133,6 +133,8 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
     // par)
     else if (pointwise_fits(cp, g.dtype)) route = FUSEDCONV_ROUTE_POINTWISE;
     else if (igemm_halo_fits(cp, g.dtype, th, tw, halo_ws)) route = FUSEDCONV_ROUTE_IGEMM_HALO;
+    // fp32: the channel-last halo kernel on the fp32 matrix cores
+    else if (halo32_fits(cp, g.dtype, nullptr, nullptr, nullptr)) route = FUSEDCONV_ROUTE_IGEMM_HALO;
     else if (smallc_fits(cp, g.dtype, th, tw, halo_ws)) route = FUSEDCONV_ROUTE_SMALLC;
     // larger non-overlapping patches (stride = kernel): explicit im2col, whose
     // column matrix is then a permutation of X (the manifest's
@@ -169,6 +171,19 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
       }
       return FUSEDCONV_OK;
     case FUSEDCONV_ROUTE_IGEMM_HALO:
+      if (g.dtype == FUSEDCONV_F32) {
+        if (!halo32_fits(cp, g.dtype, &halo_ws, &th, &tw)) {
+          err = "IGEMM_HALO (fp32) needs at most 64 taps and two input boxes of a 128- or "
+                "256-pixel tile within 64 KB of LDS";
+          return FUSEDCONV_ERR_ROUTE;
+        }
+        p.route = route;
+        p.tile_h = th;
+        p.tile_w = tw;
+        p.workspace = halo_ws;
+        snprintf(p.name, sizeof(p.name), "igemm_halo_f32_t%dx%d", th, tw);
+        return FUSEDCONV_OK;
+      }
       if (!igemm_halo_fits(cp, g.dtype, th, tw, halo_ws, &bm)) {
         err = "IGEMM_HALO needs fp16, C/group >= 32, at most 64 taps and a halo box that fits "
               "in LDS";

@@ -584,25 +584,60 @@ def test_im2col_route(ci):
         check(got, ref, "f16", f"im2col case {ci}")
 
 
+HALO32_CASES = [
+    # (x, w, attrs) for the fp32 halo kernel (stride 1: strided boxes exceed
+    # its LDS budget): 1-D grouped and dilated, 2-D with asymmetric pads, 3-D,
+    # channel tails (C/group not a multiple of 16), M/group above 64
+    # (128-channel blocks) with a tail, W not a multiple of 4 (element
+    # loads), OW not a multiple of 4 (element stores)
+    ([2, 48, 300], [48, 16, 9], dict(group=3, dilations=[3], auto_pad="SAME_LOWER")),
+    ([2, 20, 31, 33], [40, 20, 3, 3], dict(pads=[1, 1, 1, 1])),
+    ([1, 32, 24, 40], [72, 32, 3, 3], dict(pads=[1, 2, 1, 0])),
+    ([1, 16, 4, 16, 16], [24, 16, 1, 3, 3], dict(pads=[0, 1, 1, 0, 1, 1])),
+    ([2, 24, 16, 64], [150, 24, 1, 5], dict(pads=[0, 2, 0, 2])),
+    ([3, 8, 19, 21], [12, 4, 3, 2], dict(group=2, dilations=[2, 1])),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(HALO32_CASES)))
+def test_halo32_route(ci):
+    xs, ws, attrs = HALO32_CASES[ci]
+    h = B.Handle("f32", xs, ws, None, None, route="igemm_halo", **attrs)
+    assert h.kernel_name.startswith("igemm_halo_f32"), h.kernel_name
+    for k, (bias, resid) in enumerate([(True, True), (False, False), (True, False)]):
+        act, params = ACTS[(7 * ci + 5 * k) % len(ACTS)]
+        x, w, b, z = random_tensors([9650, ci, k], "f32", xs, ws, [ws[0]] if bias else None,
+                                    h.y_shape if resid else None, dist="uniform")
+        a = dict(attrs, activation=act, activation_params=f32params(params))
+        log(f"CASE halo32 {ci} x={xs} w={ws} {a} bias={bias} z={resid}")
+        got = run_gpu(x, w, b, z, route="igemm_halo", **a)
+        ref = oracle.fusedconv(x, w, b, z, **a)
+        check(got, ref, "f32", f"halo32 case {ci}")
+
+
 @pytest.mark.parametrize("route", ["igemm_halo", "igemm", "depthwise", "smallc", "pointwise",
-                                   "pointwise_patch2x2", "im2col", "im2col_oddk"])
+                                   "pointwise_patch2x2", "im2col", "im2col_oddk", "halo32"])
 def test_prepared_weights_match_plain_run(route):
     patch = route == "pointwise_patch2x2"
     oddk = route == "im2col_oddk"   # K 27: W padded to 32 columns in the workspace
-    route = "pointwise" if patch else ("im2col" if oddk else route)
+    f32 = route == "halo32"         # the fp32 halo kernel's repacked weights
+    dt = "f32" if f32 else "f16"
+    route = "pointwise" if patch else ("im2col" if oddk else ("igemm_halo" if f32 else route))
     C = {"depthwise": 16, "smallc": 3}.get(route, 3 if oddk else 64)
     M, grp = (C, C) if route == "depthwise" else (96, 1)
     k = 2 if patch else (1 if route == "pointwise" else 3)
     xs, ws = [2, C, 16, 16], [M, C // grp, k, k]
-    x, w, b, z = random_tensors([8100], "f16", xs, ws, [M], None, dist="normal", w_std=0.05)
+    x, w, b, z = random_tensors([8100], dt, xs, ws, [M], None, dist="normal", w_std=0.05)
     attrs = dict(group=grp, pads=[1, 1, 1, 1] if k == 3 else [0, 0, 0, 0], activation="Relu",
                  route=route)
     if patch:
         attrs["strides"] = [2, 2]
-    op = fc.FusedConv(xs, ws, "f16", True, False, **attrs)
+    op = fc.FusedConv(xs, ws, dt, True, False, **attrs)
     xd, wd, bd = dev(x), dev(w), dev(b)
     ws_t = torch.empty(max(op.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
     log(f"CASE prepared route={route} patch={patch} {op.handle.kernel_name}")
+    if f32:
+        assert op.handle.kernel_name.startswith("igemm_halo_f32"), op.handle.kernel_name
     if patch:
         assert op.handle.kernel_name.startswith("pointwise_f16_patch2x2"), op.handle.kernel_name
     y1 = op(xd, wd, bd, workspace=ws_t)
@@ -613,7 +648,7 @@ def test_prepared_weights_match_plain_run(route):
     assert torch.equal(y1, y2)
     assert torch.equal(y2, y3)
     ref = oracle.fusedconv(x, w, b, None, **{k_: v for k_, v in attrs.items() if k_ != "route"})
-    check(y1.cpu().numpy(), ref, "f16", f"prepared {route}")
+    check(y1.cpu().numpy(), ref, dt, f"prepared {route}")
 
 
 @pytest.mark.parametrize("route", ["igemm_halo", "pointwise"])
