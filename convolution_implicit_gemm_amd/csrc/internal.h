@@ -145,7 +145,7 @@ bool smallc_fits(const ConvParams& cp, int32_t dtype, int32_t& tile_h, int32_t& 
 // The fp32 halo kernel (kernels_halo32.hip; route IGEMM_HALO for fp32): fits,
 // with the repacked-weight workspace and the output tile; weight repack; launch.
 bool halo32_fits(const ConvParams& cp, int32_t dtype, size_t* workspace, int32_t* tile_h,
-                 int32_t* tile_w);
+                 int32_t* tile_w, int64_t* blocks = nullptr);
 int prepare_halo32(const Geometry& g, const Plan& p, const RunArgs& a);
 int launch_halo32(const Geometry& g, const Plan& p, const RunArgs& a);
 // Pointwise route (kernels_pointwise.hip), fp16: 1x1 with stride 1, or 2x2

@@ -423,11 +423,12 @@ int launch_repack32(const ConvParams& cp, const Geo32& hg, const RunArgs& a) {
 }  // namespace
 
 bool halo32_fits(const ConvParams& cp, int32_t dtype, size_t* workspace, int32_t* tile_h,
-                 int32_t* tile_w) {
+                 int32_t* tile_w, int64_t* blocks) {
   if (dtype != FUSEDCONV_F32) return false;
   int wgp = 0;
   Geo32 hg;
   if (!choose32(cp, wgp, hg)) return false;
+  if (blocks) *blocks = (int64_t)hg.ntile * hg.nmb * cp.G;
   if (workspace) *workspace = (size_t)cp.G * cp.taps * hg.ncb * hg.mgp * kCB * sizeof(float);
   if (tile_h) *tile_h = hg.TH;
   if (tile_w) *tile_w = hg.TW;

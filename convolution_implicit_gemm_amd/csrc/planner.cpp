@@ -125,6 +125,7 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
   size_t halo_ws = 0;
   int32_t bm = 0;  // halo and pointwise routes: output channels per block
   int32_t patch = 1;  // pointwise route: 1 (1x1) or 2 (2x2 with stride 2)
+  int64_t hblocks = 0;  // fp32 halo route: its grid
   if (route == FUSEDCONV_ROUTE_AUTO) {
     if (split_req > 1) route = FUSEDCONV_ROUTE_IGEMM;
     else if (cp.Cg == 1 && depthwise_fits(cp, th, tw)) route = FUSEDCONV_ROUTE_DEPTHWISE;
@@ -133,8 +134,10 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
     // par)
     else if (pointwise_fits(cp, g.dtype)) route = FUSEDCONV_ROUTE_POINTWISE;
     else if (igemm_halo_fits(cp, g.dtype, th, tw, halo_ws)) route = FUSEDCONV_ROUTE_IGEMM_HALO;
-    // fp32: the channel-last halo kernel on the fp32 matrix cores
-    else if (halo32_fits(cp, g.dtype, nullptr, nullptr, nullptr)) route = FUSEDCONV_ROUTE_IGEMM_HALO;
+    // fp32: the channel-last halo kernel on the fp32 matrix cores, when its
+    // grid fills the chip (a starved grid takes IGEMM, which splits K)
+    else if (halo32_fits(cp, g.dtype, nullptr, nullptr, nullptr, &hblocks) && hblocks >= 512)
+      route = FUSEDCONV_ROUTE_IGEMM_HALO;
     else if (smallc_fits(cp, g.dtype, th, tw, halo_ws)) route = FUSEDCONV_ROUTE_SMALLC;
     // larger non-overlapping patches (stride = kernel): explicit im2col, whose
     // column matrix is then a permutation of X (the manifest's
