@@ -1,0 +1,248 @@
+"""CPU models of two kernels' index schemes, with bounds asserted (no GPU).
+
+Each model replays one kernel's addressing in Python -- the same tile plan,
+the same LDS layout, the same per-lane offsets -- with every LDS and buffer
+access checked against its bounds and every read checked to hit a slot that
+was written, and the result it assembles compared with the definition (the
+oracle, or the column matrix written out).  A wrong offset, a missed halo
+column or an out-of-range read fails here before any GPU run.
+
+* `im2col_staged_kernel` (kernels_im2col.hip): the chunk plan of
+  `staged_plan` (32 KB of LDS rows, the pitch W + 2*(W/64) + 2 halves,
+  element j at j + 2*(j/64)), the rows a chunk of L output pixels needs, and
+  the column-matrix pieces it writes (rows k >= K zero), against the column
+  matrix from its definition.
+* `wgrad_tap_kernel` (kernels_backward.hip): the band plan of
+  `tap_plan` (80 KB per block less the 48 KB G ring and the plane skew), the
+  KW column-shifted copies of 16 channel planes (plane pitch R*OW + 8 halves),
+  cut from the three 16-byte pieces around each copy piece, the per-tap
+  offsets and the 32-pixel step walk, against the oracle's weight gradient.
+
+The constants below are the kernels' own (kTapCT, kTapLds, kTapRingBytes and
+the 32 KB stage): a change there must change them here.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import backward as obwd
+from oracle import oracle
+
+# ---------------------------------------------------------------- im2col
+
+IM2COL_STAGE_BYTES = 32 * 1024
+
+
+def _pad3(v, d):
+    return [d] * (3 - len(v)) + list(v)
+
+
+def _im2col_geo(xs, ws, attrs):
+    nsp = len(xs) - 2
+    st = attrs.get("strides", [1] * nsp)
+    dl = attrs.get("dilations", [1] * nsp)
+    pads = attrs.get("pads", [0] * (2 * nsp))
+    out, pb = oracle.output_dims(list(xs[2:]), list(ws[2:]), st, dl, "NOTSET", pads)
+    D, H, W = _pad3(xs[2:], 1)
+    OD, OH, OW = _pad3(out, 1)
+    KD, KH, KW = _pad3(ws[2:], 1)
+    sd, sh, sw = _pad3(st, 1)
+    dd, dh, dw = _pad3(dl, 1)
+    pd, ph, pw = _pad3(pb, 0)
+    G = attrs.get("group", 1)
+    return dict(n=xs[0], C=xs[1], G=G, Cg=xs[1] // G, D=D, H=H, W=W, OD=OD, OH=OH, OW=OW,
+                KD=KD, KH=KH, KW=KW, sd=sd, sh=sh, sw=sw, dd=dd, dh=dh, dw=dw, pd=pd, ph=ph, pw=pw)
+
+
+def _staged_plan(cp, Pp):
+    pitch = cp["W"] + 2 * (cp["W"] >> 6) + 2
+    rows = IM2COL_STAGE_BYTES // (pitch * 2)
+    if rows < 2:
+        return None
+    lmax = (rows - 2) * cp["OW"] + 1
+    L = min(lmax // 8 * 8, 4096, Pp)
+    if L < 8:
+        return None
+    rows = min(rows, (L - 1) // cp["OW"] + 2)
+    return dict(L=L, nchunk=-(-Pp // L), rows=rows, pitch=pitch)
+
+
+IM2COL_CASES = [
+    ([2, 3, 64, 64], [96, 3, 4, 4], dict(strides=[4, 4])),
+    ([1, 3, 224, 224], [64, 3, 16, 16], dict(strides=[16, 16])),
+    ([1, 8, 28, 28], [32, 8, 14, 14], dict(strides=[14, 14])),
+    ([1, 12, 32, 32], [64, 12, 3, 3], dict(pads=[1, 1, 1, 1])),
+    ([2, 3, 20, 20], [16, 3, 3, 3], dict(pads=[1, 1, 1, 1])),
+    ([1, 32, 8, 8], [64, 8, 3, 3], dict(group=4, pads=[1, 1, 1, 1])),
+    ([1, 8, 8, 16, 16], [32, 8, 2, 4, 4], dict(strides=[2, 4, 4])),
+    ([3, 4, 96], [16, 4, 5], dict(strides=[2], pads=[2, 2])),
+    ([1, 3, 20, 20], [16, 3, 5, 5], dict(dilations=[2, 2])),
+    ([1, 16, 30, 30], [24, 16, 5, 5], dict(strides=[5, 5])),
+    ([1, 1, 40, 1100], [8, 1, 3, 3], dict(pads=[1, 1, 1, 1])),      # wide rows: several chunks
+    ([1, 1, 9, 5000], [8, 1, 2, 3], dict(strides=[1, 2], pads=[0, 1, 0, 1])),
+    ([1, 2, 4, 20, 30], [8, 2, 3, 3, 3], dict(pads=[1, 1, 1, 1, 1, 1], strides=[1, 2, 2])),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(IM2COL_CASES)))
+def test_im2col_staged_index_model(ci):
+    xs, ws, attrs = IM2COL_CASES[ci]
+    cp = _im2col_geo(xs, ws, attrs)
+    K = cp["Cg"] * cp["KD"] * cp["KH"] * cp["KW"]
+    Kp = max(16, -(-K // 8) * 8)
+    P = cp["OD"] * cp["OH"] * cp["OW"]
+    Pp = -(-P // 8) * 8
+    sg = _staged_plan(cp, Pp)
+    assert sg is not None, "every case here takes the staged kernel"
+    x = np.random.default_rng([7400, ci]).standard_normal(xs)
+    x3 = x.reshape(cp["n"], cp["C"], cp["D"], cp["H"], cp["W"])
+    col = np.full((cp["n"] * cp["G"], Kp, Pp), np.nan)
+    skew = lambda j: j + 2 * (j >> 6)
+    for ng in range(cp["n"] * cp["G"]):
+        n, g = divmod(ng, cp["G"])
+        for c, kd, kh, chunk in itertools.product(range(cp["Cg"]), range(cp["KD"]), range(cp["KH"]),
+                                                  range(sg["nchunk"])):
+            P0 = chunk * sg["L"]
+            Pend = min(P0 + sg["L"], Pp)
+            Pv = min(Pend, P)
+            assert P0 < P
+            R0 = P0 // cp["OW"]
+            nrows = (Pv - 1) // cp["OW"] - R0 + 1
+            assert nrows <= sg["rows"], (nrows, sg)
+            lds = np.full(sg["rows"] * sg["pitch"], np.nan)
+            for r in range(nrows):            # the chunk's input rows, staged
+                od, oh = divmod(R0 + r, cp["OH"])
+                idd = od * cp["sd"] - cp["pd"] + kd * cp["dd"]
+                ih = oh * cp["sh"] - cp["ph"] + kh * cp["dh"]
+                ok = 0 <= idd < cp["D"] and 0 <= ih < cp["H"]
+                for j in range(cp["W"]):
+                    a = r * sg["pitch"] + skew(j)
+                    assert skew(j) < sg["pitch"] and a < lds.size
+                    lds[a] = x3[n, g * cp["Cg"] + c, idd, ih, j] if ok else 0.0
+            kbase = ((c * cp["KD"] + kd) * cp["KH"] + kh) * cp["KW"]
+            for kw in range(cp["KW"]):        # one 8-pixel piece per lane
+                for o in range((Pend - P0) // 8):
+                    p0 = P0 + 8 * o
+                    R, ow = divmod(p0, cp["OW"])
+                    v = np.zeros(8)
+                    for e in range(8):
+                        if p0 + e < Pv:
+                            iw = ow * cp["sw"] + kw * cp["dw"] - cp["pw"]
+                            if 0 <= iw < cp["W"]:
+                                a = (R - R0) * sg["pitch"] + skew(iw)
+                                assert not np.isnan(lds[a]), "read of an unstaged LDS slot"
+                                v[e] = lds[a]
+                        ow += 1
+                        if ow == cp["OW"]:
+                            ow, R = 0, R + 1
+                    assert p0 + 8 <= Pp
+                    col[ng, kbase + kw, p0:p0 + 8] = v
+        for chunk in range(sg["nchunk"]):     # rows K .. Kp-1 written as zeros
+            P0 = chunk * sg["L"]
+            col[ng, K:Kp, P0:P0 + min(sg["L"], Pp - P0)] = 0
+    assert not np.isnan(col).any(), "unwritten column-matrix entries"
+    ref = np.zeros_like(col)                  # the column matrix from its definition
+    for ng in range(cp["n"] * cp["G"]):
+        n, g = divmod(ng, cp["G"])
+        for k in range(K):
+            c, rem = divmod(k, cp["KD"] * cp["KH"] * cp["KW"])
+            kd, rem = divmod(rem, cp["KH"] * cp["KW"])
+            kh, kw = divmod(rem, cp["KW"])
+            for p in range(P):
+                R, ow = divmod(p, cp["OW"])
+                od, oh = divmod(R, cp["OH"])
+                idd = od * cp["sd"] - cp["pd"] + kd * cp["dd"]
+                ih = oh * cp["sh"] - cp["ph"] + kh * cp["dh"]
+                iw = ow * cp["sw"] - cp["pw"] + kw * cp["dw"]
+                if 0 <= idd < cp["D"] and 0 <= ih < cp["H"] and 0 <= iw < cp["W"]:
+                    ref[ng, k, p] = x3[n, g * cp["Cg"] + c, idd, ih, iw]
+    assert np.array_equal(col, ref), np.argwhere(col != ref)[:5]
+
+
+# ------------------------------------------------------------ weight taps
+
+TAP_CT = 16                      # kTapCT: input channels per block
+TAP_LDS = 80 * 1024              # kTapLds
+TAP_RING = 4 * 3 * 4 * 64 * 16   # kTapRingBytes: 4 waves x 3 steps x 4 tiles x 1 KB
+
+TAP_CASES = [
+    ([1, 16, 16, 16], [2, 16, 3, 3], (1, 1, 1, 1), (1, 1), TAP_LDS),
+    ([1, 16, 8, 64], [1, 16, 1, 3], (0, 1, 0, 1), (1, 1), TAP_LDS),
+    ([1, 16, 16, 16], [1, 16, 3, 3], (2, 2, 2, 2), (2, 2), TAP_LDS),
+    ([1, 16, 40, 48], [1, 16, 3, 3], (1, 1, 1, 1), (1, 1), TAP_RING + 16 * 1024),  # one-row bands
+    ([1, 16, 18, 16], [1, 16, 3, 3], (0, 1, 0, 1), (1, 1), TAP_LDS),
+    ([1, 16, 1, 64], [1, 16, 1, 5], (0, 2, 0, 2), (1, 1), TAP_LDS),
+    ([2, 32, 8, 24], [2, 32, 3, 3], (1, 1, 1, 1), (1, 1), TAP_LDS),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(TAP_CASES)))
+def test_wgrad_tap_index_model(ci):
+    xs, ws, pads, dil, lds_bytes = TAP_CASES[ci]
+    n, C, H, W = xs
+    M, Cg, KH, KW = ws
+    ph, pw, phe, pwe = pads
+    dh, dw = dil
+    OH = H + ph + phe - (KH - 1) * dh
+    OW = W + pw + pwe - (KW - 1) * dw
+    assert W % 8 == 0 and OW % 8 == 0 and Cg % TAP_CT == 0 and pw <= 8 and (KW - 1) * dw - pw <= 8
+    per_row = TAP_CT * KW * OW * 2
+    skew_bytes = TAP_CT * KW * 8 * 2
+    span = (KH - 1) * dh
+    rmax = (lds_bytes - TAP_RING - skew_bytes) // per_row
+    assert rmax >= span + 1
+    BR = min(OH, rmax - span)                 # output rows per band
+    R = BR + span                             # input rows a band needs
+    nband = -(-OH // BR)
+    assert R * per_row + skew_bytes + TAP_RING <= lds_bytes
+    taps = KH * KW
+    rng = np.random.default_rng([7500, ci])
+    x = rng.standard_normal(xs)
+    g = rng.standard_normal([n, M, OH, OW])
+    dwo = np.zeros([M, Cg * taps])
+    W8, OW8 = W // 8, OW // 8
+    CP = R * OW + 8                           # plane pitch (halves)
+    toff = [(t % KW) * TAP_CT * CP + (t // KW) * dh * OW for t in range(taps)]
+    for ct in range(Cg // TAP_CT):
+        c0 = ct * TAP_CT
+        for nn, band in itertools.product(range(n), range(nband)):
+            oh0 = band * BR
+            cpy = np.full(KW * TAP_CT * CP, np.nan)
+            for i in range(TAP_CT * R * OW8):    # one 8-column piece per item
+                c, r2 = divmod(i, R * OW8)
+                rr, u = divmod(r2, OW8)
+                ih = oh0 - ph + rr
+                rok = 0 <= ih < H
+                pieces = [x[nn, c0 + c, ih, 8 * pu:8 * pu + 8] if (rok and 0 <= pu < W8) else np.zeros(8)
+                          for pu in (u - 1, u, u + 1)]
+                win = np.concatenate(pieces)
+                for kw in range(KW):
+                    s = kw * dw - pw
+                    assert -8 <= s <= 8
+                    dst = c * CP + rr * OW + 8 * u + kw * TAP_CT * CP
+                    assert dst + 8 <= cpy.size
+                    cpy[dst:dst + 8] = win[8 + s:16 + s]
+            bandpix = min(BR, OH - oh0) * OW
+            for m in range(M):
+                for q in range(4):               # lane group q: pixels 8q.. of each 32-pixel step
+                    r, ow = divmod(8 * q, OW)
+                    for st in range(-(-bandpix // 32)):
+                        p = st * 32 + 8 * q
+                        if p < bandpix:
+                            a = g[nn, m].ravel()[oh0 * OW + p: oh0 * OW + p + 8]
+                            for cc in range(TAP_CT):
+                                cb = cc * CP + r * OW + ow
+                                for t in range(taps):
+                                    o = cb + toff[t]
+                                    assert o + 8 <= cpy.size
+                                    bv = cpy[o:o + 8]
+                                    assert not np.isnan(bv).any(), "read of an unwritten copy slot"
+                                    dwo[m, (c0 + cc) * taps + t] += a @ bv
+                        ow += 32
+                        while ow >= OW:
+                            ow -= OW
+                            r += 1
+    ref = obwd.conv_backward_weight(x, g, ws, pads=[ph, pw, phe, pwe], dilations=list(dil))
+    err = np.max(np.abs(dwo.reshape(ref.shape) - ref))
+    assert err < 1e-9, err
