@@ -73,7 +73,7 @@ KERNEL_SOURCES = {"halo_kernel": "kernels_halo.hip", "dw_fast_kernel": "kernels_
                   "depthwise_kernel": "kernels_depthwise.hip", "igemm_kernel": "kernels_igemm.hip",
                   "direct_kernel": "kernels_direct.hip", "smallc_kernel": "kernels_smallc.hip",
                   "dwm_kernel": "kernels_dwmfma.hip", "pw_kernel": "kernels_pointwise.hip",
-                  "im2col_kernel": "kernels_im2col.hip"}
+                  "im2col_kernel": "kernels_im2col.hip", "halo32_kernel": "kernels_halo32.hip"}
 
 
 def sources_hash(kernel_pat):
@@ -323,7 +323,8 @@ def pmc_summary(name, kernel_pat, fetch_csv, write_csv, copy_bytes):
                commands=[f"cd /tmp && timeout -s KILL 240 rocprofv3 --pmc {c} --output-format csv "
                          f"-d <out>/pmc_{name}_{c} -o run -- python3 /root/repo/bench.py "
                          f"--workload {name} --steps 3 --warmup 1 --no-per-config "
-                         f"--no-cpu-baseline --calib-copy-mb {copy_bytes >> 20}"
+                         f"--no-cpu-baseline --no-route-comparison --no-backward "
+                         f"--calib-copy-mb {copy_bytes >> 20}"
                          for c in ("FETCH_SIZE", "WRITE_SIZE")],
                note="FETCH_SIZE/WRITE_SIZE in KiB per dispatch, median over the kernel's "
                     "dispatches, times the factor that maps the copy kernel's reading to its "
