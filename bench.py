@@ -332,6 +332,46 @@ def pmc_summary(name, kernel_pat, fetch_csv, write_csv, copy_bytes):
     return rec
 
 
+def peaks():
+    """Reference rates of this GPU, for reading the roofline fractions: HBM
+    bandwidth of a plain 1 GiB device-to-device copy, and the fp16 matrix-core
+    rate a tuned library GEMM (torch.matmul, 8192^3) reaches on random U(-1, 1)
+    data and on zeros.  Measurement context only: the convolutions never call
+    the library."""
+    import torch
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    src = torch.rand(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src), 20)
+    copy_tbs = 2 * src.numel() * 4 / t / 1e12
+    del src, dst
+    n = 8192
+    out = dict(copy_1gib_tb_s=copy_tbs)
+    for tag, make in (("random", lambda: torch.rand(n, n, dtype=torch.float16, device="cuda") * 2 - 1),
+                      ("zeros", lambda: torch.zeros(n, n, dtype=torch.float16, device="cuda"))):
+        a, b = make(), make()
+        c = torch.empty(n, n, dtype=torch.float16, device="cuda")
+        t = timed(lambda: torch.matmul(a, b, out=c), 30)
+        out[f"gemm_fp16_{tag}_tflops"] = 2 * n ** 3 / t / 1e12
+        del a, b, c
+    out["published_hbm_tb_s"] = PEAK_HBM_GBS / 1e3
+    out["published_fp16_tflops"] = PEAK_TFLOPS["f16"]
+    out["device"] = torch.cuda.get_device_properties(0).gcnArchName
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -345,9 +385,14 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run a plain device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="print this GPU's copy bandwidth and library fp16 GEMM rate and exit")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("KERNEL_PATTERN", "FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from two counter runs and exit")
     args = ap.parse_args()
+    if args.peaks:
+        print(json.dumps(peaks()))
+        return
     if args.pmc_summary:
         rec = pmc_summary(args.workload, *args.pmc_summary, copy_bytes=args.calib_copy_mb << 20)
         path = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
