@@ -473,8 +473,9 @@ def main():
             per.append(ss)
         out["per_config"] = per
     if not args.no_route_comparison:
-        # the explicit im2col route against the implicit ones, same workload,
-        # same timing method (the planner's own choice is the per_config line)
+        # the other routes of a workload (explicit im2col against the implicit
+        # ones; the direct kernel for the fp32 convs), same timing method (the
+        # planner's own choice is the per_config line)
         comp = []
         for name, wl_c in WORKLOADS.items():
             for route in wl_c.get("compare_routes", []):

@@ -748,8 +748,9 @@ COMPARED = [(name, r) for name, wl in WORKLOADS.items() for r in wl.get("compare
 
 @pytest.mark.parametrize("name,route", COMPARED, ids=[f"{n}-{r}" for n, r in COMPARED])
 def test_full_size_compared_routes(name, route):
-    """Every route bench.py times a workload on (the implicit and explicit
-    im2col comparison), whole output tensor against the oracle."""
+    """Every route bench.py times a workload on (implicit against explicit
+    im2col; halo, gathered IGEMM and direct for the fp32 convs), whole output
+    tensor against the oracle."""
     wl = WORKLOADS[name]
     h = B.Handle(wl["dtype"], wl["x"], wl["w"], wl["b"], wl["z"], **wl["attrs"])
     if h.route == route:

@@ -19,8 +19,11 @@ input channels (12: a reduction of 108, not a multiple of 16; the tinygrad
 page's MatmulConv2d runs the CIFAR net's 3x3 convs as an explicit patch
 matrix times the weights), a non-overlapping 4x4 stride-4
 patch embedding and a SigLIP-style 16x16 stride-16 patch embedding (a 14x14
-patch grid).  "compare_routes" lists the routes each is timed on.  No
-dataset, image or trained weight is used.
+patch grid).  "compare_routes" lists the routes each is timed on: the
+implicit routes against the explicit im2col one, and for the fp32 1-D and
+3-D convs the channel-last halo kernel (where it fits) against the gathered
+implicit GEMM and the direct one-output-per-lane kernel.  No dataset, image
+or trained weight is used.
 
 Draw rule: numpy.random.default_rng([workload_index, sub]); tensors are
 drawn in the order X, W, B, Z in float64 (standard normal times a standard
@@ -96,12 +99,14 @@ WORKLOADS = {
         seed=[4, 0], dtype="f32", x=[16, 512, 4096], w=[512, 64, 9], b=None, z=None,
         y=[16, 512, 4096], dist="uniform", w_std=1.0,
         attrs=dict(group=8, dilations=[3], auto_pad="SAME_LOWER", activation="LeakyRelu",
-                   activation_params=[0.1])),
+                   activation_params=[0.1]),
+        compare_routes=["igemm_halo", "igemm", "direct"]),
     "conv3d_s122_f32": dict(
         seed=[4, 1], dtype="f32", x=[4, 64, 32, 64, 64], w=[128, 64, 3, 3, 3], b=[128],
         z=[4, 128, 32, 32, 32], y=[4, 128, 32, 32, 32], dist="uniform", w_std=1.0,
         attrs=dict(strides=[1, 2, 2], pads=[1, 1, 1, 1, 1, 1], activation="Clip",
-                   activation_params=[0.0, 6.0])),
+                   activation_params=[0.0, 6.0]),
+        compare_routes=["igemm", "direct"]),
     "conv_transpose_2x2s2_f16": dict(
         seed=[6, 0], dtype="f16", x=[8, 256, 96, 96], w=[256, 128, 2, 2], b=[128], z=None,
         y=[8, 128, 192, 192], dist="normal", w_std=1.0 / math.sqrt(256),
