@@ -1,4 +1,4 @@
-"""CPU models of two kernels' index schemes, with bounds asserted (no GPU).
+"""CPU models of three kernels' index schemes, with bounds asserted (no GPU).
 
 Each model replays one kernel's addressing in Python -- the same tile plan,
 the same LDS layout, the same per-lane offsets -- with every LDS and buffer
@@ -246,3 +246,162 @@ def test_wgrad_tap_index_model(ci):
     ref = obwd.conv_backward_weight(x, g, ws, pads=[ph, pw, phe, pwe], dilations=list(dil))
     err = np.max(np.abs(dwo.reshape(ref.shape) - ref))
     assert err < 1e-9, err
+
+
+# --------------------------------------------------- banded-MFMA depthwise
+
+DWM_THREADS = 256            # kThreads
+DWM_MAX_CHUNKS = 2           # kMaxChunks
+DWM_MAX_LDS = 80 * 1024      # kMaxLds
+DWM_RG = 4                   # kRG
+DWM_TROW, DWM_TBASE = 64, 24  # kTrow, kTbase
+
+DWM_CASES = [
+    # (x, w, attrs): the two depthwise workloads' planes and the GPU test shapes
+    ([1, 2, 56, 56], [2, 1, 7, 7], dict(group=2, auto_pad="SAME_UPPER")),
+    ([1, 2, 56, 56], [2, 1, 7, 7], dict(group=2, auto_pad="SAME_UPPER", dilations=[2, 2])),
+    ([1, 2, 16, 24], [4, 1, 5, 5], dict(group=2, auto_pad="SAME_LOWER")),
+    ([1, 1, 31, 40], [1, 1, 3, 3], dict(group=1, dilations=[2, 1], pads=[2, 4, 3, 6])),
+    ([1, 1, 13, 64], [1, 1, 7, 3], dict(group=1, dilations=[1, 2], pads=[3, 2, 3, 2])),
+    ([1, 1, 20, 32], [1, 1, 3, 17], dict(group=1, auto_pad="SAME_UPPER")),
+    ([1, 1, 18, 16], [1, 1, 5, 9], dict(group=1, dilations=[1, 2], auto_pad="SAME_UPPER")),
+    ([1, 1, 8, 8], [1, 1, 3, 3], dict(group=1, auto_pad="SAME_LOWER")),
+    ([1, 1, 61, 48], [1, 1, 7, 7], dict(group=1, pads=[0, 11, 0, 3])),
+    ([1, 1, 8, 16], [1, 1, 3, 3], dict(group=1, pads=[1, 1, 1, 1])),
+    ([1, 1, 100, 40], [1, 1, 5, 5], dict(group=1, auto_pad="SAME_UPPER")),   # two row groups
+]
+
+
+def _dwm_plan(cp):
+    """dwm_try: the kernel's geometry, or None where it does not fit."""
+    S = (8 - cp["pw"] % 8) % 8
+    if S + 16 + cp["dw"] * (cp["KW"] - 1) > 32:
+        return None
+    TW = -(-cp["OW"] // 16)
+    TV = -(-cp["OH"] // (16 * DWM_RG))
+    pitch = 16 * (TW - 1) + 32 + 8
+    if cp["W"] + cp["pw"] + S > pitch - 8:
+        return None
+    NR = 16 * DWM_RG * TV + cp["dh"] * (cp["KH"] - 1)
+    bufh = -(-(NR * pitch + 8 * ((NR + 3) // 4)) // 8) * 8
+    sp = 16 * TW + 8
+    stgh = 64 * TV * sp + 8 * 16 * TV
+    no = cp["OH"] * cp["OW"] // 8
+    if no > 2 * DWM_THREADS:
+        return None
+    lds = (2 * bufh * 2 + 2 * stgh * 2 + -(-(cp["KH"] * cp["KW"] * 2) // 16) * 16
+           + 2 * cp["KH"] * DWM_TROW * 2 + 16)
+    xch = cp["H"] * cp["W"] // 8
+    if lds > DWM_MAX_LDS or xch > DWM_MAX_CHUNKS * DWM_THREADS:
+        return None
+    return dict(S=S, TW=TW, TV=TV, pitch=pitch, NR=NR, bufh=bufh, sp=sp, stgh=stgh, no=no, xch=xch,
+                nitem=TV * TW)
+
+
+def _dwm_geo(xs, ws, attrs):
+    # 2-D geometry with the auto_pad rules resolved by the oracle
+    dl = attrs.get("dilations", [1, 1])
+    out, pb = oracle.output_dims(list(xs[2:]), list(ws[2:]), [1, 1], dl,
+                                 attrs.get("auto_pad", "NOTSET"), attrs.get("pads", [0] * 4))
+    return dict(H=xs[2], W=xs[3], OH=out[0], OW=out[1], KH=ws[2], KW=ws[3], dh=dl[0], dw=dl[1],
+                ph=pb[0], pw=pb[1])
+
+
+@pytest.mark.parametrize("ci", range(len(DWM_CASES)))
+def test_dwm_depthwise_index_model(ci):
+    xs, ws, attrs = DWM_CASES[ci]
+    cp = _dwm_geo(xs, ws, attrs)
+    assert cp["W"] % 8 == 0 and cp["OW"] % 8 == 0
+    f = _dwm_plan(cp)
+    assert f is not None, "every case here takes the banded-MFMA kernel"
+    pitch, S, bufh, sp = f["pitch"], f["S"], f["bufh"], f["sp"]
+    in_row = lambda r, pt=pitch: r * pt + 8 * (r >> 2)
+    rng = np.random.default_rng([7420, ci])
+    x = rng.standard_normal(xs)
+    w = rng.standard_normal(ws)
+    bias = rng.standard_normal(ws[0])
+    M, Mg = ws[0], ws[0] // xs[1]
+    out_sz = cp["OH"] * cp["OW"]
+    ref = oracle.fusedconv(x, w, bias, None, **attrs)
+    KH, KW, dh, dw = cp["KH"], cp["KW"], cp["dh"], cp["dw"]
+    cw8 = cp["W"] // 8
+    for n, m in itertools.product(range(xs[0]), range(M)):
+        # both LDS buffers zeroed once; this plane goes into buffer b
+        b = (n + m) & 1
+        lds = np.zeros(2 * bufh)
+        plane = x[n, m // Mg].reshape(-1)
+        for tid, kk in itertools.product(range(DWM_THREADS), range(DWM_MAX_CHUNKS)):
+            c = tid + kk * DWM_THREADS
+            cc = min(c, f["xch"] - 1)
+            row, col = divmod(cc, cw8)
+            dst = in_row(row + cp["ph"]) + col * 8 + cp["pw"] + S
+            assert col * 8 + 7 + cp["pw"] + S < pitch and dst + 8 <= bufh
+            lds[b * bufh + dst:b * bufh + dst + 8] = plane[cc * 8:cc * 8 + 8]
+        # zero-padded kernel rows, two copies one half apart
+        wk = w[m, 0]
+        trow = np.zeros(2 * KH * DWM_TROW)
+        for idx in range(2 * KH * DWM_TROW):
+            cpy, r = divmod(idx, KH * DWM_TROW)
+            kh, i = divmod(r, DWM_TROW)
+            d = i + cpy - DWM_TBASE
+            if d >= 0 and d % dw == 0 and d // dw < KW:
+                trow[idx] = wk[kh, d // dw]
+        # A operand: lane (j, q) holds T_kh[j][8q .. 8q+7]
+        A = np.zeros((KH, 16, 32))
+        for j, q in itertools.product(range(16), range(4)):
+            i0 = DWM_TBASE + 8 * q - j - S
+            assert 0 <= i0 and i0 + 8 <= DWM_TROW
+            base = (i0 & 1) * KH * DWM_TROW + 2 * (i0 >> 1)
+            for kh in range(KH):
+                A[kh, j, 8 * q:8 * q + 8] = trow[base + kh * DWM_TROW:base + kh * DWM_TROW + 8]
+        stage = np.full(2 * f["stgh"], np.nan)
+        sb = ((n + m + 1) & 1) * f["stgh"]
+        for wave in range(DWM_THREADS // 64):
+          for it in range(wave, f["nitem"], 4):
+            v, t = divmod(it, f["TW"])
+            # B operand of input fragment s: lane (r, q) reads row 64v + 4r + s,
+            # columns 16t + 8q .. +7, inside its own buffer
+            frag = []
+            for s in range(DWM_RG + dh * (KH - 1)):
+                B = np.zeros((32, 16))
+                for r, q in itertools.product(range(16), range(4)):
+                    a = in_row(64 * v + 4 * r + s) + 16 * t + 8 * q
+                    assert 64 * v + 4 * r + s < f["NR"] and 16 * t + 8 * q + 8 <= pitch - 8
+                    assert a + 8 <= bufh
+                    B[8 * q:8 * q + 8, r] = lds[b * bufh + a:b * bufh + a + 8]
+                frag.append(B)
+            for p in range(DWM_RG):
+                D = np.full((16, 16), bias[m])
+                for kh in range(KH):
+                    D += A[kh] @ frag[p + dh * kh]
+                # lane (r, q): 4 consecutive outputs into the stage, one 8-byte write
+                for r, q in itertools.product(range(16), range(4)):
+                    row, oc = 64 * v + 4 * r + p, 16 * t + 4 * q
+                    a = in_row(row, sp) + oc
+                    assert a % 4 == 0 and oc + 4 <= sp - 8 and a + 4 <= f["stgh"]
+                    stage[sb + a:sb + a + 4] = D[4 * q:4 * q + 4, r]
+        # the stage to Y: piece o (8 outputs), lanes past the last piece dropped
+        y = np.full(out_sz, np.nan)
+        writes = np.zeros(out_sz, dtype=int)
+        ow8 = cp["OW"] // 8
+        for tid, kk in itertools.product(range(DWM_THREADS), range(2)):
+            o = tid + kk * DWM_THREADS
+            oc = min(o, f["no"] - 1)
+            row, col = divmod(oc, ow8)
+            a = in_row(row, sp) + col * 8
+            assert a % 8 == 0 and a + 8 <= f["stgh"]
+            piece = stage[sb + a:sb + a + 8]
+            assert not np.isnan(piece).any(), "read of an unwritten stage slot"
+            if o < f["no"]:
+                y[oc * 8:oc * 8 + 8] = piece
+                writes[oc * 8:oc * 8 + 8] += 1
+        assert (writes == 1).all(), "every output stored exactly once"
+        np.testing.assert_allclose(y.reshape(cp["OH"], cp["OW"]), ref[n, m], rtol=1e-12, atol=1e-12)
+        # the exact loop for planes with a non-finite input, same buffer
+        for oh, ow in itertools.product(range(cp["OH"]), range(cp["OW"])):
+            s = bias[m]
+            for kh, kw in itertools.product(range(KH), range(KW)):
+                a = in_row(oh + dh * kh) + ow + dw * kw + S
+                assert a < bufh
+                s += lds[b * bufh + a] * wk[kh, kw]
+            assert abs(s - ref[n, m, oh, ow]) <= 1e-12 * max(1.0, abs(s))
