@@ -17,12 +17,13 @@
 // per CU, handing work over through LDS with one barrier per unit:
 //   * 2 producer waves load the input box of unit t+2 into registers and
 //     write the box of unit t+1 into LDS (zero outside the image);
-//   * 8 MFMA waves (16 channels each, all 128 pixels) compute unit t from its
+//   * 8 MFMA waves (32 channels x 64 pixels each, so that every box operand
+//     a wave reads from LDS feeds two channel tiles) compute unit t from its
 //     box (weights repacked into the row layout Wr[g][m][row][8] by
 //     fusedconv_prepare_weights or at the start of every run, held in
-//     registers), apply the fused epilogue (bias seeds the
-//     accumulators; residual, activation, one rounding) and write the fp16
-//     results into an LDS stage;
+//     registers): all of a wave's products first (8 independent accumulator
+//     chains), then the fused epilogue (bias seeds the accumulators;
+//     residual, activation, one rounding) into an fp16 LDS stage;
 //   * 2 store waves write unit t-1's staged results to Y as whole 16-byte
 //     pieces, 8 lanes covering 64 consecutive outputs of one row.
 // Loads and stores thus sit in different waves: a wave's vector-memory
@@ -40,7 +41,7 @@
 namespace fc {
 namespace {
 
-constexpr int kMfmaWaves = 8;     // 16 output channels each, all 128 pixels of a unit
+constexpr int kMfmaWaves = 8;     // 32 output channels x 64 pixels of a unit each
 constexpr int kThreads = (kMfmaWaves + 4) * 64;  // + 2 producer waves + 2 store waves
 constexpr int kRoleLanes = 128;  // lanes of the producer and of the store role
 constexpr int kBM = 128;       // output channels per unit
@@ -62,6 +63,10 @@ constexpr int kPersistentBlocks = 256;  // one block on each of the 256 CUs
 // VALU-bound: the stem applies Gelu to 151 million outputs.
 constexpr int kPhiN = 768;
 constexpr float kPhiScale = 64.0f, kPhiOrigin = 384.0f;  // i + f = 64 x + 384
+// largest float below kPhiN: i = floor(u) <= kPhiN - 1 and f = u - i < 1; at
+// the top (x >= 6) Phi_{kPhiN-1} + f * step differs from Phi_{kPhiN} by 6e-8
+// of a step of 1e-10
+constexpr float kPhiTop = 767.99994f;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
@@ -152,8 +157,9 @@ __device__ __forceinline__ SUnit decode_unit(int u, const ConvParams& cp, const 
 // chunks into registers, zero what is outside and write them.  A4: stride
 // % 4 == 0, with s chosen so that delta % 4 == 0: every operand stretch is
 // 8-byte aligned (the launcher checks (pw + s) % 4 == 0).  VY: OW % 8 == 0
-// (16-byte stores of Y).
-template <bool A4, bool VEC, bool VY, int ACT>
+// (16-byte stores of Y).  HZ: a residual Z is added (no residual code or
+// loads otherwise).
+template <bool A4, bool VEC, bool VY, bool HZ, int ACT>
 __global__ __launch_bounds__(kThreads, 1) void smallc_kernel(const half_t* __restrict__ x,
                                                              const half_t* __restrict__ wr,
                                                              const half_t* __restrict__ bias,
@@ -327,9 +333,11 @@ __global__ __launch_bounds__(kThreads, 1) void smallc_kernel(const half_t* __res
   }
 
   // ======================= MFMA waves =======================
-  // wave wmi owns channels [wmi*16, +16) (one m tile) of the unit's 128
-  // channels, over all 128 pixels (8 tiles of 16)
+  // wave wmi owns channels [32 wm, +32) (two m tiles) of the unit's 128
+  // channels and pixels [64 wp, +64) (four pixel tiles): each box operand it
+  // reads serves two channel tiles
   const int wmi = wave;
+  const int wm = wmi & 3, wp = wmi >> 2;
   const int r16 = lane & 15, q = lane >> 4;
   // LDS offset (halves) of this lane's reduction row in each block: row
   // kb*4 + q = (c, kh, chunk) -> c*plane + kh*dh*pitch + chunk*8; rows past R
@@ -350,17 +358,20 @@ __global__ __launch_bounds__(kThreads, 1) void smallc_kernel(const half_t* __res
   // bias of (group, m block); reloaded when a unit changes either.
   // Unconditional loads: blocks past KB re-read block 0 (never used), a
   // missing bias reads wr[0] and is replaced by 0.
-  half8 wf[kMaxKB];
-  float bv = 0.0f;
+  half8 wf[2][kMaxKB];
+  float bv[2] = {0.0f, 0.0f};
   int cur_g = -1, cur_mb = -1;
   auto load_weights = [&](int g, int mb) __attribute__((always_inline)) {
-    const int m = mb * kBM + wmi * 16 + r16;
-    const half_t* wl = wr + ((int64_t)g * st.mgp + m) * (st.KB * 4 * 8) + q * 8;
 #pragma unroll
-    for (int kb = 0; kb < kMaxKB; ++kb) wf[kb] = *(const half8*)(wl + (kb < st.KB ? kb * 32 : 0));
-    const bool ok = cp.has_bias && m < cp.Mg;
-    const float t = to_f32(*(ok ? bias + g * cp.Mg + m : wr));
-    bv = ok ? t : 0.0f;
+    for (int ct = 0; ct < 2; ++ct) {
+      const int m = mb * kBM + (2 * wm + ct) * 16 + r16;
+      const half_t* wl = wr + ((int64_t)g * st.mgp + m) * (st.KB * 4 * 8) + q * 8;
+#pragma unroll
+      for (int kb = 0; kb < kMaxKB; ++kb) wf[ct][kb] = *(const half8*)(wl + (kb < st.KB ? kb * 32 : 0));
+      const bool ok = cp.has_bias && m < cp.Mg;
+      const float t = to_f32(*(ok ? bias + g * cp.Mg + m : wr));
+      bv[ct] = ok ? t : 0.0f;
+    }
     cur_g = g;
     cur_mb = mb;
   };
@@ -376,11 +387,18 @@ __global__ __launch_bounds__(kThreads, 1) void smallc_kernel(const half_t* __res
   }
   // Phi by the table at x (clamped to the table's range)
   auto phi_of = [&](float xv) __attribute__((always_inline)) {
-    const float u = __builtin_amdgcn_fmed3f(fmaf(xv, kPhiScale, kPhiOrigin), 0.0f, (float)kPhiN);
-    const int i = min((int)u, kPhiN - 1);
-    const float2 pe = phi[i];
-    return fmaf(u - (float)i, pe.y, pe.x);
+    const float u = __builtin_amdgcn_fmed3f(fmaf(xv, kPhiScale, kPhiOrigin), 0.0f, kPhiTop);
+    const float2 pe = phi[(int)u];
+    return fmaf(__builtin_amdgcn_fractf(u), pe.y, pe.x);
   };
+  // operand row of lane r16 in pixel tile pt4: pixel (wp*4 + pt4)*16 + r16
+  // of the unit, at this LDS offset from the window start
+  int pixb[kBN / 32];
+#pragma unroll
+  for (int pt4 = 0; pt4 < kBN / 32; ++pt4) {
+    const int pa = (wp * (kBN / 32) + pt4) * 16 + r16;
+    pixb[pt4] = (pa >> st.ltw) * cp.sh * st.pitch + (pa & (st.TW - 1)) * cp.sw;
+  }
   lds_barrier();  // the producers' first box is in LDS; the Phi table is written
   for (int t = 0; t <= nu; ++t) {
     if (t < nu) {
@@ -388,78 +406,87 @@ __global__ __launch_bounds__(kThreads, 1) void smallc_kernel(const half_t* __res
       if (cu.g != cur_g || cu.mb != cur_mb) load_weights(cu.g, cu.mb);
       const int delta = cu.ow0 * cp.sw - cp.pw - st.s - box_x0(cu);  // 0 .. 7
       const half_t* buf = lds + (t % kBoxBufs) * box;
-      half_t* sb = stage0 + (t & 1) * kBM * kSP + (wmi * 16 + r16) * kSP;
-      const int m = cu.mb * kBM + wmi * 16 + r16;
-      const int64_t zbase = (cu.n * cp.M + (int64_t)cu.g * cp.Mg + m) * cp.out_sz;
-      for (int pt = 0; pt < kBN / 16; ++pt) {
-        // residual for this lane's 4 pixels, requested before the tile's
-        // products (an 8-byte load when OW % 4 == 0, so that a lane's 4
-        // pixels are all in or all out of the row)
-        const int pe = pt * 16 + 4 * q;
-        uint2v zr = {0u, 0u};
-        if (cp.has_z && (cp.OW & 3) == 0) {
-          const int oh = cu.oh0 + (pe >> st.ltw), ow = cu.ow0 + (pe & (st.TW - 1));
-          const bool ok = m < cp.Mg && oh < cp.OH && ow < cp.OW;
-          zr = *(const uint2v*)(ok ? z + zbase + oh * cp.OW + ow : z);
-        }
-        // operand row of lane r16: pixel pt*16 + r16
-        const int pa = pt * 16 + r16;
-        const int pix = (pa >> st.ltw) * cp.sh * st.pitch + (pa & (st.TW - 1)) * cp.sw + delta;
-        float4v acc = float4v{bv, bv, bv, bv};
-        auto read_a = [&](int kb) __attribute__((always_inline)) {
-          const int o = roff[kb] + pix;
-          if constexpr (A4) {
-            const uint2v lo = *(const uint2v*)(buf + o);
-            const uint2v hi = *(const uint2v*)(buf + o + 4);
-            return __builtin_bit_cast(half8, (__attribute__((ext_vector_type(4))) unsigned){lo[0], lo[1], hi[0], hi[1]});
-          }
-          // any alignment: 5 dwords, shifted
-          const unsigned* d = (const unsigned*)buf + (o >> 1);
-          const unsigned sh = (o & 1) * 16;
-          unsigned w5[5];
+      constexpr int kPT = kBN / 32;  // pixel tiles per wave
+      // residuals of this lane's 4 pixels in each (pixel tile, channel tile),
+      // requested before the products (8-byte loads when OW % 4 == 0, so
+      // that a lane's 4 pixels are all in or all out of the row)
+      uint2v zr[kPT][2];
 #pragma unroll
-          for (int k = 0; k < 5; ++k) w5[k] = d[k];
-          __attribute__((ext_vector_type(4))) unsigned uu;
+      for (int pt4 = 0; pt4 < kPT; ++pt4)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) uu[k] = __builtin_amdgcn_alignbit(w5[k + 1], w5[k], sh);
-          return __builtin_bit_cast(half8, uu);
-        };
-        if (st.KB == kMaxKB) {
-          // every reduction block used: all operands are read before the
-          // first product, so the tile waits for LDS once
-          half8 af[kMaxKB];
-#pragma unroll
-          for (int kb = 0; kb < kMaxKB; ++kb) af[kb] = read_a(kb);
-#pragma unroll
-          for (int kb = 0; kb < kMaxKB; ++kb)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[kb], wf[kb], acc, 0, 0, 0);
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < kMaxKB; ++kb) {
-            if (kb >= st.KB) break;
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(read_a(kb), wf[kb], acc, 0, 0, 0);
+        for (int ct = 0; ct < 2; ++ct) {
+          zr[pt4][ct] = uint2v{0u, 0u};
+          if (HZ && (cp.OW & 3) == 0) {
+            const int pe = (wp * kPT + pt4) * 16 + 4 * q;
+            const int m = cu.mb * kBM + (2 * wm + ct) * 16 + r16;
+            const int64_t zbase = (cu.n * cp.M + (int64_t)cu.g * cp.Mg + m) * cp.out_sz;
+            const int oh = cu.oh0 + (pe >> st.ltw), ow = cu.ow0 + (pe & (st.TW - 1));
+            const bool ok = m < cp.Mg && oh < cp.OH && ow < cp.OW;
+            zr[pt4][ct] = *(const uint2v*)(ok ? z + zbase + oh * cp.OW + ow : z);
           }
         }
-        // The accumulator is read by VALU a few instructions after the last
-        // MFMA when the epilogue is short (no residual, no activation); the
-        // compiler's wait states for v_mfma_f32_16x16x32_f16 results were
-        // measured too few on gfx950 (the second half of the accumulator read
-        // stale), so 32 wait states are forced here (at most 256 cycles per
-        // unit and wave, covered by the other MFMA wave of the SIMD).
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        // epilogue: lane holds pixels pt*16 + 4q .. +3 (4 consecutive columns
-        // of one tile row) of channel wmi*16 + r16; residual, activation and
+      auto read_a = [&](int pix, int kb) __attribute__((always_inline)) {
+        const int o = roff[kb] + pix;
+        if constexpr (A4) {
+          const uint2v lo = *(const uint2v*)(buf + o);
+          const uint2v hi = *(const uint2v*)(buf + o + 4);
+          return __builtin_bit_cast(half8, (__attribute__((ext_vector_type(4))) unsigned){lo[0], lo[1], hi[0], hi[1]});
+        }
+        // any alignment: 5 dwords, shifted
+        const unsigned* d = (const unsigned*)buf + (o >> 1);
+        const unsigned sh = (o & 1) * 16;
+        unsigned w5[5];
+#pragma unroll
+        for (int k = 0; k < 5; ++k) w5[k] = d[k];
+        __attribute__((ext_vector_type(4))) unsigned uu;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) uu[k] = __builtin_amdgcn_alignbit(w5[k + 1], w5[k], sh);
+        return __builtin_bit_cast(half8, uu);
+      };
+      // the products of all the wave's tiles first (8 independent
+      // accumulator chains keep the matrix core busy), then one wait-state
+      // gap, then the epilogues (32 independent values)
+      float4v acc[kPT][2];
+#pragma unroll
+      for (int pt4 = 0; pt4 < kPT; ++pt4) {
+        const int pix = pixb[pt4] + delta;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) acc[pt4][ct] = float4v{bv[ct], bv[ct], bv[ct], bv[ct]};
+#pragma unroll
+        for (int kb = 0; kb < kMaxKB; ++kb) {
+          if (kb >= st.KB) break;
+          const half8 af = read_a(pix, kb);
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+            acc[pt4][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, wf[ct][kb], acc[pt4][ct], 0, 0, 0);
+        }
+      }
+      // The accumulators are read by VALU soon after the last MFMA; the
+      // compiler's wait states for v_mfma_f32_16x16x32_f16 results were
+      // measured too few on gfx950 (the second half of an accumulator read
+      // stale), so 32 wait states are forced here.
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int pt4 = 0; pt4 < kPT; ++pt4)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        // lane holds pixels pt*16 + 4q .. +3 (4 consecutive columns of one
+        // tile row) of channel (2 wm + ct)*16 + r16; residual, activation and
         // the rounding here, the store from the stage
-        float4v v = acc;
-        if (cp.has_z) {
+        const int pe = (wp * kPT + pt4) * 16 + 4 * q;
+        const int m = cu.mb * kBM + (2 * wm + ct) * 16 + r16;
+        half_t* sb = stage0 + (t & 1) * kBM * kSP + ((2 * wm + ct) * 16 + r16) * kSP;
+        float4v v = acc[pt4][ct];
+        if constexpr (HZ) {
           if ((cp.OW & 3) == 0) {
-            const half4 zh = __builtin_bit_cast(half4, zr);
+            const half4 zh = __builtin_bit_cast(half4, zr[pt4][ct]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] += (float)zh[r];
           } else {
             // OW % 4 != 0: element by element (a lane's 4 pixels may leave the row)
+            const int64_t zbase = (cu.n * cp.M + (int64_t)cu.g * cp.Mg + m) * cp.out_sz;
             const int oh = cu.oh0 + (pe >> st.ltw), ow = cu.ow0 + (pe & (st.TW - 1));
             if (m < cp.Mg && oh < cp.OH) {
 #pragma unroll
@@ -571,17 +598,22 @@ int launch_repack(const ConvParams& cp, const SmallTile& st, const RunArgs& a) {
   return hipPeekAtLastError() == hipSuccess ? FUSEDCONV_OK : FUSEDCONV_ERR_LAUNCH;
 }
 
-template <bool A4, bool VEC, bool VY>
-int launch_t(const ConvParams& cp, const SmallTile& st, const RunArgs& a) {
-  const void* kfn = (const void*)smallc_kernel<A4, VEC, VY, FC_ACT>;
+template <bool A4, bool VEC, bool VY, bool HZ>
+int launch_hz(const ConvParams& cp, const SmallTile& st, const RunArgs& a) {
+  const void* kfn = (const void*)smallc_kernel<A4, VEC, VY, HZ, FC_ACT>;
   if (set_max_dynamic_lds(kfn, (int)kMaxLds) != FUSEDCONV_OK) return FUSEDCONV_ERR_LAUNCH;
   // persistent: one block per CU (256 CUs), each looping over units
   const int64_t units = (int64_t)cp.G * cp.n * st.tiles_h * st.tiles_w * st.nmb;
   const unsigned blocks = (unsigned)(units < kPersistentBlocks ? units : kPersistentBlocks);
-  return launch_conv(smallc_kernel<A4, VEC, VY, FC_ACT>, dim3(blocks), dim3(kThreads),
+  return launch_conv(smallc_kernel<A4, VEC, VY, HZ, FC_ACT>, dim3(blocks), dim3(kThreads),
                      lds_bytes(), a, kEdgeBoth, (const half_t*)a.x,
                      (const half_t*)a.ws, (const half_t*)a.bias, (const half_t*)a.z, (half_t*)a.y,
                      cp, st);
+}
+
+template <bool A4, bool VEC, bool VY>
+int launch_t(const ConvParams& cp, const SmallTile& st, const RunArgs& a) {
+  return cp.has_z ? launch_hz<A4, VEC, VY, true>(cp, st, a) : launch_hz<A4, VEC, VY, false>(cp, st, a);
 }
 
 }  // namespace
