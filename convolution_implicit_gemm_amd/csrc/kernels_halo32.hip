@@ -20,6 +20,12 @@
 // The per-element im2col gather of the IGEMM route, whose loads wait at the
 // joins of their bounds tests, is gone: X is read once per channel block as
 // whole 16-byte rows of the box.
+// Depth-stepped form (DS): when a 3-D tile's box, every kernel depth at
+// once, does not fit, the box holds one input depth plane and the K loop
+// walks (channel block, kernel depth kd, in-plane tap): plane kd of a tile at
+// output depth od is input depth od*sd - pd + kd*dd, planes outside the input
+// are skipped (their products are zero), and one box buffer per block (two
+// blocks per CU) takes the next plane after a barrier.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -44,6 +50,8 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int log2i(int v) { return 31 - __builtin_clz((unsigned)v); }
 
 struct Geo32 {
+  int ds;                    // depth-stepped: the box is one input depth plane
+  int taps2;                 // taps per box: KH*KW when depth-stepped, else all taps
   int TD, TH, TW, ltw, lth;  // output tile (TW a power of two >= 16)
   int BD, BH, BW;            // input box extents
   int ND, NH, NW;            // positions per stride phase
@@ -53,7 +61,7 @@ struct Geo32 {
   int ntile;
   int nmb, ncb, mgp;         // m blocks, channel blocks, Wp rows per (tap, block)
   int vec;                   // W % 4 == 0: 16-byte row loads
-  int tap_off[kMaxTaps];     // LDS row offset (positions) of each tap
+  int tap_off[kMaxTaps];     // LDS row offset (positions) of each tap of a box
 };
 
 __device__ __forceinline__ int phase_index(int a, int s, int n) {
@@ -82,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void repack32_kernel(const float* __restr
 
 // Block tile: WGP x WGM waves, each 64 pixels x 64 output channels (4 x 4
 // MFMA tiles of 16 x 16); BN = 64*WGP pixels, BM = 64*WGM channels.
-template <int WGP>
+template <int WGP, bool DS>
 __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __restrict__ x,
                                                              const float* __restrict__ wp,
                                                              const float* __restrict__ bias,
@@ -114,20 +122,39 @@ __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __rest
   const int wpi = wave % WGP, wmi = wave / WGP;
   const int r16 = lane & 15, q = lane >> 4;
 
-  // ---- zero both boxes: positions outside the image stay zero
-  for (int i = tid; i < 2 * box / 4; i += kThreads) ((float4v*)lds32)[i] = float4v{0.f, 0.f, 0.f, 0.f};
+  // ---- zero the boxes: positions outside the image stay zero
+  constexpr int kBufs = DS ? 1 : 2;
+  for (int i = tid; i < kBufs * box / 4; i += kThreads) ((float4v*)lds32)[i] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  // ---- boxes: (channel block cb, kernel depth kd) for bi = cb * nkd + (kd -
+  // kd_lo); without depth steps one box per channel block (nkd = 1, kd = 0)
+  int kd_lo = 0, nkd = 1;
+  if constexpr (DS) {
+    const int z0 = od0 * cp.sd - cp.pd;  // input depth of kd = 0
+    while (kd_lo < cp.KD && z0 + kd_lo * cp.dd < 0) ++kd_lo;
+    int kd_hi = kd_lo;
+    while (kd_hi < cp.KD && z0 + kd_hi * cp.dd < cp.D) ++kd_hi;
+    nkd = kd_hi - kd_lo;
+  }
+  const int nbox = hg.ncb * nkd;
+  auto box_cb = [&](int bi) __attribute__((always_inline)) { return DS ? bi / nkd : bi; };
+  auto box_kd = [&](int bi) __attribute__((always_inline)) { return DS ? kd_lo + bi % nkd : 0; };
+  // element offset of box bi's input plane (depth-stepped) from the image base
+  auto box_zoff = [&](int bi) __attribute__((always_inline)) {
+    return DS ? (int64_t)(od0 * cp.sd - cp.pd + box_kd(bi) * cp.dd) * cp.H * cp.W : (int64_t)0;
+  };
 
   // ---- box loader: item = (channel quad cq, in-image box row, 4-column
   // group): four 16-byte loads (4 channels, same 4 columns), written as up
   // to 4 LDS rows of 4 channels
-  const int d_lo = max(bd0, 0), d_hi = min(bd0 + hg.BD, cp.D);
+  const int d_lo = DS ? 0 : max(bd0, 0), d_hi = DS ? 1 : min(bd0 + hg.BD, cp.D);
   const int h_lo = max(bh0, 0), h_hi = min(bh0 + hg.BH, cp.H);
   const int w_lo = max(bw0, 0), w_hi = min(bw0 + hg.BW, cp.W);
   const int g_lo = w_lo >> 2, g_hi = (w_hi + 3) >> 2;
   const int nd = max(d_hi - d_lo, 0), nh = max(h_hi - h_lo, 0), ngr = max(g_hi - g_lo, 0);
   const int nitems = 4 * nd * nh * ngr;
   const float* ximg = x + (n * cp.C + (int64_t)g * cp.Cg) * cp.in_sz;
-  constexpr int PF = 2;  // items per thread held across a channel block
+  constexpr int PF = 2;  // items per thread held across a box
   struct Item { int goff, ldst, cq, mask, aw0; };
   auto decode = [&](int i) __attribute__((always_inline)) {
     Item it;
@@ -144,18 +171,20 @@ __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __rest
       if (iw + e >= w_lo && iw + e < w_hi) mask |= 1 << e;
     it.mask = mask;
     it.goff = (id * cp.H + ih) * cp.W + iw;
-    it.ldst = (phase_index(id - bd0, cp.sd, hg.ND) * hg.LH + phase_index(ih - bh0, cp.sh, hg.NH)) * hg.LW;
+    it.ldst = ((DS ? 0 : phase_index(id - bd0, cp.sd, hg.ND)) * hg.LH + phase_index(ih - bh0, cp.sh, hg.NH)) *
+              hg.LW;
     it.aw0 = iw - bw0;
     return it;
   };
   Item items[PF];
   float4v xr[PF][4];
-  auto load_item = [&](const Item& it, int cb, float4v* v) __attribute__((always_inline)) {
-    const int c0 = cb * kCB + it.cq * 4;
+  auto load_item = [&](const Item& it, int bi, float4v* v) __attribute__((always_inline)) {
+    const int c0 = box_cb(bi) * kCB + it.cq * 4;
+    const float* xz = ximg + box_zoff(bi);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bool ok = it.mask != 0 && c0 + j < cp.Cg;
-      const float* s = ok ? ximg + (int64_t)(c0 + j) * cp.in_sz + it.goff : x;
+      const float* s = ok ? xz + (int64_t)(c0 + j) * cp.in_sz + it.goff : x;
       if (hg.vec) {
         v[j] = *(const float4v*)s;
       } else {
@@ -167,9 +196,9 @@ __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __rest
       }
     }
   };
-  auto store_item = [&](const Item& it, int cb, float* xs, const float4v* v) __attribute__((always_inline)) {
+  auto store_item = [&](const Item& it, int bi, float* xs, const float4v* v) __attribute__((always_inline)) {
     if (it.mask == 0) return;
-    const int cvalid = cp.Cg - cb * kCB - it.cq * 4;
+    const int cvalid = cp.Cg - box_cb(bi) * kCB - it.cq * 4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (!((it.mask >> e) & 1)) continue;
@@ -187,14 +216,14 @@ __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __rest
     items[k].goff = items[k].ldst = items[k].cq = items[k].aw0 = 0;
     if (i < nitems) items[k] = decode(i);
   }
-  auto prefetch_box = [&](int cb) __attribute__((always_inline)) {
+  auto prefetch_box = [&](int bi) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < PF; ++k) load_item(items[k], cb, xr[k]);
+    for (int k = 0; k < PF; ++k) load_item(items[k], bi, xr[k]);
   };
-  auto store_box = [&](int buf, int cb) __attribute__((always_inline)) {
+  auto store_box = [&](int buf, int bi) __attribute__((always_inline)) {
     float* xs = lds32 + buf * box;
 #pragma unroll
-    for (int k = 0; k < PF; ++k) store_item(items[k], cb, xs, xr[k]);
+    for (int k = 0; k < PF; ++k) store_item(items[k], bi, xs, xr[k]);
     for (int i0 = PF * kThreads; i0 < nitems; i0 += kThreads) {  // items beyond the held ones
       const int i = i0 + tid;
       Item it;
@@ -202,8 +231,8 @@ __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __rest
       it.goff = it.ldst = it.cq = it.aw0 = 0;
       if (i < nitems) it = decode(i);
       float4v v[4];
-      load_item(it, cb, v);
-      store_item(it, cb, xs, v);
+      load_item(it, bi, v);
+      store_item(it, bi, xs, v);
     }
   };
 
@@ -232,30 +261,32 @@ __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __rest
     for (int i = 0; i < 4; ++i) acc[i][j] = float4v{bv, bv, bv, bv};
   }
 
+  const int taps2 = hg.taps2, ncb = hg.ncb, nsteps = nbox * taps2;
+  // step s = (box bi, in-box tap t2) reads Wp tile (kd*taps2 + t2)*ncb + cb
+  auto woff = [&](int s) __attribute__((always_inline)) {
+    const int bi = s / taps2, t2 = s - bi * taps2;
+    return ((int64_t)(box_kd(bi) * taps2 + t2) * ncb + box_cb(bi)) * wstep;
+  };
   lds_barrier();  // zero fill done
-  prefetch_box(0);
-  store_box(0, 0);
-  if (hg.ncb > 1) prefetch_box(1);
+  if (nbox > 0) {
+    prefetch_box(0);
+    store_box(0, 0);
+  }
+  if (nbox > 1) prefetch_box(1);
   float4v wa[4], wb[4];
   auto load_w = [&](int64_t off, float4v* v) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) v[j] = *(const float4v*)(wg + off + wl + j * 16 * kCB);
   };
-  load_w(0, wa);
+  load_w(nsteps > 0 ? woff(0) : 0, wa);
   lds_barrier();
 
-  const int taps = cp.taps, ncb = hg.ncb, nsteps = ncb * taps;
-  // step s = (cb, t) reads Wp tile t*ncb + cb
-  auto woff = [&](int s) __attribute__((always_inline)) {
-    const int cb = s / taps, t = s - cb * taps;
-    return ((int64_t)t * ncb + cb) * wstep;
-  };
   auto step = [&](int s, const float4v* wc, float4v* wn) __attribute__((always_inline)) {
-    const int cb = s / taps, t = s - cb * taps;
+    const int bi = s / taps2, t2 = s - bi * taps2;
     // the next step's weights (past the last step: the first tile again)
     load_w(s + 1 < nsteps ? woff(s + 1) : 0, wn);
     __builtin_amdgcn_sched_barrier(0);
-    const float* xb = lds32 + (cb & 1) * box + hg.tap_off[t] * kLdc + q * 4;
+    const float* xb = lds32 + (DS ? 0 : (bi & 1) * box) + hg.tap_off[t2] * kLdc + q * 4;
     float4v a[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = *(const float4v*)(xb + apos[i] * kLdc);
@@ -266,13 +297,14 @@ __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __rest
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][e], wc[j][e], acc[i][j], 0, 0, 0);
-    if (t + 1 == taps && cb + 1 < ncb) {
-      // the next channel block's box (held in registers) into the other
-      // buffer: its previous readers (channel block cb - 1) all passed the
-      // last barrier
-      store_box((cb + 1) & 1, cb + 1);
+    if (t2 + 1 == taps2 && bi + 1 < nbox) {
+      // the next box (held in registers) into the other buffer, whose
+      // previous readers (box bi - 1) all passed the last barrier; with one
+      // buffer, after every wave is done with this box
+      if constexpr (DS) lds_barrier();
+      store_box(DS ? 0 : (bi + 1) & 1, bi + 1);
       lds_barrier();
-      if (cb + 2 < ncb) prefetch_box(cb + 2);
+      if (bi + 2 < nbox) prefetch_box(bi + 2);
     }
   };
   int s = 0;
@@ -338,20 +370,25 @@ __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __rest
 // Tile choice: WGP = 4 (256 pixels x 64 channels) when M/group <= 64, else
 // WGP = 2 (128 x 128); tile widths 16 .. 256 in order of padded output
 // area; the first whose two boxes fit is taken.
-bool choose32_wgp(const ConvParams& cp, int wgp, Geo32& hg);
+bool choose32_wgp(const ConvParams& cp, int wgp, bool ds, Geo32& hg);
 
+// Full-depth boxes first; for 3-D convs whose box does not fit, the
+// depth-stepped form (one input depth plane per box).
 bool choose32(const ConvParams& cp, int& wgp, Geo32& hg) {
-  if (cp.taps > kMaxTaps || cp.transposed) return false;
-  wgp = cp.Mg <= 64 ? 4 : 2;
-  if (choose32_wgp(cp, wgp, hg)) return true;
-  if (wgp == 4 && choose32_wgp(cp, 2, hg)) {  // smaller pixel tiles for small images
-    wgp = 2;
-    return true;
+  if (cp.transposed) return false;
+  for (int ds = 0; ds < (cp.KD > 1 ? 2 : 1); ++ds) {
+    if ((ds ? cp.KH * cp.KW : cp.taps) > kMaxTaps) continue;  // taps of one box
+    wgp = cp.Mg <= 64 ? 4 : 2;
+    if (choose32_wgp(cp, wgp, ds, hg)) return true;
+    if (wgp == 4 && choose32_wgp(cp, 2, ds, hg)) {  // smaller pixel tiles for small images
+      wgp = 2;
+      return true;
+    }
   }
   return false;
 }
 
-bool choose32_wgp(const ConvParams& cp, int wgp, Geo32& hg) {
+bool choose32_wgp(const ConvParams& cp, int wgp, bool ds, Geo32& hg) {
   const int bn = 64 * wgp, bm = 64 * (4 / wgp);
   int order[5], no = 0;
   double waste[5];
@@ -371,19 +408,21 @@ bool choose32_wgp(const ConvParams& cp, int wgp, Geo32& hg) {
   for (int oi = 0; oi < no; ++oi) {
     const int tw = order[oi], th = bn / tw, td = 1;
     Geo32 h{};
+    h.ds = ds;
+    h.taps2 = ds ? cp.KH * cp.KW : cp.taps;
     h.TD = td; h.TH = th; h.TW = tw;
     h.ltw = log2i(tw);
     h.lth = log2i(th);
-    h.BD = (td - 1) * cp.sd + (cp.KD - 1) * cp.dd + 1;
+    h.BD = ds ? 1 : (td - 1) * cp.sd + (cp.KD - 1) * cp.dd + 1;
     h.BH = (th - 1) * cp.sh + (cp.KH - 1) * cp.dh + 1;
     h.BW = (tw - 1) * cp.sw + (cp.KW - 1) * cp.dw + 1;
-    h.ND = (int)cdiv(h.BD, cp.sd);
+    h.ND = ds ? 1 : (int)cdiv(h.BD, cp.sd);
     h.NH = (int)cdiv(h.BH, cp.sh);
     h.NW = (int)cdiv(h.BW, cp.sw);
     h.LH = cp.sh * h.NH;
     h.LW = cp.sw * h.NW;
-    const int64_t bpos = (int64_t)cp.sd * h.ND * h.LH * h.LW;
-    if ((size_t)2 * bpos * kLdc * sizeof(float) > kMaxLds) continue;
+    const int64_t bpos = (int64_t)(ds ? 1 : cp.sd) * h.ND * h.LH * h.LW;
+    if ((size_t)(ds ? 1 : 2) * bpos * kLdc * sizeof(float) > kMaxLds) continue;
     if ((double)cdiv(cp.OD, td) * td * cdiv(cp.OH, th) * th * cdiv(cp.OW, tw) * tw > 2.0 * cp.out_sz)
       continue;
     h.box_pos = (int)bpos;
@@ -399,8 +438,8 @@ bool choose32_wgp(const ConvParams& cp, int wgp, Geo32& hg) {
     if (cp.in_sz >= ((int64_t)1 << 31)) continue;
     h.ntile = (int)ntile;
     h.vec = cp.W % 4 == 0;
-    for (int t = 0; t < cp.taps; ++t) {
-      const int kw = t % cp.KW, kh = (t / cp.KW) % cp.KH, kd = t / (cp.KW * cp.KH);
+    for (int t = 0; t < h.taps2; ++t) {
+      const int kw = t % cp.KW, kh = (t / cp.KW) % cp.KH, kd = ds ? 0 : t / (cp.KW * cp.KH);
       const int ad = kd * cp.dd, ah = kh * cp.dh, aw = kw * cp.dw;
       h.tap_off[t] = (((ad % cp.sd) * h.ND + ad / cp.sd) * h.LH + (ah % cp.sh) * h.NH + ah / cp.sh) * h.LW +
                      (aw % cp.sw) * h.NW + aw / cp.sw;
@@ -452,14 +491,15 @@ int launch_halo32(const Geometry& g, const Plan&, const RunArgs& a) {
     if (rc != FUSEDCONV_OK) return rc;
   }
   const unsigned blocks = (unsigned)((int64_t)hg.ntile * hg.nmb * cp.G);
-  const size_t lds = (size_t)2 * hg.box_pos * kLdc * sizeof(float);
+  const size_t lds = (size_t)(hg.ds ? 1 : 2) * hg.box_pos * kLdc * sizeof(float);
   auto go = [&](auto kfn) -> int {
     if (set_max_dynamic_lds((const void*)kfn, (int)kMaxLds) != FUSEDCONV_OK) return FUSEDCONV_ERR_LAUNCH;
     return launch_conv(kfn, dim3(blocks), dim3(kThreads), lds, a, kEdgeBoth, (const float*)a.x,
                        (const float*)a.ws, (const float*)a.bias, (const float*)a.z,
                        (const float*)a.pre, (float*)a.y, cp, hg);
   };
-  return wgp == 4 ? go(halo32_kernel<4>) : go(halo32_kernel<2>);
+  if (hg.ds) return wgp == 4 ? go(halo32_kernel<4, true>) : go(halo32_kernel<2, true>);
+  return wgp == 4 ? go(halo32_kernel<4, false>) : go(halo32_kernel<2, false>);
 }
 
 }  // namespace fc

@@ -176,8 +176,9 @@ int make_plan(const Geometry& g, int32_t route, int32_t split_req, Plan& p, std:
     case FUSEDCONV_ROUTE_IGEMM_HALO:
       if (g.dtype == FUSEDCONV_F32) {
         if (!halo32_fits(cp, g.dtype, &halo_ws, &th, &tw)) {
-          err = "IGEMM_HALO (fp32) needs at most 64 taps and two input boxes of a 128- or "
-                "256-pixel tile within 64 KB of LDS";
+          err = "IGEMM_HALO (fp32) needs at most 64 taps per box and two input boxes of a "
+                "128- or 256-pixel tile within 64 KB of LDS (3-D: or one box of one input "
+                "depth plane)";
           return FUSEDCONV_ERR_ROUTE;
         }
         p.route = route;

@@ -585,8 +585,8 @@ def test_im2col_route(ci):
 
 
 HALO32_CASES = [
-    # (x, w, attrs) for the fp32 halo kernel (stride 1: strided boxes exceed
-    # its LDS budget): 1-D grouped and dilated, 2-D with asymmetric pads, 3-D,
+    # (x, w, attrs) for the fp32 halo kernel: 1-D grouped and dilated, 2-D
+    # with asymmetric pads, 3-D,
     # channel tails (C/group not a multiple of 16), M/group above 64
     # (128-channel blocks) with a tail, W not a multiple of 4 (element
     # loads), OW not a multiple of 4 (element stores)
@@ -596,6 +596,13 @@ HALO32_CASES = [
     ([1, 16, 4, 16, 16], [24, 16, 1, 3, 3], dict(pads=[0, 1, 1, 0, 1, 1])),
     ([2, 24, 16, 64], [150, 24, 1, 5], dict(pads=[0, 2, 0, 2])),
     ([3, 8, 19, 21], [12, 4, 3, 2], dict(group=2, dilations=[2, 1])),
+    # depth-stepped boxes (3-D, one input depth plane per box): stride 1;
+    # depth stride 2 with asymmetric pads (planes skipped at the borders);
+    # depth dilation 2, stride 2 in-plane, W and OW not multiples of 4
+    ([1, 32, 6, 16, 16], [48, 32, 3, 3, 3], dict(pads=[1] * 6)),
+    ([2, 20, 5, 24, 40], [24, 20, 3, 3, 3], dict(strides=[2, 2, 2], pads=[1, 0, 1, 2, 1, 0])),
+    ([1, 16, 7, 30, 30], [32, 16, 3, 5, 5], dict(strides=[1, 2, 2], dilations=[2, 1, 1],
+                                                 pads=[0, 2, 2, 1, 2, 2])),
 ]
 
 
