@@ -1,4 +1,4 @@
-"""CPU models of three kernels' index schemes, with bounds asserted (no GPU).
+"""CPU models of four kernels' index schemes, with bounds asserted (no GPU).
 
 Each model replays one kernel's addressing in Python -- the same tile plan,
 the same LDS layout, the same per-lane offsets -- with every LDS and buffer
@@ -18,8 +18,18 @@ column or an out-of-range read fails here before any GPU run.
   cut from the three 16-byte pieces around each copy piece, the per-tap
   offsets and the 32-pixel step walk, against the oracle's weight gradient.
 
-The constants below are the kernels' own (kTapCT, kTapLds, kTapRingBytes and
-the 32 KB stage): a change there must change them here.
+* `dwm_kernel` (kernels_dwmfma.hip): the banded-MFMA depthwise plan, the
+  input chunks in the double-buffered LDS planes, the zero-padded Toeplitz
+  table and the lane fragments, the MFMA operand layouts, the fp16 stage and
+  the 16-byte store pieces, against the oracle.
+* `halo32_kernel` in its depth-stepped form (kernels_halo32.hip): the tile
+  and box choice, the loader items of one input depth plane, the phase-split
+  LDS positions and the per-tap offsets, for first, middle and last tiles
+  along every axis, against X itself (zero outside).
+
+The constants below are the kernels' own (kTapCT, kTapLds, kTapRingBytes,
+kMaxLds, kTrow, kLdc and the 32 KB stage): a change there must change them
+here.
 """
 import itertools
 
@@ -405,3 +415,113 @@ def test_dwm_depthwise_index_model(ci):
                 assert a < bufh
                 s += lds[b * bufh + a] * wk[kh, kw]
             assert abs(s - ref[n, m, oh, ow]) <= 1e-12 * max(1.0, abs(s))
+
+
+# ------------------------------------------------- fp32 halo, depth-stepped
+
+H32_LDC, H32_CB, H32_MAX_LDS, H32_MAX_TAPS = 20, 16, 64 * 1024, 64  # kLdc, kCB, kMaxLds, kMaxTaps
+
+H32_DS_CASES = [
+    # (x, w, strides, pads, dilations): 3-D convs whose full-depth box does not fit
+    ([1, 16, 32, 64, 64], [128, 16, 3, 3, 3], [1, 2, 2], [1] * 6, [1, 1, 1]),  # the 3-D workload's planes
+    ([1, 32, 6, 16, 16], [48, 32, 3, 3, 3], [1, 1, 1], [1] * 6, [1, 1, 1]),
+    ([2, 20, 5, 24, 40], [24, 20, 3, 3, 3], [2, 2, 2], [1, 0, 1, 2, 1, 0], [1, 1, 1]),
+    ([1, 16, 7, 30, 30], [32, 16, 3, 5, 5], [1, 2, 2], [0, 2, 2, 1, 2, 2], [2, 1, 1]),
+]
+
+
+def _h32_choose(cp, wgp, ds):
+    """choose32_wgp: tile, box and per-box tap offsets, or None."""
+    cd = lambda a, b: -(-a // b)
+    bn = 64 * wgp
+    order = []
+    for w in (16, 32, 64, 128, 256):
+        if w > bn:
+            break
+        th = bn // w
+        if th > 1 and cp["OH"] == 1 and cp["OD"] == 1:
+            continue
+        order.append((cd(cp["OH"], th) * th * cd(cp["OW"], w) * w / (cp["OH"] * cp["OW"]), -w, w))
+    for _, _, tw in sorted(order):
+        th = bn // tw
+        h = dict(TH=th, TW=tw, taps2=cp["KH"] * cp["KW"] if ds else cp["KD"] * cp["KH"] * cp["KW"])
+        BD = 1 if ds else (cp["KD"] - 1) * cp["dd"] + 1
+        BH = (th - 1) * cp["sh"] + (cp["KH"] - 1) * cp["dh"] + 1
+        BW = (tw - 1) * cp["sw"] + (cp["KW"] - 1) * cp["dw"] + 1
+        h.update(BH=BH, BW=BW, ND=1 if ds else cd(BD, cp["sd"]), NH=cd(BH, cp["sh"]), NW=cd(BW, cp["sw"]))
+        h.update(LH=cp["sh"] * h["NH"], LW=cp["sw"] * h["NW"])
+        bpos = (1 if ds else cp["sd"]) * h["ND"] * h["LH"] * h["LW"]
+        if (1 if ds else 2) * bpos * H32_LDC * 4 > H32_MAX_LDS:
+            continue
+        if cd(cp["OH"], th) * th * cd(cp["OW"], tw) * tw > 2.0 * cp["OH"] * cp["OW"]:
+            continue
+        h["box_pos"] = bpos
+        h["tap_off"] = []
+        for t in range(h["taps2"]):
+            kw, kh, kd = t % cp["KW"], (t // cp["KW"]) % cp["KH"], 0 if ds else t // (cp["KW"] * cp["KH"])
+            ad, ah, aw = kd * cp["dd"], kh * cp["dh"], kw * cp["dw"]
+            h["tap_off"].append((((ad % cp["sd"]) * h["ND"] + ad // cp["sd"]) * h["LH"] + (ah % cp["sh"]) * h["NH"]
+                                 + ah // cp["sh"]) * h["LW"] + (aw % cp["sw"]) * h["NW"] + aw // cp["sw"])
+        return h
+    return None
+
+
+@pytest.mark.parametrize("ci", range(len(H32_DS_CASES)))
+def test_halo32_depth_stepped_index_model(ci):
+    xs, ws, st, pads, dl = H32_DS_CASES[ci]
+    C, D, H, W = xs[1:]
+    M, Cg, KD, KH, KW = ws
+    out, pb = oracle.output_dims([D, H, W], [KD, KH, KW], st, dl, "NOTSET", pads)
+    cp = dict(D=D, H=H, W=W, OD=out[0], OH=out[1], OW=out[2], KD=KD, KH=KH, KW=KW, sd=st[0], sh=st[1],
+              sw=st[2], dd=dl[0], dh=dl[1], dw=dl[2], pd=pb[0], ph=pb[1], pw=pb[2])
+    wgps = [4, 2] if M <= 64 else [2]
+    taps = KD * KH * KW
+    full = None if taps > H32_MAX_TAPS else next((h for g in wgps if (h := _h32_choose(cp, g, False))), None)
+    assert full is None, "every case here needs the depth-stepped form"
+    h = next((h for g in wgps if (h := _h32_choose(cp, g, True))), None)
+    assert h is not None and h["taps2"] <= H32_MAX_TAPS
+    ph = lambda a, s, n: a if s == 1 else (a % s) * n + a // s
+    x = np.random.default_rng([7440, ci]).standard_normal((C, D, H, W))
+    box = h["box_pos"] * H32_LDC
+    tiles_h, tiles_w = -(-cp["OH"] // h["TH"]), -(-cp["OW"] // h["TW"])
+    # first, last and a middle tile along each axis
+    pick = lambda n: sorted({0, n // 2, n - 1})
+    for od0, th_i, tw_i in itertools.product(pick(cp["OD"]), pick(tiles_h), pick(tiles_w)):
+        oh0, ow0 = th_i * h["TH"], tw_i * h["TW"]
+        bh0, bw0, z0 = oh0 * cp["sh"] - cp["ph"], ow0 * cp["sw"] - cp["pw"], od0 * cp["sd"] - cp["pd"]
+        kds = [kd for kd in range(KD) if 0 <= z0 + kd * cp["dd"] < D]   # planes inside the input
+        h_lo, h_hi = max(bh0, 0), min(bh0 + h["BH"], H)
+        w_lo, w_hi = max(bw0, 0), min(bw0 + h["BW"], W)
+        g_lo, g_hi = w_lo >> 2, (w_hi + 3) >> 2
+        nh, ngr = max(h_hi - h_lo, 0), max(g_hi - g_lo, 0)
+        for cb, kd in itertools.product(range(-(-Cg // H32_CB)), kds):
+            idd = z0 + kd * cp["dd"]
+            lds = np.zeros(box)
+            for i in range(4 * nh * ngr):             # loader items: (channel quad, row, 4 columns)
+                cq, r = i & 3, i >> 2
+                gi, hh = r % ngr, r // ngr
+                ih, iw = h_lo + hh, (g_lo + gi) * 4
+                ldst = ph(ih - bh0, cp["sh"], h["NH"]) * h["LW"]
+                for e in range(4):
+                    if w_lo <= iw + e < w_hi:
+                        a = (ldst + ph(iw + e - bw0, cp["sw"], h["NW"])) * H32_LDC + cq * 4
+                        assert a + 4 <= box
+                        c = cb * H32_CB + cq * 4 + np.arange(4)
+                        lds[a:a + 4] = np.where(c < Cg, x[np.minimum(c, Cg - 1), idd, ih, iw + e], 0.0)
+            ncb = min(H32_CB, Cg - cb * H32_CB)
+            for pu in range(h["TH"] * h["TW"]):       # every pixel, every in-plane tap
+                th, tw = divmod(pu, h["TW"])
+                oh, ow = oh0 + th, ow0 + tw
+                if oh >= cp["OH"] or ow >= cp["OW"]:
+                    continue
+                for t2 in range(h["taps2"]):
+                    kw, kh = t2 % KW, t2 // KW
+                    p = th * h["LW"] + tw + h["tap_off"][t2]
+                    assert (p + 1) * H32_LDC <= box
+                    ih, iw = oh * cp["sh"] - cp["ph"] + kh * cp["dh"], ow * cp["sw"] - cp["pw"] + kw * cp["dw"]
+                    got = lds[p * H32_LDC:p * H32_LDC + ncb]
+                    if 0 <= ih < H and 0 <= iw < W:
+                        want = x[cb * H32_CB:cb * H32_CB + ncb, idd, ih, iw]
+                    else:
+                        want = np.zeros(ncb)
+                    assert np.array_equal(got, want), (od0, th_i, tw_i, cb, kd, pu, t2)
