@@ -126,9 +126,11 @@ __global__ __launch_bounds__(256) void repack_frag_kernel(const half_t* __restri
 // NWM 2: two blocks of 6 waves per CU; NWM 4: one block of 10 waves; either way
 // at most 3 waves per SIMD (the launch bound), 168 VGPRs each.
 // Block b -> (pixel tile, channel block).  Blocks are dealt to the 8 XCDs
-// round-robin, so the channel blocks of one pixel tile are placed 8 blocks
-// apart: they run on the same XCD at about the same time and all but the
-// first read X from that XCD's L2.
+// round-robin (block b on XCD b % 8, the b / 8-th there), so XCD x takes a
+// contiguous run of pixel tiles, and each tile's channel blocks back to back:
+// the channel blocks of one tile run on one XCD at about the same time and
+// all but the first read X from its L2, and so do the line pieces that two
+// neighbouring tiles of a channel row share.
 template <int ACT, int PATCH, int NWM>
 __global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t* __restrict__ x,
                                                          const half_t* __restrict__ wf,
@@ -137,8 +139,9 @@ __global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t*
                                                          ConvParams cp, PwTile pt) {
   extern __shared__ __attribute__((aligned(16))) half_t lds[];
   const int b = blockIdx.x;
-  const int mb = (b >> 3) % pt.nmb;
-  const int64_t tg = (int64_t)(b / (8 * pt.nmb)) * 8 + (b & 7);
+  const int64_t jx = b >> 3;  // the block's place in its XCD's sequence
+  const int mb = (int)(jx % pt.nmb);
+  const int64_t tg = (int64_t)(b & 7) * (gridDim.x / (8 * pt.nmb)) + jx / pt.nmb;
   if (tg >= pt.tiles) return;
   const int tile = (int)(tg % pt.ntile);
   const int64_t gn = tg / pt.ntile;       // g * n + image
