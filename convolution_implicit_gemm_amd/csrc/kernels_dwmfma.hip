@@ -208,7 +208,8 @@ void dwm_kernel(const half_t* __restrict__ x, const half_t* __restrict__ w,
   auto load_x = [&](int n, uint4v (&r)[kMaxChunks]) __attribute__((always_inline)) {
     const half_t* xp = xm + (int64_t)n * xstride;
 #pragma unroll
-    for (int kk = 0; kk < kMaxChunks; ++kk) r[kk] = *(const uint4v*)(xp + xoff[kk]);
+    // streamed once: nontemporal (X is not read again by this launch)
+    for (int kk = 0; kk < kMaxChunks; ++kk) r[kk] = __builtin_nontemporal_load((const uint4v*)(xp + xoff[kk]));
   };
   // The input of the next kPre planes is in flight in registers (rotating
   // sets: set s holds the planes i = s mod kPre), which keeps enough bytes in
@@ -287,7 +288,8 @@ void dwm_kernel(const half_t* __restrict__ x, const half_t* __restrict__ w,
       const half_t* sb = stage + (i & 1) * f.stgh;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
-        __builtin_amdgcn_raw_buffer_store_b128(*(const uint4v*)(sb + sof[kk]), yb, gof[kk], 0, 0);
+        // cache policy 2 = nt: Y is streamed out, not re-read (measured 3-5 us faster)
+        __builtin_amdgcn_raw_buffer_store_b128(*(const uint4v*)(sb + sof[kk]), yb, gof[kk], 0, 2);
     };
 
     // plane i's outputs; the input kPre planes past plane i+1 is loaded into
