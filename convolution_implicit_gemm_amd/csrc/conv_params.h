@@ -46,6 +46,11 @@ struct ConvParams {
   // Y = (acc + Z) * act'(P): Z the optional residual gradient, act the
   // activation that produced the convolution's input (no bias).
   int32_t bwd;
+  // 1: the POINTWISE GEMM view of an explicit im2col column matrix, with pixel
+  // tiles over the flattened (image, pixel) axis of n * in_sz entries (in_sz
+  // the padded column row, out_sz the valid pixels of each image), so that
+  // images smaller than a tile fill whole tiles.
+  int32_t flat;
 };
 
 // True when the depth axis is trivial, i.e. the problem is really 1-D or 2-D:

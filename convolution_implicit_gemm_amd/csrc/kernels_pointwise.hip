@@ -144,9 +144,9 @@ __global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t*
   const int64_t tg = (int64_t)(b & 7) * (gridDim.x / (8 * pt.nmb)) + jx / pt.nmb;
   if (tg >= pt.tiles) return;
   const int tile = (int)(tg % pt.ntile);
-  const int64_t gn = tg / pt.ntile;       // g * n + image
-  const int64_t n = gn % cp.n;
-  const int g = (int)(gn / cp.n);
+  const int64_t gn = tg / pt.ntile;       // g * n + image (flat: g)
+  const int64_t n = cp.flat ? 0 : gn % cp.n;
+  const int g = (int)(cp.flat ? gn : gn / cp.n);
   const int64_t P = pt.P;
   const int64_t p0 = (int64_t)tile * kBN;
   constexpr int BM = 64 * NWM;
@@ -225,11 +225,17 @@ __global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t*
       const int it = ptid + 128 * k;
       po[k] = (it & 7) + 8 * ((it >> 4) & 1);
       cq[k] = ((it >> 3) & 1) + 2 * (it >> 5);
-      const int64_t pp = p0 + 8 * po[k];
+      int64_t pp = p0 + 8 * po[k];
       // P (and OW for a patch conv) % 8 == 0, or the padded rows of an
       // im2col column matrix: an octet is all in or all out of X
       pix_ok[k] = pp < P;
-      const half_t* img = x + (n * cp.C + (int64_t)g * cp.Cg) * cp.in_sz;
+      int64_t nx = n;
+      if (cp.flat) {  // octet of image pp / in_sz (in_sz % 8 == 0: never split)
+        nx = pp / cp.in_sz;
+        pp -= nx * cp.in_sz;
+        pix_ok[k] = nx < cp.n;  // the row padding past P reads the zero columns
+      }
+      const half_t* img = x + (nx * cp.C + (int64_t)g * cp.Cg) * cp.in_sz;
       if constexpr (PATCH != 2) {
         xs[k] = img + pp;
       } else {  // first input column of the octet's 2x2 patches in input row 2*oh
@@ -343,8 +349,15 @@ __global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t*
   float* stage = (float*)lds + wave * 16 * RP;
   const int mw0 = m0 + wmi * 64;  // first channel of this wave
   const int p4 = (lane & 15) * 4, rsub = lane >> 4;
-  const int64_t pg = p0 + wpi * 64 + p4;  // image pixel of this lane
-  const bool pok = pg < P;
+  int64_t pg = p0 + wpi * 64 + p4;  // image pixel of this lane
+  bool pok = pg < P;
+  int64_t imgoff = 0;  // flat: the offset of the lane's image in Y and Z
+  if (cp.flat) {       // (in_sz and P multiples of 4: a 4-pixel group is never split)
+    const int64_t nq = pg / cp.in_sz;
+    pg -= nq * cp.in_sz;
+    pok = nq < cp.n && pg < P;
+    imgoff = nq * cp.M * P;
+  }
   int64_t wbase = (n * cp.M + (int64_t)g * cp.Mg + mw0) * P;
   // transposed form: lane (pr, ah) owns input pixels 2pr, 2pr+1 of the
   // wave's 64 and output row phase a = ah; iteration it of block j is output
@@ -369,7 +382,7 @@ __global__ __launch_bounds__(64 * (2 * NWM + 2), 3) void pw_kernel(const half_t*
       return (pok2 && mo0 + cm < mg_out) ? (unsigned)((cm * cp.out_sz + obase) * 2) : kOff;
     }
     const int r = j * 16 + it * 4 + rsub;  // channel relative to mw0
-    return (pok && mw0 + r < cp.Mg) ? (unsigned)((r * P + pg) * 2) : kOff;
+    return (pok && mw0 + r < cp.Mg) ? (unsigned)((imgoff + r * P + pg) * 2) : kOff;
   };
   uint2v zr[4][4];
 #pragma unroll
@@ -453,13 +466,16 @@ bool choose(const ConvParams& cp, int32_t dtype, PwTile& pt) {
   // epilogue offsets: 64 channel planes of one image (16 planes of 4P
   // outputs for the transposed form) in 31-bit byte offsets
   if (pt.P * 64 * 2 * (tr ? 2 : 1) >= ((int64_t)1 << 31)) return false;
+  // flat pixel axis: a 1x1 GEMM over padded column rows; Y offsets then span
+  // every image (n * M * P outputs) in 31-bit byte offsets
+  if (cp.flat && (patch != 1 || cp.n * cp.M * pt.P * 2 >= ((int64_t)1 << 31))) return false;
   const int64_t mg = tr ? 4 * (int64_t)cp.Mg : cp.Mg;  // GEMM columns per group
   if (mg >= ((int64_t)1 << 30)) return false;
-  pt.ntile = (int)cdiv(pt.P, kBN);
+  pt.ntile = (int)cdiv(cp.flat ? cp.n * cp.in_sz : pt.P, kBN);
   pt.nwm = mg > 128 ? 4 : 2;
   pt.nmb = (int)cdiv(mg, 64 * pt.nwm);
   pt.ks = (int)cdiv(pt.kp, kBK);
-  pt.tiles = (int64_t)cp.G * cp.n * pt.ntile;
+  pt.tiles = (int64_t)cp.G * (cp.flat ? 1 : cp.n) * pt.ntile;
   const int64_t blocks = cdiv(pt.tiles, 8) * 8 * pt.nmb;
   return blocks < ((int64_t)1 << 31);
 }

@@ -1,4 +1,4 @@
-"""CPU models of four kernels' index schemes, with bounds asserted (no GPU).
+"""CPU models of five kernels' index schemes, with bounds asserted (no GPU).
 
 Each model replays one kernel's addressing in Python -- the same tile plan,
 the same LDS layout, the same per-lane offsets -- with every LDS and buffer
@@ -26,6 +26,10 @@ column or an out-of-range read fails here before any GPU run.
   and box choice, the loader items of one input depth plane, the phase-split
   LDS positions and the per-tap offsets, for first, middle and last tiles
   along every axis, against X itself (zero outside).
+* `pw_kernel` over a flat pixel axis (kernels_pointwise.hip, the explicit
+  im2col route's GEMM): pixel tiles over all images' padded column rows, the
+  producer's per-octet image split and the epilogue's per-group image offset,
+  against the column-matrix product.
 
 The constants below are the kernels' own (kTapCT, kTapLds, kTapRingBytes,
 kMaxLds, kTrow, kLdc and the 32 KB stage): a change there must change them
@@ -525,3 +529,62 @@ def test_halo32_depth_stepped_index_model(ci):
                     else:
                         want = np.zeros(ncb)
                     assert np.array_equal(got, want), (od0, th_i, tw_i, cb, kd, pu, t2)
+
+
+# ------------------------------------------- pointwise GEMM, flat pixel axis
+
+PW_BN, PW_BK = 128, 64       # kBN, kBK
+
+PW_FLAT_CASES = [
+    # (n, G, Kp, P, M): column matrices of the explicit im2col route
+    (256, 1, 16, 196, 64),     # the SigLIP patch embedding's pixel geometry (256 images of
+                               # a 14 x 14 grid; fewer channels, the same tiles and offsets)
+    (3, 2, 48, 36, 40),        # groups, P % 8 != 0 (padded rows), M not a multiple of 64
+    (5, 1, 112, 1024, 64),     # P a multiple of the tile: tiles end on image boundaries
+    (7, 1, 16, 4, 16),         # tiny images: many images per tile
+]
+
+
+@pytest.mark.parametrize("ci", range(len(PW_FLAT_CASES)))
+def test_pointwise_flat_axis_index_model(ci):
+    n, G, Kp, P, M = PW_FLAT_CASES[ci]
+    Mg = M // G
+    Pp = -(-P // 8) * 8                       # column row pitch (in_sz of the GEMM view)
+    assert P % 4 == 0 and Pp % 8 == 0 and n * M * P * 2 < (1 << 31)
+    ntile = -(-(n * Pp) // PW_BN)
+    rng = np.random.default_rng([7460, ci])
+    col = np.zeros((n, G, Kp, Pp))
+    col[..., :P] = rng.standard_normal((n, G, Kp, P))   # padding columns are zeros
+    w = rng.standard_normal((G, Mg, Kp))
+    flat = col.reshape(-1)
+    y = np.full(n * M * P, np.nan)
+    writes = np.zeros(n * M * P, dtype=int)
+    for g, tile in itertools.product(range(G), range(ntile)):
+        p0 = tile * PW_BN
+        # producer: 32 pixel octets of the tile, each from one image's column row
+        a = np.zeros((Kp, PW_BN))
+        for po in range(PW_BN // 8):
+            pp = p0 + 8 * po
+            nx, pin = divmod(pp, Pp)
+            if nx >= n:
+                continue                           # pix_ok false: written as zeros
+            assert pin + 8 <= Pp                   # an octet never leaves its row
+            off = ((nx * G + g) * Kp + np.arange(Kp)) * Pp + pin   # channel rows c
+            assert off[-1] + 8 <= flat.size
+            a[:, 8 * po:8 * po + 8] = flat[off[:, None] + np.arange(8)]
+        acc = w[g] @ a                             # [Mg, 128]
+        # epilogue: 4-pixel groups, offsets relative to y + (g*Mg + m)*P
+        for q4 in range(PW_BN // 4):
+            pg = p0 + 4 * q4
+            nq, pin = divmod(pg, Pp)
+            if not (nq < n and pin < P):
+                continue                           # kOff: dropped
+            assert pin + 4 <= P                    # a group is never split
+            off = nq * M * P + (g * Mg + np.arange(Mg)) * P + pin      # channels m
+            assert off[-1] + 4 <= y.size
+            idx = off[:, None] + np.arange(4)
+            y[idx] = acc[:, 4 * q4:4 * q4 + 4]
+            np.add.at(writes, idx, 1)
+    assert (writes == 1).all(), "every output written exactly once"
+    ref = np.einsum("gmk,ngkp->ngmp", w, col[..., :P]).reshape(-1)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
