@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __rest
                                                              const float* z, const float* pre,
                                                              float* y, ConvParams cp, Geo32 hg) {
   constexpr int WGM = 4 / WGP;
-  constexpr int BN = 64 * WGP, BM = 64 * WGM;
+  constexpr int BM = 64 * WGM;  // the block's channels (its pixels: 64 * WGP)
   extern __shared__ __attribute__((aligned(16))) float lds32[];
   const int box = hg.box_pos * kLdc;  // floats per box
 
