@@ -279,24 +279,45 @@ __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __rest
     for (int j = 0; j < 4; ++j) v[j] = *(const float4v*)(wg + off + wl + j * 16 * kCB);
   };
   load_w(nsteps > 0 ? woff(0) : 0, wa);
+  // lane t holds the LDS row offset of tap t: a step takes its tap's offset
+  // with a lane read instead of a scalar memory load (whose wait would also
+  // wait for the operand reads in flight)
+  int toff_v = 0;
+  for (int t = 0; t < taps2; ++t)
+    if (lane == t) toff_v = hg.tap_off[t];
+  auto tap_base = [&](int bi, int t2) __attribute__((always_inline)) {
+    return lds32 + (DS ? 0 : (bi & 1) * box) + __builtin_amdgcn_readlane(toff_v, t2) * kLdc + q * 4;
+  };
   lds_barrier();
 
+  // a[i]: this lane's operand (4 channels of one pixel) of pixel tile i for
+  // the current step; each is re-read for the next step as soon as the 16
+  // products that use it are issued, so the reads land under the step's
+  // remaining products
+  float4v a[4];
+  if (nsteps > 0) {
+    const float* xb = tap_base(0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *(const float4v*)(xb + apos[i] * kLdc);
+  }
   auto step = [&](int s, const float4v* wc, float4v* wn) __attribute__((always_inline)) {
     const int bi = s / taps2, t2 = s - bi * taps2;
     // the next step's weights (past the last step: the first tile again)
     load_w(s + 1 < nsteps ? woff(s + 1) : 0, wn);
+    // the next step's operands, from this box (at the box's last tap these
+    // reads of its first tap are discarded and re-read from the next box)
+    const float* xn = tap_base(bi, t2 + 1 == taps2 ? 0 : t2 + 1);
     __builtin_amdgcn_sched_barrier(0);
-    const float* xb = lds32 + (DS ? 0 : (bi & 1) * box) + hg.tap_off[t2] * kLdc + q * 4;
-    float4v a[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *(const float4v*)(xb + apos[i] * kLdc);
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][e], wc[j][e], acc[i][j], 0, 0, 0);
+      a[i] = *(const float4v*)(xn + apos[i] * kLdc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (t2 + 1 == taps2 && bi + 1 < nbox) {
       // the next box (held in registers) into the other buffer, whose
       // previous readers (box bi - 1) all passed the last barrier; with one
@@ -305,6 +326,9 @@ __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __rest
       store_box(DS ? 0 : (bi + 1) & 1, bi + 1);
       lds_barrier();
       if (bi + 2 < nbox) prefetch_box(bi + 2);
+      const float* xb = tap_base(bi + 1, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *(const float4v*)(xb + apos[i] * kLdc);
     }
   };
   int s = 0;
@@ -323,12 +347,27 @@ __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __rest
   // ---- epilogue: lane holds pixels 4q .. 4q+3 of pixel tile i (consecutive
   // columns of one tile row) for channel m0 + wmi*64 + 16j + r16
   const bool vec_y = (cp.OW & 3) == 0;
+  // bias is in the accumulator; the residual, then the activation (or, for an
+  // input gradient, the derivative of the producer's activation)
+  auto finish4 = [&](float4v v, int64_t yi) __attribute__((always_inline)) {
+    if (cp.has_z) v += *(const float4v*)(z + yi);
+    if (cp.bwd) {
+      if (cp.act != ACT_NONE) {
+        const float4v pv = *(const float4v*)(pre + yi);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+        for (int e = 0; e < 4; ++e) v[e] *= dact_apply(cp.act, pv[e], cp.alpha, cp.beta);
+      }
+    } else {
+      v = act_apply4(cp.act, v, cp.alpha, cp.beta);
+    }
+    return v;
+  };
+  // one pixel tile, lane by lane (image edges, widths not a multiple of 4)
+  auto store_tile = [&](int i) __attribute__((always_inline)) {
     const int pu = wpi * 64 + i * 16 + q * 4;
     const int tw = pu & (hg.TW - 1), th = (pu >> hg.ltw) & (hg.TH - 1), td = pu >> (hg.ltw + hg.lth);
     const int od = od0 + td, oh = oh0 + th, ow = ow0 + tw;
-    if (od >= cp.OD || oh >= cp.OH || ow >= cp.OW) continue;
+    if (od >= cp.OD || oh >= cp.OH || ow >= cp.OW) return;
     const int nv = min(4, cp.OW - ow);
     const int64_t pix = ((int64_t)od * cp.OH + oh) * cp.OW + ow;
 #pragma unroll
@@ -338,17 +377,7 @@ __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __rest
       const int64_t yi = (n * cp.M + (int64_t)g * cp.Mg + m) * cp.out_sz + pix;
       float4v v = acc[i][j];
       if (vec_y && nv == 4) {
-        if (cp.has_z) v += *(const float4v*)(z + yi);
-        if (cp.bwd) {
-          if (cp.act != ACT_NONE) {
-            const float4v pv = *(const float4v*)(pre + yi);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] *= dact_apply(cp.act, pv[e], cp.alpha, cp.beta);
-          }
-        } else {
-          v = act_apply4(cp.act, v, cp.alpha, cp.beta);
-        }
-        *(float4v*)(y + yi) = v;
+        *(float4v*)(y + yi) = finish4(v, yi);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -363,6 +392,56 @@ __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __rest
           y[yi + e] = u;
         }
       }
+    }
+  };
+  // Tiles 2k and 2k+1 are 32 consecutive pixels of one tile row when TW >= 32.
+  // There a store covers whole 128-byte lines: lanes r16 < 8 of each 16-lane
+  // row (one q) swap their tile-2k values of channels r16 + 8 for the
+  // tile-(2k+1) values of channels r16 held by lanes r16 + 8 (row shifts by 8
+  // lanes), so store A writes channels 0 .. 7 of the 16-channel tile and store
+  // B channels 8 .. 15, each over all 32 pixels.
+  auto lanes_down8 = [](float4v v) __attribute__((always_inline)) {  // lane r16 takes lane r16 - 8
+    float4v r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      r[e] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v[e]), 0x118, 0xF, 0xF, true));
+    return r;
+  };
+  auto lanes_up8 = [](float4v v) __attribute__((always_inline)) {  // lane r16 takes lane r16 + 8
+    float4v r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      r[e] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v[e]), 0x108, 0xF, 0xF, true));
+    return r;
+  };
+#pragma unroll
+  for (int ip = 0; ip < 4; ip += 2) {
+    // the pair's first pixel (the same for every lane of the wave)
+    const int pu0 = wpi * 64 + ip * 16;
+    const int tw0 = pu0 & (hg.TW - 1), th0 = (pu0 >> hg.ltw) & (hg.TH - 1),
+              td0 = pu0 >> (hg.ltw + hg.lth);
+    const int od = od0 + td0, oh = oh0 + th0, ow = ow0 + tw0;
+    if (!(vec_y && hg.TW >= 32 && od < cp.OD && oh < cp.OH && ow + 32 <= cp.OW)) {
+      store_tile(ip);
+      store_tile(ip + 1);
+      continue;
+    }
+    const int64_t ybase = (n * cp.M + (int64_t)g * cp.Mg) * cp.out_sz + ((int64_t)od * cp.OH + oh) * cp.OW + ow;
+    const bool lo = r16 < 8;
+    const int px = lo ? 4 * q : 16 + 4 * q;  // pixel offset of both stores
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int mrow = m0 + wmi * 64 + j * 16;  // the 16-channel tile's first channel
+      float4v v0 = acc[ip][j], v1 = acc[ip + 1][j];
+      if (mrow + r16 < cp.Mg) {
+        const int64_t yi = ybase + (int64_t)(mrow + r16) * cp.out_sz + 4 * q;
+        v0 = finish4(v0, yi);
+        v1 = finish4(v1, yi + 16);
+      }
+      const float4v from_lo = lanes_down8(v1), from_hi = lanes_up8(v0);
+      const int ca = mrow + (lo ? r16 : r16 - 8), cb = mrow + (lo ? r16 + 8 : r16);
+      if (ca < cp.Mg) *(float4v*)(y + ybase + (int64_t)ca * cp.out_sz + px) = lo ? v0 : from_lo;
+      if (cb < cp.Mg) *(float4v*)(y + ybase + (int64_t)cb * cp.out_sz + px) = lo ? from_hi : v1;
     }
   }
 }

@@ -25,7 +25,9 @@ column or an out-of-range read fails here before any GPU run.
 * `halo32_kernel` in its depth-stepped form (kernels_halo32.hip): the tile
   and box choice, the loader items of one input depth plane, the phase-split
   LDS positions and the per-tap offsets, for first, middle and last tiles
-  along every axis, against X itself (zero outside).
+  along every axis, against X itself (zero outside); and its epilogue's
+  paired whole-line stores (two pixel tiles exchanged by 8-lane row shifts),
+  every output written once with its own value.
 * `pw_kernel` over a flat pixel axis (kernels_pointwise.hip, the explicit
   im2col route's GEMM): pixel tiles over all images' padded column rows, the
   producer's per-octet image split and the epilogue's per-group image offset,
@@ -529,6 +531,114 @@ def test_halo32_depth_stepped_index_model(ci):
                     else:
                         want = np.zeros(ncb)
                     assert np.array_equal(got, want), (od0, th_i, tw_i, cb, kd, pu, t2)
+
+
+H32_STORE_CASES = [
+    # (WGP, TW, TH, OD, OH, OW, Mg, M-block count): output tiles of the fp32 halo kernel
+    (4, 256, 1, 1, 1, 4096, 64, 1),    # the 1-D conv's 256-pixel rows (every pair whole)
+    (2, 32, 4, 5, 32, 32, 128, 1),     # the 3-D conv's 4 x 32 tiles
+    (4, 64, 4, 1, 30, 56, 40, 2),      # last tile column 8 wide (pairs cut), Mg < the tile's rows
+    (2, 16, 8, 2, 9, 20, 100, 1),      # TW = 16: tiles 2k, 2k+1 are different rows (no pairing)
+    (4, 128, 2, 1, 3, 130, 70, 2),     # OW % 4 != 0: the lane-by-lane path throughout
+]
+
+
+@pytest.mark.parametrize("ci", range(len(H32_STORE_CASES)))
+def test_halo32_paired_store_index_model(ci):
+    """The fp32 halo kernel's epilogue: lane (r16, q) of wave (wpi, wmi) holds
+    pixels 4q .. 4q+3 of pixel tile i for channel m0 + 64*wmi + 16j + r16.
+    Where tiles 2k and 2k+1 form 32 whole pixels of one row, the row shifts by
+    8 lanes (row_shr / row_shl of a 16-lane DPP row) pair them and store A
+    (channels +0 .. 7) and store B (+8 .. 15) each write whole 128-byte lines;
+    elsewhere every lane stores its own values.  Every output of the block must
+    be written exactly once, with the value computed for that channel and
+    pixel, and nothing outside the output."""
+    WGP, TW, TH, OD, OH, OW, Mg, nmb = H32_STORE_CASES[ci]
+    WGM, BM = 4 // WGP, 64 * (4 // WGP)
+    TD = 1
+    assert TW * TH == 64 * WGP
+    ltw, lth = TW.bit_length() - 1, TH.bit_length() - 1
+    out_sz = OD * OH * OW
+    vec_y = OW % 4 == 0
+    tiles = [(od0, oh0, ow0) for od0 in range(0, OD, TD) for oh0 in range(0, OH, TH) for ow0 in range(0, OW, TW)]
+    for mb, (od0, oh0, ow0) in itertools.product(range(nmb), tiles):
+        m0 = mb * BM
+        written = {}
+
+        def put(m, pix, val, where):
+            assert 0 <= m < Mg and 0 <= pix < out_sz, where
+            assert (m, pix) not in written, where
+            written[(m, pix)] = val
+
+        def pixel_of(pu):
+            tw, th, td = pu & (TW - 1), (pu >> ltw) & (TH - 1), pu >> (ltw + lth)
+            return od0 + td, oh0 + th, ow0 + tw
+
+        for wave in range(4):
+            wpi, wmi = wave % WGP, wave // WGP
+            # acc[i][j][lane] -> the (channel, pixel) its 4 values belong to (value e: pixel + e)
+            def acc(i, j, r16, q):
+                pu = wpi * 64 + i * 16 + q * 4
+                d, hh, w = pixel_of(pu)
+                return (m0 + wmi * 64 + j * 16 + r16, (d * OH + hh) * OW + w)
+
+            def store_tile(i):
+                for r16, q in itertools.product(range(16), range(4)):
+                    d, hh, w = pixel_of(wpi * 64 + i * 16 + q * 4)
+                    if d >= OD or hh >= OH or w >= OW:
+                        continue
+                    nv = min(4, OW - w)
+                    for j in range(4):
+                        m, pix = acc(i, j, r16, q)
+                        if m >= Mg:
+                            continue
+                        for e in range(4 if vec_y and nv == 4 else nv):
+                            put(m, pix + e, (m, pix + e), ("tile", wave, i, j, r16, q))
+
+            for ip in (0, 2):
+                d, hh, w = pixel_of(wpi * 64 + ip * 16)
+                if not (vec_y and TW >= 32 and d < OD and hh < OH and w + 32 <= OW):
+                    store_tile(ip)
+                    store_tile(ip + 1)
+                    continue
+                base = (d * OH + hh) * OW + w
+                for j in range(4):
+                    mrow = m0 + wmi * 64 + j * 16
+                    pieces = {"A": [], "B": []}        # 16-byte pieces of each store instruction
+                    for q in range(4):                 # one 16-lane DPP row per q
+                        v0 = [acc(ip, j, r, q) for r in range(16)]
+                        v1 = [acc(ip + 1, j, r, q) for r in range(16)]
+                        down = [v1[r - 8] if r >= 8 else None for r in range(16)]   # row_shr:8
+                        up = [v0[r + 8] if r < 8 else None for r in range(16)]      # row_shl:8
+                        for r16 in range(16):
+                            lo = r16 < 8
+                            px = 4 * q if lo else 16 + 4 * q
+                            for name, ch, val in (("A", mrow + (r16 if lo else r16 - 8), v0[r16] if lo else down[r16]),
+                                                  ("B", mrow + (r16 + 8 if lo else r16), up[r16] if lo else v1[r16])):
+                                if ch >= Mg:
+                                    continue
+                                pix = base + px
+                                assert val == (ch, pix), (name, wave, ip, j, r16, q)
+                                for e in range(4):
+                                    put(ch, pix + e, (ch, pix + e), (name, wave, ip, j, r16, q))
+                                pieces[name].append(ch * out_sz + pix)
+                    # where the pair starts on a 128-byte boundary, each instruction's pieces
+                    # make up whole lines: 8 pieces of 4 floats in every line it touches
+                    if base % 32 == 0 and out_sz % 32 == 0:
+                        for name in ("A", "B"):
+                            per_line = {}
+                            for a in pieces[name]:
+                                per_line.setdefault(a // 32, set()).add(a % 32)
+                            assert all(v == set(range(0, 32, 4)) for v in per_line.values()), (name, j)
+        # exactly the block's outputs: channels m0 .. m0 + BM (below Mg), pixels of the tile
+        want = set()
+        for pu in range(64 * WGP):
+            d, hh, w = pixel_of(pu)
+            if d < OD and hh < OH and w < OW:
+                for m in range(m0, min(m0 + BM, Mg)):
+                    want.add((m, (d * OH + hh) * OW + w))
+        assert set(written) == want
+        assert all(v == k for k, v in written.items())
 
 
 # ------------------------------------------- pointwise GEMM, flat pixel axis
