@@ -140,7 +140,8 @@ __device__ __forceinline__ SUnit decode_unit(int u, const ConvParams& cp, const 
   return r;
 }
 
-// Persistent blocks: block b takes units b, b + gridDim.x, ... (nu of them).
+// Persistent blocks: block b takes units f, f + gridDim.x, ... (nu of them),
+// f a permutation of b (below).
 // Box buffers rotate over kBoxBufs = 3: in interval t (t = 0 .. nu, one
 // barrier at its end) the MFMA waves compute unit t from box buffer t % 3
 // into stage buffer t & 1, the producers fill box buffer (t+2) % 3 with unit
@@ -174,7 +175,13 @@ __global__ __launch_bounds__(kThreads, 1) void smallc_kernel(const half_t* __res
   // Phi table (erf-form Gelu and Erf): (Phi_i, Phi_{i+1} - Phi_i) pairs
   float2* const phi = (float2*)(stage0 + 2 * kBM * kSP);
   constexpr bool kPhiAct = ACT == ACT_GELU || ACT == ACT_ERF;
-  const int first = blockIdx.x;
+  // Block b runs on XCD b % 8.  With a grid of 8k blocks, interval t's units
+  // tB .. tB + B - 1 are dealt so that XCD x takes the k consecutive units
+  // tB + kx .. tB + kx + k - 1: neighbouring tiles of one image, whose boxes
+  // share input rows and columns, run on one XCD at about the same time and
+  // read the shared lines from its L2 rather than from HBM once per XCD.
+  const int first = (gridDim.x & 7) == 0 ? (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3))
+                                         : (int)blockIdx.x;
   const int nu = first < nunits ? (nunits - 1 - first) / (int)gridDim.x + 1 : 0;
   auto unit_of = [&](int t) __attribute__((always_inline)) {
     return decode_unit(first + t * (int)gridDim.x, cp, st);
