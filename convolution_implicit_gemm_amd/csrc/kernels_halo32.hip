@@ -101,10 +101,19 @@ __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __rest
   extern __shared__ __attribute__((aligned(16))) float lds32[];
   const int box = hg.box_pos * kLdc;  // floats per box
 
-  // ---- block -> (group, m block, tile)
+  // ---- block -> (group, m block, tile).  Block b runs on XCD b % 8.  With
+  // full-depth boxes, in each whole chunk of 256 block ids XCD x takes the 32
+  // consecutive work units 32x .. 32x + 31 of the chunk, so neighbouring
+  // tiles, whose boxes share halo columns and rows, run on one XCD at about
+  // the same time and read the shared lines from its L2.  Depth-stepped
+  // tiles keep the plain order: the tiles of neighbouring output depths,
+  // which read the same input planes, are tiles_h * tiles_w ids apart, on one
+  // XCD when that is a multiple of 8.
+  int bid = blockIdx.x;
+  if (!DS && bid < (int)(gridDim.x & ~255u)) bid = (bid & ~255) + (bid & 7) * 32 + ((bid & 255) >> 3);
   const int per_g = hg.ntile * hg.nmb;
-  const int g = blockIdx.x / per_g;
-  int rb = blockIdx.x - g * per_g;
+  const int g = bid / per_g;
+  int rb = bid - g * per_g;
   const int mb = rb % hg.nmb;
   int tile = rb / hg.nmb;
   const int tw_i = tile % hg.tiles_w;
