@@ -163,7 +163,10 @@ __global__ __launch_bounds__(kThreads, 2) void halo32_kernel(const float* __rest
   const int nd = max(d_hi - d_lo, 0), nh = max(h_hi - h_lo, 0), ngr = max(g_hi - g_lo, 0);
   const int nitems = 4 * nd * nh * ngr;
   const float* ximg = x + (n * cp.C + (int64_t)g * cp.Cg) * cp.in_sz;
-  constexpr int PF = 2;  // items per thread held across a box
+  // items per thread held across a box: a depth plane of the 3-D conv's
+  // 4 x 32 tile has 612 (3 per thread, 247 VGPRs, so none is loaded at the
+  // box switch); a full-depth box holds 2 (a 256-pixel 1-D row box has 280)
+  constexpr int PF = DS ? 3 : 2;
   struct Item { int goff, ldst, cq, mask, aw0; };
   auto decode = [&](int i) __attribute__((always_inline)) {
     Item it;
