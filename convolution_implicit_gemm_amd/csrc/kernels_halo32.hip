@@ -14,9 +14,10 @@
 //   * the weights, repacked tap-major as Wp[g][tap][channel block][m][16]
 //     (fusedconv_prepare_weights or at the start of every run), go straight
 //     into registers one (channel block, tap) step ahead;
-//   * bias seeds the accumulators; Z, the activation and the store follow
-//     per lane: 4 consecutive pixels of one output channel, one 16-byte
-//     store where the row allows.
+//   * bias seeds the accumulators; Z and the activation follow per lane (4
+//     consecutive pixels of one output channel), and where two pixel tiles
+//     make 32 whole pixels of a row, lanes 8 apart swap halves so that each
+//     store instruction writes whole 128-byte lines.
 // The per-element im2col gather of the IGEMM route, whose loads wait at the
 // joins of their bounds tests, is gone: X is read once per channel block as
 // whole 16-byte rows of the box.
