@@ -55,12 +55,47 @@ def run_gpu(x, w, b, z, **kw):
     return y.cpu().numpy()
 
 
+class Ref(np.ndarray):
+    """The oracle's Y with `alt`: where not NaN, a second value an output
+    may take (see reference())."""
+    alt = None
+
+
+def reference(x, w, b, z, **attrs):
+    """oracle.fusedconv(x, w, b, z, **attrs), and for ThresholdedRelu the
+    outputs whose decision x > alpha is not fixed by the kernels' precision.
+    The kernels decide on an fp32 sum; recursive fp32 summation of K products
+    plus bias and residual is within 2 (K + 2) 2^-24 sum|terms| of the exact
+    value, and sum|terms| is the oracle run on |X|, |W|, |B|, |Z|.  Where the
+    float64 pre-activation lies within that bound of alpha, both 0 and the
+    pre-activation are correct outputs."""
+    ref = oracle.fusedconv(x, w, b, z, **attrs)
+    if attrs.get("activation") != "ThresholdedRelu":
+        return ref
+    p = attrs.get("activation_params")
+    alpha = float(p[0]) if p else 1.0
+    base = dict(attrs, activation=None, activation_params=None)
+    pre = oracle.fusedconv(x, w, b, z, **base)
+    ab = lambda a: None if a is None else np.abs(a)
+    mag = oracle.fusedconv(np.abs(x), np.abs(w), ab(b), ab(z), **base)
+    k = int(np.prod(w.shape[1:]))
+    near = np.abs(pre - alpha) <= 2.0 * (k + 2) * 2.0 ** -24 * mag
+    out = np.asarray(ref).view(Ref)
+    out.alt = np.where(near, np.where(pre > alpha, 0.0, pre), np.nan)
+    return out
+
+
 def check(got, ref, dtype, what):
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     g = got.astype(np.float64)
     assert np.all(np.isfinite(g)), what
-    scale = max(np.max(np.abs(ref)), 1e-30)
-    err = np.max(np.abs(g - ref)) / scale
+    ref_ = np.asarray(ref)
+    scale = max(np.max(np.abs(ref_)), 1e-30)
+    d = np.abs(g - ref_)
+    alt = getattr(ref, "alt", None)
+    if alt is not None:  # either side of a ThresholdedRelu decision the kernels' sum leaves open
+        d = np.where(np.isnan(alt), d, np.minimum(d, np.abs(g - np.nan_to_num(alt))))
+    err = np.max(d) / scale
     assert err <= TAU[dtype], f"{what}: rel err {err:.3e} > {TAU[dtype]}"
     return err
 
@@ -95,7 +130,7 @@ def run_case(c, dtype, seed, route, split_k=0, act=(None, None), bias=True, resi
     what = f"seed={seed} route={route} split={split_k} dtype={dtype} x={x_shape} w={w_shape} {attrs}"
     log("CASE " + what)
     got = run_gpu(x, w, b, z, route=route, split_k=split_k, **attrs)
-    ref = oracle.fusedconv(x, w, b, z, **attrs)
+    ref = reference(x, w, b, z, **attrs)
     return check(got, ref, dtype, what)
 
 
@@ -182,7 +217,7 @@ def test_depthwise_fast_path(ci):
         a = dict(attrs, activation=act, activation_params=f32params(params))
         log(f"CASE dw fast {ci} x={xs} w={ws} {a}")
         got = run_gpu(x, w, b, z, route="depthwise", **a)
-        ref = oracle.fusedconv(x, w, b, z, **a)
+        ref = reference(x, w, b, z, **a)
         check(got, ref, "f16", f"dw fast case {ci}")
 
 
@@ -199,7 +234,7 @@ def test_depthwise_fast_path_parametrised_activations(act):
     x, w, b, z = random_tensors([9210, len(act[0])], "f16", xs, ws, [5], xs, dist="normal")
     log(f"CASE dw fast {act[0]} x={xs} w={ws}")
     got = run_gpu(x, w, b, z, route="depthwise", **attrs)
-    ref = oracle.fusedconv(x, w, b, z, **attrs)
+    ref = reference(x, w, b, z, **attrs)
     check(got, ref, "f16", f"dw fast {act[0]}")
 
 
@@ -235,7 +270,7 @@ def test_depthwise_mfma_path(ci):
         a = dict(attrs, activation=act, activation_params=f32params(params))
         log(f"CASE dw mfma {ci} x={xs} w={ws} {a}")
         got = run_gpu(x, w, b, z, route="depthwise", **a)
-        ref = oracle.fusedconv(x, w, b, z, **a)
+        ref = reference(x, w, b, z, **a)
         check(got, ref, "f16", f"dw mfma case {ci}")
 
 
@@ -248,7 +283,7 @@ def test_depthwise_mfma_many_images_per_block():
     x, w, b, z = random_tensors([9310], "f16", xs, ws, [2048], h.y_shape, dist="normal")
     log(f"CASE dw mfma many images x={xs}")
     got = run_gpu(x, w, b, z, route="depthwise", **attrs)
-    ref = oracle.fusedconv(x, w, b, z, **attrs)
+    ref = reference(x, w, b, z, **attrs)
     check(got, ref, "f16", "dw mfma many images")
 
 
@@ -264,7 +299,7 @@ def test_depthwise_mfma_nonfinite_input_stays_local():
     x[1, 2, 3, 4] = -np.inf
     log("CASE dw mfma non-finite")
     got = run_gpu(x, w, b, None, route="depthwise", **attrs).astype(np.float64)
-    ref = oracle.fusedconv(x, w, b, None, **attrs)
+    ref = reference(x, w, b, None, **attrs)
     fin = np.isfinite(ref)
     assert (~fin).sum() == 2 * 25
     assert np.array_equal(np.isfinite(got), fin)
@@ -286,7 +321,7 @@ def test_depthwise_mfma_nonfinite_across_channels():
     x[1, 1499, 7, 15] = -np.inf
     log("CASE dw mfma non-finite across channels")
     got = run_gpu(x, w, b, z, route="depthwise", **attrs).astype(np.float64)
-    ref = oracle.fusedconv(x, w, b, z, **attrs)
+    ref = reference(x, w, b, z, **attrs)
     fin = np.isfinite(ref)
     assert (~fin).sum() > 0
     assert np.array_equal(np.isfinite(got), fin)
@@ -327,7 +362,7 @@ def test_halo_route(ci):
         a = dict(attrs, activation=act, activation_params=f32params(params))
         log(f"CASE halo {ci} x={xs} w={ws} {a} bias={bias} z={resid}")
         got = run_gpu(x, w, b, z, route="igemm_halo", **a)
-        ref = oracle.fusedconv(x, w, b, z, **a)
+        ref = reference(x, w, b, z, **a)
         check(got, ref, "f16", f"halo case {ci}")
 
 
@@ -359,7 +394,7 @@ def test_smallc_route(ci):
         a = dict(attrs, activation=act, activation_params=f32params(params))
         log(f"CASE smallc {ci} x={xs} w={ws} {a} bias={bias} z={resid}")
         got = run_gpu(x, w, b, z, route="smallc", **a)
-        ref = oracle.fusedconv(x, w, b, z, **a)
+        ref = reference(x, w, b, z, **a)
         check(got, ref, "f16", f"smallc case {ci}")
 
 
@@ -378,8 +413,8 @@ def test_smallc_phi_table_activations(act):
                                 w_std=0.5)
     log(f"CASE smallc phi table {act} {h.kernel_name}")
     got = run_gpu(x, w, b, None, route="smallc", **attrs).astype(np.float64)
-    ref = oracle.fusedconv(x, w, b, None, **attrs)
-    pre = oracle.fusedconv(x, w, b, None, **dict(attrs, activation=None))
+    ref = reference(x, w, b, None, **attrs)
+    pre = reference(x, w, b, None, **dict(attrs, activation=None))
     assert np.abs(pre).max() > 8 and np.mean(np.abs(pre) < 6) > 0.3  # both regions covered
     err = np.abs(got - ref)
     if act == "Erf":
@@ -406,7 +441,7 @@ def test_halo_large_grid(ci):
     a = dict(attrs, activation="QuickGelu", activation_params=f32params([1.702]))
     log(f"CASE halo large grid {ci} x={xs} w={ws} {a}")
     got = run_gpu(x, w, b, z, route="igemm_halo", **a)
-    ref = oracle.fusedconv(x, w, b, z, **a)
+    ref = reference(x, w, b, z, **a)
     check(got, ref, "f16", f"halo large grid case {ci}")
 
 
@@ -433,7 +468,7 @@ def test_halo_wide_blocks(ci):
     a = dict(attrs, activation="QuickGelu", activation_params=f32params([1.702]))
     log(f"CASE halo wide {ci} x={xs} w={ws} {a}")
     got = run_gpu(x, w, b, z, route="igemm_halo", **a)
-    ref = oracle.fusedconv(x, w, b, z, **a)
+    ref = reference(x, w, b, z, **a)
     check(got, ref, "f16", f"halo wide case {ci}")
 
 
@@ -474,7 +509,7 @@ def test_starved_grid_splits_and_matches_unsplit():
     log(f"CASE starved split={h.split_k}")
     ys = run_gpu(x, w, b, z, **attrs)
     y1 = run_gpu(x, w, b, z, route="igemm", split_k=1, **attrs)
-    ref = oracle.fusedconv(x, w, b, z, **attrs)
+    ref = reference(x, w, b, z, **attrs)
     check(ys, ref, "f32", "split")
     check(y1, ref, "f32", "unsplit")
     check(ys, y1.astype(np.float64), "f32", "split vs unsplit")
@@ -537,7 +572,7 @@ def test_pointwise_route(ci):
         a = dict(attrs, activation=act, activation_params=f32params(params))
         log(f"CASE pointwise {ci} x={xs} w={ws} {a} bias={bias} z={resid}")
         got = run_gpu(x, w, b, z, route="pointwise", **a)
-        ref = oracle.fusedconv(x, w, b, z, **a)
+        ref = reference(x, w, b, z, **a)
         check(got, ref, "f16", f"pointwise case {ci}")
 
 
@@ -580,7 +615,7 @@ def test_im2col_route(ci):
         a = dict(attrs, activation=act, activation_params=f32params(params))
         log(f"CASE im2col {ci} x={xs} w={ws} {a} bias={bias} z={resid}")
         got = run_gpu(x, w, b, z, route="im2col", **a)
-        ref = oracle.fusedconv(x, w, b, z, **a)
+        ref = reference(x, w, b, z, **a)
         check(got, ref, "f16", f"im2col case {ci}")
 
 
@@ -618,7 +653,7 @@ def test_halo32_route(ci):
         a = dict(attrs, activation=act, activation_params=f32params(params))
         log(f"CASE halo32 {ci} x={xs} w={ws} {a} bias={bias} z={resid}")
         got = run_gpu(x, w, b, z, route="igemm_halo", **a)
-        ref = oracle.fusedconv(x, w, b, z, **a)
+        ref = reference(x, w, b, z, **a)
         check(got, ref, "f32", f"halo32 case {ci}")
 
 
@@ -654,7 +689,7 @@ def test_prepared_weights_match_plain_run(route):
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
     assert torch.equal(y2, y3)
-    ref = oracle.fusedconv(x, w, b, None, **{k_: v for k_, v in attrs.items() if k_ != "route"})
+    ref = reference(x, w, b, None, **{k_: v for k_, v in attrs.items() if k_ != "route"})
     check(y1.cpu().numpy(), ref, dt, f"prepared {route}")
 
 
@@ -731,7 +766,7 @@ def full_size_check(name, route=None):
             kw = {k: v for k, v in attrs.items() if k != "transposed"}
             ref = oracle.conv_transpose(inp["x"][n0:n1], inp["w"], inp["b"], zi, **kw)
         else:
-            ref = oracle.fusedconv(inp["x"][n0:n1], inp["w"], inp["b"], zi, **attrs)
+            ref = reference(inp["x"][n0:n1], inp["w"], inp["b"], zi, **attrs)
         assert ref.shape == got[n0:n1].shape
         max_err = max(max_err, float(np.max(np.abs(got[n0:n1].astype(np.float64) - ref))))
         max_ref = max(max_ref, float(np.max(np.abs(ref))))
@@ -845,7 +880,7 @@ def test_depth_one_3d_problems(ci):
     a = dict(attrs, activation="Relu")
     log(f"CASE depth one {ci} {h.kernel_name} x={xs} w={ws} {a}")
     got = run_gpu(x, w, b, z, **a)
-    ref = oracle.fusedconv(x, w, b, z, **a)
+    ref = reference(x, w, b, z, **a)
     check(got, ref, dt, f"depth one case {ci}")
 
 
